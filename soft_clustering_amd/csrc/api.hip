@@ -1,0 +1,223 @@
+// C ABI of libgmm (declared in include/gmm.h): argument validation, the
+// workspace layout and dispatch to the kernel families.  The library never
+// allocates memory; every launch goes to the caller's stream.
+
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+#include "plan.h"
+
+namespace gmm {
+
+bool diag_shape_supported(int dp, int kb);
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+static int pad_dim(int64_t d) {
+    if (d <= 16) return 16;
+    if (d <= 32) return 32;
+    if (d <= 64) return 64;
+    if (d <= 128) return 128;
+    return -1;
+}
+
+gmm_status make_plan(const gmm_desc* desc, Plan* p) {
+    if (desc == nullptr || p == nullptr) return GMM_E_ARG;
+    memset(p, 0, sizeof(*p));
+    p->n = desc->n;
+    p->d = desc->d;
+    p->k = desc->k;
+    p->ldx = desc->ldx;
+    p->cov = desc->cov;
+    p->xdt = desc->x_dtype;
+    p->var_floor = desc->var_floor;
+    p->ridge_rel = desc->ridge_rel;
+    if (p->n < 0 || p->d < 1 || p->k < 1 || p->ldx < p->d) return GMM_E_ARG;
+    if (p->n > ((int64_t)1 << 40) || p->d > (1 << 20) || p->k > (1 << 20)) return GMM_E_ARG;
+    if (p->cov < GMM_COV_DIAG || p->cov > GMM_COV_FULL) return GMM_E_ARG;
+    if (p->xdt < GMM_F32 || p->xdt > GMM_F16) return GMM_E_ARG;
+    if (!(p->var_floor >= 0.0f) || !isfinite(p->var_floor)) return GMM_E_ARG;
+    if (!(p->ridge_rel >= 0.0f) || !isfinite(p->ridge_rel)) return GMM_E_ARG;
+
+    const size_t A = 256;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes, A);
+        return o;
+    };
+
+    if (p->cov == GMM_COV_DIAG) {
+        const int dp = pad_dim(p->d);
+        const int kb = (int)((p->k + 15) / 16);
+        if (dp < 0 || !diag_shape_supported(dp, kb)) return GMM_E_UNSUPPORTED;
+        p->path = PATH_DIAG_F32;
+        p->dp = dp;
+        p->kb = kb;
+        p->p_max = 512;
+        p->ncols = 1 + 2 * p->d;
+        p->off_pi = take(sizeof(float) * p->k);
+        p->off_mu = take(sizeof(float) * p->k * p->d);
+        p->off_cov = take(sizeof(float) * p->k * p->d);
+        p->off_shift = take(sizeof(float) * dp);
+        p->off_panel = take(sizeof(float) * (dp / 4) * 2 * kb * 64);
+        p->off_cvec = take(sizeof(float) * 16 * kb);
+        p->off_part = take(sizeof(double) * p->p_max * p->k * p->ncols);
+        p->off_part_ll = take(sizeof(double) * p->p_max);
+        p->off_stats = take(sizeof(double) * p->k * p->ncols);
+        p->off_ll = take(sizeof(double));
+        p->off_diag = take(sizeof(int) * (2 * p->k + 2));
+        p->off_chunk = take(sizeof(double) * 4 * p->k * ((p->d + 31) / 32));
+        p->off_comp_arrivals = take(sizeof(unsigned int) * p->k);
+        p->total = off;
+        return GMM_OK;
+    }
+    return GMM_E_UNSUPPORTED;
+}
+
+static gmm_status check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+    if (ws == nullptr) return GMM_E_ARG;
+    if ((uintptr_t)ws % 256 != 0) return GMM_E_ARG;
+    if (ws_bytes < p.total) return GMM_E_WORKSPACE;
+    return GMM_OK;
+}
+
+}  // namespace gmm
+
+using namespace gmm;
+
+extern "C" {
+
+gmm_status gmm_workspace_bytes(const gmm_desc* desc, size_t* bytes) {
+    if (bytes == nullptr) return GMM_E_ARG;
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    *bytes = p.total;
+    return GMM_OK;
+}
+
+gmm_status gmm_prepare(const gmm_desc* desc, void* ws, size_t ws_bytes, const float* pi,
+                       const float* mu, const float* cov, hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    if (pi == nullptr || mu == nullptr || cov == nullptr) return GMM_E_ARG;
+    return diag_prepare(p, (char*)ws, pi, mu, cov, stream);
+}
+
+gmm_status gmm_em_step(const gmm_desc* desc, void* ws, size_t ws_bytes, const void* x,
+                       double* ll_out, hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    if (x == nullptr || p.n < 1) return GMM_E_ARG;
+    return diag_em_step(p, (char*)ws, x, ll_out, stream);
+}
+
+gmm_status gmm_finalize(const gmm_desc* desc, void* ws, size_t ws_bytes, float* pi_out,
+                        float* mu_out, float* cov_out, hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    if (p.n < 1) return GMM_E_ARG;
+    return diag_finalize(p, (char*)ws, pi_out, mu_out, cov_out, stream);
+}
+
+gmm_status gmm_loglik(const gmm_desc* desc, void* ws, size_t ws_bytes, const void* x,
+                      double* ll_out, float* point_lse, int32_t* point_argmax,
+                      hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    if (x == nullptr && p.n > 0) return GMM_E_ARG;
+    return diag_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
+}
+
+gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes, double* s0,
+                         double* s1, double* s2, hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    const char* base = (const char*)ws + p.off_stats;
+    const size_t pitch = sizeof(double) * p.ncols;
+    hipError_t e = hipSuccess;
+    if (s0 && e == hipSuccess)
+        e = hipMemcpy2DAsync(s0, sizeof(double), base, pitch, sizeof(double), p.k,
+                             hipMemcpyDeviceToDevice, stream);
+    if (s1 && e == hipSuccess)
+        e = hipMemcpy2DAsync(s1, sizeof(double) * p.d, base + sizeof(double), pitch,
+                             sizeof(double) * p.d, p.k, hipMemcpyDeviceToDevice, stream);
+    if (s2 && e == hipSuccess)
+        e = hipMemcpy2DAsync(s2, sizeof(double) * p.d, base + sizeof(double) * (1 + p.d), pitch,
+                             sizeof(double) * p.d, p.k, hipMemcpyDeviceToDevice, stream);
+    return e == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes, gmm_diag* out,
+                           hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    if (out == nullptr) return GMM_E_ARG;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GMM_E_HIP;
+    const size_t nint = 2 * p.k + 2;
+    int small[2 * 64 + 2];
+    int* host = (size_t)nint <= sizeof(small) / sizeof(int) ? small : new int[nint];
+    double ll = 0.0;
+    hipError_t e = hipMemcpy(host, (const char*)ws + p.off_diag, sizeof(int) * nint,
+                             hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+        e = hipMemcpy(&ll, (const char*)ws + p.off_ll, sizeof(double), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) {
+        memset(out, 0, sizeof(*out));
+        for (int64_t k = 0; k < p.k; ++k) {
+            const int f = host[k];
+            if (f & 1) out->bad_params++;
+            if (f & 2) out->not_pd++;
+            if (f & 4) out->empty++;
+            if (f & 8) out->nonfinite = 1;
+            if (host[p.k + k] > out->ridge_retries) out->ridge_retries = host[p.k + k];
+        }
+        if (host[2 * p.k]) out->nonfinite = 1;
+        out->ll = ll;
+    }
+    if (host != small) delete[] host;
+    return e == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+const char* gmm_status_str(gmm_status s) {
+    switch (s) {
+        case GMM_OK: return "ok";
+        case GMM_E_ARG: return "invalid argument";
+        case GMM_E_UNSUPPORTED: return "unsupported (covariance, dtype, D, K) combination";
+        case GMM_E_WORKSPACE: return "workspace too small";
+        case GMM_E_HIP: return "HIP runtime error";
+        case GMM_E_NOT_PD: return "covariance not positive definite";
+        case GMM_E_NONFINITE: return "non-finite result";
+    }
+    return "unknown status";
+}
+
+const char* gmm_version(void) { return "0.1.0"; }
+
+}  // extern "C"

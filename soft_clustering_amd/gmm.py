@@ -1,0 +1,193 @@
+"""ctypes binding of libgmm (include/gmm.h).
+
+Argument marshalling only: every step of the EM iteration runs in the HIP
+kernels of libgmm.so.  PyTorch provides device memory and the stream.  If
+the library is missing the import fails; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgmm.so")
+
+GMM_OK, GMM_E_ARG, GMM_E_UNSUPPORTED, GMM_E_WORKSPACE, GMM_E_HIP, GMM_E_NOT_PD, GMM_E_NONFINITE = range(7)
+COV = {"diag": 0, "iso": 1, "full": 2}
+DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+class GmmError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {status_str(status)} (status {status})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("cov", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("var_floor", ctypes.c_float), ("ridge_rel", ctypes.c_float)]
+
+
+class Diag(ctypes.Structure):
+    _fields_ = [("bad_params", ctypes.c_int32), ("not_pd", ctypes.c_int32),
+                ("ridge_retries", ctypes.c_int32), ("empty", ctypes.c_int32),
+                ("nonfinite", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ll", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m soft_clustering_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+    sig = {
+        "gmm_workspace_bytes": [D, ctypes.POINTER(ctypes.c_size_t)],
+        "gmm_prepare": [D, P, S, P, P, P, P],
+        "gmm_em_step": [D, P, S, P, P, P],
+        "gmm_finalize": [D, P, S, P, P, P, P],
+        "gmm_loglik": [D, P, S, P, P, P, P, P],
+        "gmm_get_stats": [D, P, S, P, P, P, P],
+        "gmm_diagnostics": [D, P, S, ctypes.POINTER(Diag), P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.gmm_status_str.argtypes = [ctypes.c_int]
+    lib.gmm_status_str.restype = ctypes.c_char_p
+    lib.gmm_version.argtypes = []
+    lib.gmm_version.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("gmm_workspace_bytes", "gmm_prepare", "gmm_em_step", "gmm_finalize", "gmm_loglik",
+            "gmm_get_stats", "gmm_diagnostics", "gmm_status_str", "gmm_version")
+
+
+def status_str(status: int) -> str:
+    return _lib.gmm_status_str(status).decode()
+
+
+def version() -> str:
+    return _lib.gmm_version().decode()
+
+
+def _check(status: int, call: str):
+    if status != GMM_OK:
+        raise GmmError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_desc(n, d, k, cov="diag", x_dtype="f32", ldx=None, var_floor=1e-6, ridge_rel=1e-3) -> Desc:
+    return Desc(int(n), int(d), int(k), int(d if ldx is None else ldx), COV[cov], DTYPE[x_dtype],
+                float(var_floor), float(ridge_rel))
+
+
+def workspace_bytes(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.gmm_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)), "gmm_workspace_bytes")
+    return int(out.value)
+
+
+@dataclass
+class Stats:
+    s0: torch.Tensor
+    s1: torch.Tensor
+    s2: torch.Tensor
+
+
+class Gmm:
+    """One descriptor plus its workspace (a torch uint8 device buffer)."""
+
+    def __init__(self, n, d, k, cov="diag", x_dtype="f32", ldx=None, var_floor=1e-6,
+                 ridge_rel=1e-3, device="cuda"):
+        self.desc = make_desc(n, d, k, cov, x_dtype, ldx, var_floor, ridge_rel)
+        self.n, self.d, self.k, self.cov, self.x_dtype = int(n), int(d), int(k), cov, x_dtype
+        self.device = torch.device(device)
+        self.ws_bytes = workspace_bytes(self.desc)
+        self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.ws.data_ptr()) % 256          # the library wants 256-byte alignment
+        self.ws_view = self.ws[off:off + self.ws_bytes]
+
+    # --- shapes -----------------------------------------------------------
+    @property
+    def cov_shape(self):
+        return {"diag": (self.k, self.d), "iso": (self.k,), "full": (self.k, self.d, self.d)}[self.cov]
+
+    def _ws(self):
+        return ctypes.c_void_p(self.ws_view.data_ptr()), ctypes.c_size_t(self.ws_bytes)
+
+    def _check_x(self, x):
+        if x.device.type != "cuda" or x.dtype != TORCH_DTYPE[self.x_dtype]:
+            raise ValueError("x must be a device tensor of the descriptor's storage dtype")
+        if x.dim() != 2 or x.shape[0] != self.n or x.shape[1] != self.d or x.stride(1) != 1 \
+                or (self.n > 1 and x.stride(0) != self.desc.ldx):
+            raise ValueError("x must be [n, d] with unit column stride and row stride ldx")
+
+    # --- calls ------------------------------------------------------------
+    def prepare(self, pi, mu, cov, stream=None):
+        for t in (pi, mu, cov):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError("parameters must be contiguous fp32 device tensors")
+        ws, nb = self._ws()
+        _check(_lib.gmm_prepare(ctypes.byref(self.desc), ws, nb, _ptr(pi), _ptr(mu), _ptr(cov),
+                                _stream(stream)), "gmm_prepare")
+
+    def em_step(self, x, ll_out=None, stream=None):
+        self._check_x(x)
+        ws, nb = self._ws()
+        _check(_lib.gmm_em_step(ctypes.byref(self.desc), ws, nb, _ptr(x), _ptr(ll_out),
+                                _stream(stream)), "gmm_em_step")
+
+    def finalize(self, pi_out=None, mu_out=None, cov_out=None, stream=None):
+        ws, nb = self._ws()
+        _check(_lib.gmm_finalize(ctypes.byref(self.desc), ws, nb, _ptr(pi_out), _ptr(mu_out),
+                                 _ptr(cov_out), _stream(stream)), "gmm_finalize")
+
+    def loglik(self, x, ll_out=None, point_lse=None, point_argmax=None, stream=None):
+        if self.n > 0:
+            self._check_x(x)
+        ws, nb = self._ws()
+        _check(_lib.gmm_loglik(ctypes.byref(self.desc), ws, nb, _ptr(x) if self.n > 0 else None,
+                               _ptr(ll_out), _ptr(point_lse), _ptr(point_argmax), _stream(stream)),
+               "gmm_loglik")
+
+    def get_stats(self, stream=None) -> Stats:
+        f64 = dict(dtype=torch.float64, device=self.device)
+        s0 = torch.empty(self.k, **f64)
+        s1 = torch.empty(self.k, self.d, **f64)
+        s2 = torch.empty({"diag": (self.k, self.d), "iso": (self.k,),
+                          "full": (self.k, self.d, self.d)}[self.cov], **f64)
+        ws, nb = self._ws()
+        _check(_lib.gmm_get_stats(ctypes.byref(self.desc), ws, nb, _ptr(s0), _ptr(s1), _ptr(s2),
+                                  _stream(stream)), "gmm_get_stats")
+        return Stats(s0, s1, s2)
+
+    def diagnostics(self, stream=None) -> Diag:
+        out = Diag()
+        ws, nb = self._ws()
+        _check(_lib.gmm_diagnostics(ctypes.byref(self.desc), ws, nb, ctypes.byref(out),
+                                    _stream(stream)), "gmm_diagnostics")
+        return out
+
+    # --- convenience: one full iteration ---------------------------------
+    def iterate(self, x, pi_out, mu_out, cov_out, ll_out=None, stream=None):
+        """gmm_em_step then gmm_finalize (the finalize also prepares the next step)."""
+        self.em_step(x, ll_out, stream)
+        self.finalize(pi_out, mu_out, cov_out, stream)
