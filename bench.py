@@ -79,6 +79,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="diag-f32-n1e6-d64-k16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy a buffer of the size of X once (a plain copy kernel "
+                         "whose HBM counters calibrate FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the fused EM "
@@ -161,6 +164,13 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if a.copy_calibration:
+        src = torch.empty(int(nbytes) // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = int(nbytes)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, (pi0, mu0, cov0))
     print(json.dumps(out), flush=True)

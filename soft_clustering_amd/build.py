@@ -33,9 +33,14 @@ FLAGS = [
 ]
 
 
+# Translation units whose kernels never test floats for NaN: IEEE mode off
+# lets max/min fold into DPP forms (one v_max_f32_dpp per reduction step).
+NO_IEEE = {"diag_fused.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str, asm_dir: str | None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *NO_IEEE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if asm_dir:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)

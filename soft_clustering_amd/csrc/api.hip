@@ -6,7 +6,7 @@
 #include <string.h>
 
 #include "common.h"
-#include "plan.h"
+#include "diag_internal.h"
 
 namespace gmm {
 
@@ -47,6 +47,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
     p->ridge_rel = desc->ridge_rel;
     if (p->n < 0 || p->d < 1 || p->k < 1 || p->ldx < p->d) return GMM_E_ARG;
     if (p->n > ((int64_t)1 << 40) || p->d > (1 << 20) || p->k > (1 << 20)) return GMM_E_ARG;
+    if (p->ldx > ((int64_t)1 << 22)) return GMM_E_ARG;   // tile offsets are 32-bit
     if (p->cov < GMM_COV_DIAG || p->cov > GMM_COV_FULL) return GMM_E_ARG;
     if (p->xdt < GMM_F32 || p->xdt > GMM_F16) return GMM_E_ARG;
     if (!(p->var_floor >= 0.0f) || !isfinite(p->var_floor)) return GMM_E_ARG;
@@ -67,21 +68,19 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->path = PATH_DIAG_F32;
         p->dp = dp;
         p->kb = kb;
-        p->p_max = 512;
+        p->p_max = 1024;
         p->ncols = 1 + 2 * p->d;
         p->off_pi = take(sizeof(float) * p->k);
         p->off_mu = take(sizeof(float) * p->k * p->d);
         p->off_cov = take(sizeof(float) * p->k * p->d);
         p->off_shift = take(sizeof(float) * dp);
         p->off_panel = take(sizeof(float) * (dp / 4) * 2 * kb * 64);
-        p->off_cvec = take(sizeof(float) * 16 * kb);
         p->off_part = take(sizeof(double) * p->p_max * p->k * p->ncols);
         p->off_part_ll = take(sizeof(double) * p->p_max);
         p->off_stats = take(sizeof(double) * p->k * p->ncols);
         p->off_ll = take(sizeof(double));
         p->off_diag = take(sizeof(int) * (2 * p->k + 2));
-        p->off_chunk = take(sizeof(double) * 4 * p->k * ((p->d + 31) / 32));
-        p->off_comp_arrivals = take(sizeof(unsigned int) * p->k);
+        p->off_chunk = take(sizeof(double) * 4 * p->k * diag_chunks(*p));
         p->total = off;
         return GMM_OK;
     }
@@ -190,14 +189,24 @@ gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes
         e = hipMemcpy(&ll, (const char*)ws + p.off_ll, sizeof(double), hipMemcpyDeviceToHost);
     if (e == hipSuccess) {
         memset(out, 0, sizeof(*out));
-        for (int64_t k = 0; k < p.k; ++k) {
-            const int f = host[k];
+        // per-(component, chunk) counts of bad / non-finite values
+        const int nch = diag_chunks(p);
+        const size_t nck = (size_t)p.k * nch * 4;
+        double* ck = new double[nck];
+        e = hipMemcpy(ck, (const char*)ws + p.off_chunk, sizeof(double) * nck, hipMemcpyDeviceToHost);
+        for (int64_t k = 0; k < p.k && e == hipSuccess; ++k) {
+            int f = host[k];
+            for (int c = 0; c < nch; ++c) {
+                if (ck[(k * nch + c) * 4 + 2] > 0.0) f |= 1;
+                if (ck[(k * nch + c) * 4 + 3] > 0.0) f |= 8;
+            }
             if (f & 1) out->bad_params++;
             if (f & 2) out->not_pd++;
             if (f & 4) out->empty++;
             if (f & 8) out->nonfinite = 1;
             if (host[p.k + k] > out->ridge_retries) out->ridge_retries = host[p.k + k];
         }
+        delete[] ck;
         if (host[2 * p.k]) out->nonfinite = 1;
         out->ll = ll;
     }

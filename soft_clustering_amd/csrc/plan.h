@@ -26,12 +26,11 @@ struct Plan {
     // workspace layout (byte offsets)
     size_t off_pi, off_mu, off_cov;   // fp32 copy of the prepared parameters
     size_t off_shift;                 // per-dimension centre of X
-    size_t off_panel, off_cvec;       // score panel and per-component constants
+    size_t off_panel;                 // score panel (MFMA register layout)
     size_t off_part, off_part_ll;     // per-workgroup partial statistics
     size_t off_stats, off_ll;         // reduced statistics and LL
     size_t off_diag;                  // status flags, counters
     size_t off_chunk;                 // per-(component, dimension chunk) sums
-    size_t off_comp_arrivals;         // per-component arrival counters
     size_t total;
     int64_t ncols;                    // statistic columns per component
 };
@@ -40,7 +39,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* plan);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Launchers of the diagonal fp32 family (diag_f32.hip).
+// Entry points of the diagonal fp32 family (diag_params.hip, diag_fused.hip).
 gmm_status diag_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
                         const float* var, hipStream_t s);
 gmm_status diag_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s);
@@ -48,8 +47,6 @@ gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* v
                          hipStream_t s);
 gmm_status diag_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
                        int32_t* argmax, hipStream_t s);
-int diag_grid(const Plan& p);
-
 int device_cu_count();
 
 }  // namespace gmm
