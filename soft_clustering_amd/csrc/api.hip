@@ -68,7 +68,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->path = PATH_DIAG_F32;
         p->dp = dp;
         p->kb = kb;
-        p->p_max = 1024;
+        p->p_max = 512;   // one workgroup per CU on up to 512 CUs
         p->ncols = 1 + 2 * p->d;
         p->off_pi = take(sizeof(float) * p->k);
         p->off_mu = take(sizeof(float) * p->k * p->d);
