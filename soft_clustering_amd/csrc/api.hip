@@ -7,6 +7,7 @@
 
 #include "common.h"
 #include "diag_internal.h"
+#include "largek_internal.h"
 
 namespace gmm {
 
@@ -61,9 +62,11 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         return o;
     };
 
-    if (p->cov == GMM_COV_DIAG) {
+    const int64_t kb64 = (p->k + 15) / 16;
+    const bool x16 = p->xdt == GMM_BF16 || p->xdt == GMM_F16;
+    if (p->cov == GMM_COV_DIAG && kb64 <= 4) {
         const int dp = pad_dim(p->d);
-        const int kb = (int)((p->k + 15) / 16);
+        const int kb = (int)kb64;
         if (dp < 0 || !diag_shape_supported(dp, kb)) return GMM_E_UNSUPPORTED;
         p->path = PATH_DIAG_F32;
         p->dp = dp;
@@ -81,6 +84,42 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_ll = take(sizeof(double));
         p->off_diag = take(sizeof(int) * (2 * p->k + 2));
         p->off_chunk = take(sizeof(double) * 4 * p->k * diag_chunks(*p));
+        p->total = off;
+        return GMM_OK;
+    }
+    if ((p->cov == GMM_COV_DIAG || p->cov == GMM_COV_ISO) && x16) {
+        // large-K family: fp16 MFMA operands, 256-component slices
+        int dp = pad_dim(p->d);
+        if (dp < 0 || p->k > 16 * kLkSlice) return GMM_E_UNSUPPORTED;
+        if (dp < 32) dp = 32;
+        const bool iso = p->cov == GMM_COV_ISO;
+        const int S = (int)((p->k + kLkSlice - 1) / kLkSlice);
+        const int64_t tiles = (p->n + kLkT - 1) / kLkT;
+        p->path = PATH_LARGEK;
+        p->dp = dp;
+        p->kb = (int)kb64;
+        p->lk_slices = S;
+        p->lk_kpad = S * kLkSlice;
+        // one workgroup per CU on up to 256 CUs, never more than S per tile
+        int64_t pm = 256;
+        if (pm > S * (tiles < 1 ? 1 : tiles)) pm = S * (tiles < 1 ? 1 : tiles);
+        p->p_max = (int)pm;
+        p->ncols = lk_ncols(p->cov, p->d);
+        p->off_pi = take(sizeof(float) * p->k);
+        p->off_mu = take(sizeof(float) * p->k * p->d);
+        p->off_cov = take(sizeof(float) * p->k * (iso ? 1 : p->d));
+        p->off_shift = take(sizeof(float) * (2 + 3 * kLkScanWgs) * dp);
+        p->off_panel = take((size_t)(iso ? 1 : 2) * (dp / 32) * (p->lk_kpad / 16) * 64 * 16);
+        p->off_chunk = take(sizeof(float) * 3 * p->lk_kpad);
+        if (S > 1) {
+            p->off_lse = take(sizeof(float) * (size_t)S * p->n);
+            p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)S * p->n);
+        }
+        p->off_part = take(sizeof(double) * (size_t)p->p_max * kLkSlice * p->ncols);
+        p->off_part_ll = take((sizeof(double) + sizeof(int)) * kLkLLSlots);
+        p->off_stats = take(sizeof(double) * p->k * p->ncols);
+        p->off_ll = take(sizeof(double));
+        p->off_diag = take(sizeof(int) * (2 * p->k + 4));
         p->total = off;
         return GMM_OK;
     }
@@ -116,6 +155,7 @@ gmm_status gmm_prepare(const gmm_desc* desc, void* ws, size_t ws_bytes, const fl
     if (st != GMM_OK) return st;
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (pi == nullptr || mu == nullptr || cov == nullptr) return GMM_E_ARG;
+    if (p.path == PATH_LARGEK) return lk_prepare(p, (char*)ws, pi, mu, cov, stream);
     return diag_prepare(p, (char*)ws, pi, mu, cov, stream);
 }
 
@@ -126,6 +166,7 @@ gmm_status gmm_em_step(const gmm_desc* desc, void* ws, size_t ws_bytes, const vo
     if (st != GMM_OK) return st;
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (x == nullptr || p.n < 1) return GMM_E_ARG;
+    if (p.path == PATH_LARGEK) return lk_em_step(p, (char*)ws, x, ll_out, stream);
     return diag_em_step(p, (char*)ws, x, ll_out, stream);
 }
 
@@ -136,6 +177,7 @@ gmm_status gmm_finalize(const gmm_desc* desc, void* ws, size_t ws_bytes, float* 
     if (st != GMM_OK) return st;
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (p.n < 1) return GMM_E_ARG;
+    if (p.path == PATH_LARGEK) return lk_finalize(p, (char*)ws, pi_out, mu_out, cov_out, stream);
     return diag_finalize(p, (char*)ws, pi_out, mu_out, cov_out, stream);
 }
 
@@ -147,6 +189,8 @@ gmm_status gmm_loglik(const gmm_desc* desc, void* ws, size_t ws_bytes, const voi
     if (st != GMM_OK) return st;
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (x == nullptr && p.n > 0) return GMM_E_ARG;
+    if (p.path == PATH_LARGEK)
+        return lk_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
     return diag_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
 }
 
@@ -165,9 +209,10 @@ gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes, 
     if (s1 && e == hipSuccess)
         e = hipMemcpy2DAsync(s1, sizeof(double) * p.d, base + sizeof(double), pitch,
                              sizeof(double) * p.d, p.k, hipMemcpyDeviceToDevice, stream);
+    const int64_t w2 = p.cov == GMM_COV_ISO ? 1 : p.d;   // iso: sum gamma |x|^2
     if (s2 && e == hipSuccess)
-        e = hipMemcpy2DAsync(s2, sizeof(double) * p.d, base + sizeof(double) * (1 + p.d), pitch,
-                             sizeof(double) * p.d, p.k, hipMemcpyDeviceToDevice, stream);
+        e = hipMemcpy2DAsync(s2, sizeof(double) * w2, base + sizeof(double) * (1 + p.d), pitch,
+                             sizeof(double) * w2, p.k, hipMemcpyDeviceToDevice, stream);
     return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
@@ -180,7 +225,7 @@ gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes
     if (out == nullptr) return GMM_E_ARG;
     if (hipStreamSynchronize(stream) != hipSuccess) return GMM_E_HIP;
     const size_t nint = 2 * p.k + 2;
-    int small[2 * 64 + 2];
+    int small[2 * 64 + 4];
     int* host = (size_t)nint <= sizeof(small) / sizeof(int) ? small : new int[nint];
     double ll = 0.0;
     hipError_t e = hipMemcpy(host, (const char*)ws + p.off_diag, sizeof(int) * nint,
@@ -189,11 +234,14 @@ gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes
         e = hipMemcpy(&ll, (const char*)ws + p.off_ll, sizeof(double), hipMemcpyDeviceToHost);
     if (e == hipSuccess) {
         memset(out, 0, sizeof(*out));
-        // per-(component, chunk) counts of bad / non-finite values
-        const int nch = diag_chunks(p);
+        // diagonal fp32 path: per-(component, chunk) counts of bad / non-finite values
+        const bool dg = p.path == PATH_DIAG_F32;
+        const int nch = dg ? diag_chunks(p) : 0;
         const size_t nck = (size_t)p.k * nch * 4;
-        double* ck = new double[nck];
-        e = hipMemcpy(ck, (const char*)ws + p.off_chunk, sizeof(double) * nck, hipMemcpyDeviceToHost);
+        double* ck = new double[nck + 1];
+        if (nck)
+            e = hipMemcpy(ck, (const char*)ws + p.off_chunk, sizeof(double) * nck,
+                          hipMemcpyDeviceToHost);
         for (int64_t k = 0; k < p.k && e == hipSuccess; ++k) {
             int f = host[k];
             for (int c = 0; c < nch; ++c) {
@@ -204,10 +252,12 @@ gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes
             if (f & 2) out->not_pd++;
             if (f & 4) out->empty++;
             if (f & 8) out->nonfinite = 1;
+            if (f & 16) out->ill_cond++;
             if (host[p.k + k] > out->ridge_retries) out->ridge_retries = host[p.k + k];
         }
         delete[] ck;
         if (host[2 * p.k]) out->nonfinite = 1;
+        if (p.path == PATH_LARGEK) out->x_range = host[2 * p.k + 1];
         out->ll = ll;
     }
     if (host != small) delete[] host;

@@ -1,0 +1,125 @@
+// Internal interface of the large-K family (isotropic or diagonal covariance,
+// X stored in bf16 or fp16, fp16 MFMA operands, fp32 softmax and statistics):
+// workspace pointers, kernel arguments and launch helpers.
+#pragma once
+
+#include "common.h"
+#include "plan.h"
+
+namespace gmm {
+
+// Points per tile and waves per workgroup of the fused kernel.
+constexpr int kLkT = 32;
+constexpr int kLkWaves = 4;
+// Components per wave: the wave keeps their score panel in registers.
+constexpr int kLkKW = 64;
+constexpr int kLkSlice = kLkWaves * kLkKW;   // components per workgroup (slice)
+
+// Fused-kernel variants.
+enum LkMode : int {
+    LK_FUSED_EM = 0,   // K fits one slice: LSE and statistics in one sweep
+    LK_SWEEP1 = 1,     // per (slice, point) base-2 LSE (+ argmax) over the slice
+    LK_SWEEP2 = 2,     // merge the slices' LSE, statistics of this slice
+    LK_FUSED_E = 3,    // K fits one slice: E-step only (LL, per-point outputs)
+};
+
+// fp16 operand range: squares and entries are clamped / scaled below this.
+constexpr float kF16Max = 65504.0f;
+
+// A component whose estimated score rounding error near its own mean exceeds
+// this many nats is reported as ill-conditioned (flag bit 4).
+constexpr double kLkIllCondNats = 4.0;
+
+// Slots for per-workgroup LL partials and range flags (fused kernel and the
+// slice-merge kernel), and workgroups of the slice-merge kernel.
+constexpr int kLkLLSlots = 1024;
+constexpr int kLkMergeWgs = 1024;
+
+// Rows of X sampled for the centre / scale, and workgroups scanning them.
+constexpr int kLkScanRows = 4096;
+constexpr int kLkScanWgs = 32;
+
+struct LkWs {
+    float *pi, *mu, *var;        // fp32 parameters theta (var: [K] iso, [K*D] diag)
+    float2* dsc;                 // [DP] (c_d, s_d): y' = (x - c_d) * s_d, s_d = 2^-e_d
+    float* scan;                 // [scan workgroups][DP][3] sample (sum, min, max)
+    uint4* panel;                // fp16 score panel, MFMA register layout
+    float *cvec, *fsc, *pvec;    // [Kpad] base-2 constant, panel scale 2^f_k, iso ||y||^2 coeff.
+    float* part_lse;             // [S][N] base-2 LSE of each slice; row 0 is then
+                                 // overwritten with the merged LSE (two-sweep only)
+    int* part_arg;               // [S][N] argmax within each slice (two-sweep only)
+    float* part_max;             // [S][N] largest score within each slice
+    double *part, *part_ll;      // per-workgroup partials
+    int* part_flag;              // per workgroup: X outside the fp16 operand range
+    double *stats, *ll;          // reduced statistics (raw moments), LL
+    int* flags;                  // [K] bit0 bad params, bit2 empty, bit3 non-finite,
+                                 //     bit4 ill-conditioned fp16 score
+    int* misc;                   // [0] non-finite LL, [1] X outside the fp16 operand range
+};
+
+inline LkWs lk_ws(const Plan& p, char* ws) {
+    LkWs w;
+    w.pi = (float*)(ws + p.off_pi);
+    w.mu = (float*)(ws + p.off_mu);
+    w.var = (float*)(ws + p.off_cov);
+    w.dsc = (float2*)(ws + p.off_shift);
+    w.scan = (float*)(w.dsc + p.dp);
+    w.panel = (uint4*)(ws + p.off_panel);
+    w.cvec = (float*)(ws + p.off_chunk);
+    w.fsc = w.cvec + p.lk_kpad;
+    w.pvec = w.fsc + p.lk_kpad;
+    const bool two = p.lk_slices > 1;
+    w.part_lse = two ? (float*)(ws + p.off_lse) : nullptr;
+    w.part_arg = two ? (int*)(ws + p.off_arg) : nullptr;
+    w.part_max = two ? (float*)(w.part_arg + (size_t)p.lk_slices * p.n) : nullptr;
+    w.part = (double*)(ws + p.off_part);
+    w.part_ll = (double*)(ws + p.off_part_ll);
+    w.part_flag = (int*)(w.part_ll + kLkLLSlots);
+    w.stats = (double*)(ws + p.off_stats);
+    w.ll = (double*)(ws + p.off_ll);
+    w.flags = (int*)(ws + p.off_diag);
+    w.misc = w.flags + 2 * p.k;   // after [K] flags and [K] ridge retries (unused here)
+    return w;
+}
+
+// Arguments of the fused kernel (one struct, passed by value).
+struct LkArgs {
+    const void* x;
+    int64_t n, ldx;
+    int d, k_real, S, vec;
+    const uint4* panel;
+    int nblk;                    // 16-component blocks in the panel (Kpad / 16)
+    const float* cvec;
+    const float* fsc;
+    const float* pvec;
+    const float2* dsc;
+    float* part_lse;             // sweep 1 output [S][N] (base-2 LSE per slice)
+    int* part_arg;               // sweep 1 output [S][N] (nullable: no argmax)
+    float* part_max;             // sweep 1 output [S][N] (with part_arg)
+    const float* lse_in;         // sweep 2 input [N]: merged base-2 LSE
+    double* part;
+    double* part_ll;
+    int* part_flag;
+    float* out_lse;              // E-only: natural-log LSE per point (nullable)
+    int* out_arg;                // E-only: argmax per point (nullable)
+};
+
+// Statistic columns per component: diag [s0, s1(D), s2(D)], iso [s0, s1(D), s2].
+inline int64_t lk_ncols(int cov, int64_t d) { return cov == GMM_COV_ISO ? 2 + d : 1 + 2 * d; }
+
+// Workgroups of the fused kernel (chunks x slices), a function of the plan
+// and the device only.
+int lk_grid(const Plan& p);
+
+// Launch the fused kernel in `mode` (largek.hip).
+hipError_t lk_launch(const Plan& p, const LkArgs& a, int mode, int grid, hipStream_t s);
+
+// Workgroup index of (slice, chunk) in a grid of G = chunks * S workgroups
+// (XCD-aware when G is a multiple of 8 * S: the slices of one chunk share
+// blockIdx % 8, i.e. one XCD and its L2).
+__host__ __device__ inline int lk_wg_of(int slice, int chunk, int G, int S) {
+    if (G % (8 * S) == 0) return 8 * ((chunk / 8) * S + slice) + (chunk % 8);
+    return chunk * S + slice;
+}
+
+}  // namespace gmm

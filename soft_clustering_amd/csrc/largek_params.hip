@@ -1,0 +1,504 @@
+// Large-K family: parameter preparation, the slice merge of the two-sweep
+// log-sum-exp, reduction of the fused kernel's partials, M-step, and the host
+// entry points.
+//
+// Preprocess ([LP-GMM] 3.1): per component the precisions, the fp16 score
+// panel and the log-normaliser, here in base 2 and with power-of-two scales
+// (per dimension on X, per component on the panel) chosen so that every fp16
+// operand is in range.  The centre and the per-dimension scale come from a
+// sample of X, so they are set at the start of every pass over X (em_step,
+// loglik), and the panel is rebuilt then from the current theta.  M-step ([Flash-GMM] Method, parameter update):
+// pi' = s0/N, mu' = s1/s0, var' = max(s2/s0 - mu'^2, floor) per dimension
+// (diagonal) or max((s2/s0 - |mu'|^2) / D, floor) (isotropic), evaluated from
+// moments about the centre c used by the fused kernel.  A component with
+// s0 < 1e-6 keeps its mean and variance.
+//
+// Every output has a single writer; kernels never wait on each other except
+// through stream order.
+
+#include <math.h>
+#include <string.h>
+
+#include "largek_internal.h"
+
+namespace gmm {
+
+namespace {
+
+constexpr int kKpw = 4;   // components per workgroup in the panel kernel (one per wave)
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// gmm_prepare, step 1: copy theta into the workspace and reset the flags.
+// Grid K, 128 threads.
+__global__ __launch_bounds__(128) void k_lk_load(int k_real, int d, bool iso, const float* pi,
+                                                 const float* mu, const float* var, float* th_pi,
+                                                 float* th_mu, float* th_var, int* flags) {
+    const int k = blockIdx.x;
+    for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
+        th_mu[(int64_t)k * d + dd] = mu[(int64_t)k * d + dd];
+        if (!iso) th_var[(int64_t)k * d + dd] = var[(int64_t)k * d + dd];
+    }
+    if (threadIdx.x == 0) {
+        const float pk = pi[k];
+        th_pi[k] = pk;
+        if (iso) th_var[k] = var[k];
+        flags[k] = (!(pk >= 0.0f) || !isfinite(pk)) ? 1 : 0;
+        flags[k_real + k] = 0;
+        if (k == 0) {
+            flags[2 * k_real] = 0;
+            flags[2 * k_real + 1] = 0;
+        }
+    }
+}
+
+// Sample of X for the centre and scale: up to kLkScanRows rows spread evenly
+// over N; workgroup b scans sample rows [b * R, (b + 1) * R), R = rows per
+// workgroup.  Thread t handles dimension t % DP for rows t / DP, t / DP +
+// 256 / DP, ...  Output per (workgroup, dim): (sum, min, max), fixed order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_lk_scan(const uint16_t* __restrict__ x, int64_t n,
+                                                 int64_t ldx, int d, int dp, float* scan) {
+    __shared__ float red[3][256];
+    const int tid = threadIdx.x, dd = tid % dp, ph = tid / dp, nph = 256 / dp;
+    const int64_t ns = n < kLkScanRows ? n : kLkScanRows;
+    const int per = kLkScanRows / kLkScanWgs;
+    float sum = 0.0f, lo = INFINITY, hi = -INFINITY;
+    if (dd < d) {
+        for (int i = blockIdx.x * per + ph; i < (blockIdx.x + 1) * per && i < ns; i += nph) {
+            const int64_t row = (int64_t)i * n / ns;
+            const uint32_t b = x[row * ldx + dd];
+            float v;
+            if constexpr (BF16) v = __uint_as_float(b << 16);
+            else v = (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+            if (isfinite(v)) {
+                sum += v;
+                lo = fminf(lo, v);
+                hi = fmaxf(hi, v);
+            }
+        }
+    }
+    red[0][tid] = sum;
+    red[1][tid] = lo;
+    red[2][tid] = hi;
+    __syncthreads();
+    if (tid < dp) {
+        float s = 0.0f, l = INFINITY, h = -INFINITY;
+        for (int q = 0; q < nph; ++q) {
+            s += red[0][q * dp + tid];
+            l = fminf(l, red[1][q * dp + tid]);
+            h = fmaxf(h, red[2][q * dp + tid]);
+        }
+        float* o = scan + ((int64_t)blockIdx.x * dp + tid) * 3;
+        o[0] = s;
+        o[1] = l;
+        o[2] = h;
+    }
+}
+
+// Centre and per-dimension scale of X for the fused kernel, from the scan:
+// c_d = sample mean of the finite values rounded to the storage type, s_d = 2^-e_d with 2^e_d the power of two
+// at or below 1/8 of the sample's largest |x_d - c_d|, so the sampled y' lie
+// in [-16, 16] and y'^2 stays below the fp16 maximum for |y'| < 255.  One
+// workgroup.
+__global__ __launch_bounds__(128) void k_lk_centre(int64_t n, int d, int dp, bool bf16,
+                                                   const float* scan, float2* dsc) {
+    const int dd = threadIdx.x;
+    if (dd >= dp) return;
+    if (dd >= d) {
+        dsc[dd] = make_float2(0.0f, 0.0f);
+        return;
+    }
+    const int64_t ns = n < kLkScanRows ? n : kLkScanRows;
+    double s = 0.0;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int b = 0; b < kLkScanWgs; ++b) {
+        const float* o = scan + ((int64_t)b * dp + dd) * 3;
+        s += (double)o[0];
+        lo = fminf(lo, o[1]);
+        hi = fmaxf(hi, o[2]);
+    }
+    // c is rounded to X's storage type, so x - c is exact in fp32 and, for
+    // data within ~2^11 storage ulps of c, exact in fp16 too: no rounding
+    // bias shared by every point of a coarse storage lattice
+    double c = (ns > 0 && isfinite(s)) ? s / (double)ns : 0.0;
+    if (bf16) c = (double)(float)(__bf16)(float)c;
+    else if (fabs(c) < 65504.0) c = (double)(float)(_Float16)(float)c;
+    const double r = fmax((double)hi - c, c - (double)lo);
+    int e = 0;
+    if (r > 0.0 && isfinite(r)) {
+        e = ilogb(r) - 3;
+        e = e < -60 ? -60 : (e > 60 ? 60 : e);
+    }
+    dsc[dd] = make_float2((float)c, (float)ldexp(1.0, -e));
+}
+
+// Score panel and constants of one component per wave (grid Kpad / 4, 256
+// threads).  Lane l handles dimensions l and l + 64.  Panel entry of
+// (array pa, dim dd, component k) lives at half index
+//   (((pa * KS + dd / 32) * nblk + k / 16) * 64 + 16 * ((dd % 32) / 8) + k % 16) * 8 + dd % 8,
+// the B-operand register layout of v_mfma_f32_16x16x32_f16 (lane 16 g + j
+// holds rows 8g..8g+7 of column j).
+__global__ __launch_bounds__(256) void k_lk_panel(int k_real, int d, int dp, bool iso, int nblk,
+                                                  const float* pi, const float* mu,
+                                                  const float* var, const float2* dsc,
+                                                  uint16_t* panel, float* cvec, float* fsc,
+                                                  float* pvec, int* flags) {
+    const int lane = threadIdx.x & 63;
+    const int k = blockIdx.x * kKpw + (threadIdx.x >> 6);
+    const int KS = dp / 32;
+    const int npa = iso ? 1 : 2;
+    auto put = [&](int pa, int dd, float v) {
+        const _Float16 h = (_Float16)v;
+        const int64_t idx =
+            (((int64_t)(pa * KS + dd / 32) * nblk + k / 16) * 64 + 16 * ((dd % 32) / 8) + k % 16) * 8 + dd % 8;
+        panel[idx] = __builtin_bit_cast(uint16_t, h);
+    };
+    if (k >= k_real) {   // padding component: zero panel, weight 0
+        for (int dd = lane; dd < dp; dd += 64)
+            for (int pa = 0; pa < npa; ++pa) put(pa, dd, 0.0f);
+        if (lane == 0) {
+            cvec[k] = -INFINITY;
+            fsc[k] = 1.0f;
+            pvec[k] = 0.0f;
+        }
+        return;
+    }
+    // unscaled panel entries (fp64) for dims lane, lane + 64
+    double ea[2] = {0.0, 0.0}, eb[2] = {0.0, 0.0};
+    double logv = 0.0, m2p = 0.0, mx = 0.0, bad = 0.0, err2 = 0.0;
+    const double vi = iso ? (double)var[k] : 0.0;
+    for (int h = 0; h < 2; ++h) {
+        const int dd = lane + 64 * h;
+        if (dd >= d) continue;
+        const double v = iso ? vi : (double)var[(int64_t)k * d + dd];
+        const double c = dsc[dd].x, esc = 1.0 / (double)dsc[dd].y;   // 2^e_d
+        const double mc = (double)mu[(int64_t)k * d + dd] - c;
+        if (!(v > 0.0) || !isfinite(v) || !isfinite(mc)) bad = 1.0;
+        const double pr = 1.0 / v;
+        // |y| of a point near this component: |mu - c| + 3 sigma
+        const double yt = fabs(mc) + 3.0 * sqrt(fabs(v));
+        if (iso) {
+            ea[h] = kLog2e * mc * pr * esc;                 // W
+            mx = fmax(mx, fabs(ea[h]));
+            err2 += (kLog2e * mc * pr * yt) * (kLog2e * mc * pr * yt);
+        } else {
+            ea[h] = -0.5 * kLog2e * pr * esc * esc;         // A (multiplies y'^2)
+            eb[h] = kLog2e * mc * pr * esc;                 // B (multiplies y')
+            mx = fmax(mx, fmax(fabs(ea[h]), fabs(eb[h])));
+            logv += log(v);
+            const double ta = 0.5 * kLog2e * pr * yt * yt, tb = kLog2e * mc * pr * yt;
+            err2 += ta * ta + tb * tb;
+        }
+        m2p += mc * mc * pr;
+    }
+    logv = wave_sum_f64(logv);
+    m2p = wave_sum_f64(m2p);
+    mx = wave_max_f64(mx);
+    bad = wave_max_f64(bad);
+    err2 = wave_sum_f64(err2);
+    if (iso) logv = (double)d * log(vi);
+    // per-component scale: largest entry in [2^13, 2^14)
+    int f = 0;
+    if (mx > 0.0 && isfinite(mx)) f = ilogb(mx) - 13;
+    const double sc = ldexp(1.0, -f);
+    for (int h = 0; h < 2; ++h) {
+        const int dd = lane + 64 * h;
+        if (dd >= dp) continue;
+        put(0, dd, (float)(ea[h] * sc));
+        if (!iso) put(1, dd, (float)(eb[h] * sc));
+    }
+    if (lane == 0) {
+        const double lp = log((double)pi[k]);
+        const double c = kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logv + m2p));
+        cvec[k] = (float)c;
+        fsc[k] = (float)ldexp(1.0, f);
+        pvec[k] = iso ? (float)(-0.5 * kLog2e / vi * sc) : 0.0f;
+        if (bad > 0.0) flags[k] |= 1;
+        // rounding-error estimate of the fp16 expanded score near the mean
+        // (two roundings of relative size <= 2^-11 per term, random signs)
+        if (sqrt(err2) * ldexp(1.0, -11) * (1.41421356 / 1.7320508) * kLn2 > kLkIllCondNats)
+            flags[k] |= 16;
+    }
+}
+
+// Two-sweep merge: per point, the base-2 LSE over the slices (written over
+// slice 0's entry), LL partial per workgroup (fixed order), and for the
+// E-step alone the natural-log LSE and the argmax (lowest component on ties:
+// the first slice whose maximum is the overall maximum).
+__global__ __launch_bounds__(256) void k_lk_merge(int64_t n, int S, float* part_lse,
+                                                  const int* part_arg, const float* part_max,
+                                                  double* part_ll, float* out_lse, int* out_arg) {
+    __shared__ double red[256];
+    double ll = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += stride) {
+        float M = -INFINITY;
+        for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[(int64_t)s * n + p]);
+        const float Ms = M == -INFINITY ? 0.0f : M;
+        float Z = 0.0f;
+        for (int s = 0; s < S; ++s) Z += fast_exp2(part_lse[(int64_t)s * n + p] - Ms);
+        const float lse = Ms + fast_log2(Z);
+        part_lse[p] = lse;
+        ll += (double)lse;
+        if (out_lse) out_lse[p] = lse * (float)kLn2;
+        if (out_arg) {
+            float bm = -INFINITY;
+            int arg = 0x7FFFFFFF;
+            for (int s = 0; s < S; ++s) {
+                const float v = part_max[(int64_t)s * n + p];
+                if (v > bm || (arg == 0x7FFFFFFF && v == bm)) {
+                    bm = v;
+                    arg = part_arg[(int64_t)s * n + p];
+                }
+            }
+            out_arg[p] = arg;
+        }
+    }
+    ll = block_sum_f64(ll, red);
+    if (threadIdx.x == 0) part_ll[blockIdx.x] = ll * kLn2;
+}
+
+// LL = fixed-order sum of the LL partials; OR of the range flags.
+__global__ __launch_bounds__(256) void k_lk_sum(const double* part_ll, int P, const int* part_flag,
+                                                int Pf, double* ll_ws, double* ll_out, int* misc) {
+    __shared__ double red[256];
+    double v = 0.0;
+    for (int p = threadIdx.x; p < P; p += 256) v += part_ll[p];
+    v = block_sum_f64(v, red);
+    int f = 0;
+    for (int p = threadIdx.x; p < Pf; p += 256) f |= part_flag[p];
+    f = __syncthreads_or(f);
+    if (threadIdx.x == 0) {
+        *ll_ws = v;
+        if (ll_out) *ll_out = v;
+        misc[0] = isfinite(v) ? 0 : 1;
+        misc[1] = f;
+    }
+}
+
+// Reduce component k's partials over the point chunks (fixed order), then
+// the M-step.  Grid K, 256 threads.  Partial columns are [s0, s1'(D),
+// s2'(D)] (diag) or [s0, s1'(D), s2] (iso), with s1' = sum gamma y',
+// s2' = sum gamma y'^2, y' = (x - c) s; the isotropic s2 = sum gamma |y|^2.
+__global__ __launch_bounds__(256) void k_lk_reduce(
+    const double* __restrict__ part, int G, int S, int64_t n, int d, bool iso, float var_floor,
+    const float2* __restrict__ dsc, double* __restrict__ stats, float* __restrict__ th_pi,
+    float* __restrict__ th_mu, float* __restrict__ th_var, float* __restrict__ out_pi,
+    float* __restrict__ out_mu, float* __restrict__ out_var, int* __restrict__ flags) {
+    extern __shared__ double colsum[];   // [ncol]
+    __shared__ double red[256];
+    const int k = blockIdx.x, tid = threadIdx.x;
+    const int ncol = iso ? 2 + d : 1 + 2 * d;
+    const int slice = k / kLkSlice, kl = k % kLkSlice;
+    const int nchunks = G / S;
+    for (int col = tid; col < ncol; col += 256) {
+        double a0 = 0.0;
+        for (int ch = 0; ch < nchunks; ++ch) {
+            const int b = lk_wg_of(slice, ch, G, S);
+            a0 += part[((int64_t)b * kLkSlice + kl) * ncol + col];
+        }
+        colsum[col] = a0;
+    }
+    __syncthreads();
+    const double s0 = colsum[0];
+    const bool empty = s0 < kEmptyNk;
+    double nonfin = isfinite(s0) ? 0.0 : 1.0;
+    // per dimension: t1 = sum gamma y, t2 = sum gamma y^2 (diag)
+    double mu2 = 0.0, c_t1 = 0.0, cc = 0.0;
+    for (int dd = tid; dd < d; dd += 256) {
+        const double c = dsc[dd].x, esc = 1.0 / (double)dsc[dd].y;
+        const double t1 = colsum[1 + dd] * esc;
+        const int64_t i = (int64_t)k * d + dd;
+        const int64_t so = (int64_t)k * ncol;
+        stats[so + 1 + dd] = t1 + c * s0;
+        if (!isfinite(t1)) nonfin = 1.0;
+        float mf = th_mu[i];
+        if (!empty) mf = (float)(c + t1 / s0);
+        const double dm = empty ? 0.0 : t1 / s0;
+        if (!iso) {
+            const double t2 = colsum[1 + d + dd] * esc * esc;
+            stats[so + 1 + d + dd] = t2 + 2.0 * c * t1 + c * c * s0;
+            if (!isfinite(t2)) nonfin = 1.0;
+            float vf = th_var[i];
+            if (!empty) vf = (float)fmax(t2 / s0 - dm * dm, (double)var_floor);
+            th_var[i] = vf;
+            if (out_var) out_var[i] = vf;
+        } else {
+            mu2 += dm * dm;
+            c_t1 += c * t1;
+            cc += c * c;
+        }
+        th_mu[i] = mf;
+        if (out_mu) out_mu[i] = mf;
+    }
+    nonfin = block_sum_f64(nonfin, red);
+    if (iso) {
+        mu2 = block_sum_f64(mu2, red);
+        c_t1 = block_sum_f64(c_t1, red);
+        cc = block_sum_f64(cc, red);
+    }
+    if (tid == 0) {
+        stats[(int64_t)k * ncol] = s0;
+        if (iso) {
+            const double s2 = colsum[1 + d];
+            stats[(int64_t)k * ncol + 1 + d] = s2 + 2.0 * c_t1 + cc * s0;
+            if (!isfinite(s2)) nonfin = 1.0;
+            float vf = th_var[k];
+            if (!empty) vf = (float)fmax((s2 / s0 - mu2) / (double)d, (double)var_floor);
+            th_var[k] = vf;
+            if (out_var) out_var[k] = vf;
+        }
+        const float pf = (float)(s0 / (double)n);
+        th_pi[k] = pf;
+        if (out_pi) out_pi[k] = pf;
+        int f = 0;
+        if (!(pf >= 0.0f) || !isfinite(pf)) f |= 1 | 8;
+        if (nonfin > 0.0) f |= 8;
+        if (empty) f |= 4;
+        flags[k] = f | (flags[k] & 16);   // keep the conditioning flag of this pass's theta
+    }
+}
+
+// Centre / scale from a sample of X, then the panel of the current theta.
+hipError_t refresh_panel(const Plan& p, const LkWs& w, const void* x, hipStream_t s) {
+    const bool iso = p.cov == GMM_COV_ISO;
+    if (p.xdt == GMM_BF16)
+        hipLaunchKernelGGL(k_lk_scan<true>, dim3(kLkScanWgs), dim3(256), 0, s, (const uint16_t*)x,
+                           p.n, p.ldx, (int)p.d, p.dp, w.scan);
+    else
+        hipLaunchKernelGGL(k_lk_scan<false>, dim3(kLkScanWgs), dim3(256), 0, s, (const uint16_t*)x,
+                           p.n, p.ldx, (int)p.d, p.dp, w.scan);
+    hipLaunchKernelGGL(k_lk_centre, dim3(1), dim3(128), 0, s, p.n, (int)p.d, p.dp,
+                       p.xdt == GMM_BF16, w.scan, w.dsc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_lk_panel, dim3(p.lk_kpad / kKpw), dim3(256), 0, s, (int)p.k, (int)p.d, p.dp,
+                       iso, p.lk_kpad / 16, w.pi, w.mu, w.var, w.dsc, (uint16_t*)w.panel, w.cvec,
+                       w.fsc, w.pvec, w.flags);
+    return hipGetLastError();
+}
+
+LkArgs make_args(const Plan& p, const LkWs& w, const void* x) {
+    LkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.n = p.n;
+    a.ldx = p.ldx;
+    a.d = (int)p.d;
+    a.k_real = (int)p.k;
+    a.S = p.lk_slices;
+    a.vec = ((uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0) ? 1 : 0;
+    a.panel = w.panel;
+    a.nblk = p.lk_kpad / 16;
+    a.cvec = w.cvec;
+    a.fsc = w.fsc;
+    a.pvec = w.pvec;
+    a.dsc = w.dsc;
+    a.part = w.part;
+    a.part_ll = w.part_ll;
+    a.part_flag = w.part_flag;
+    return a;
+}
+
+int merge_grid(const Plan& p) {
+    int64_t g = (p.n + 255) / 256;
+    if (g > kLkMergeWgs) g = kLkMergeWgs;
+    return (int)(g < 1 ? 1 : g);
+}
+
+gmm_status lk_sum(const Plan& p, const LkWs& w, int P, int Pf, double* ll_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_lk_sum, dim3(1), dim3(256), 0, s, w.part_ll, P, w.part_flag, Pf, w.ll,
+                       ll_out, w.misc);
+    return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+}  // namespace
+
+// Grid: one workgroup per CU, chunks a multiple of 8 so that each chunk's
+// slices share an XCD; never more chunks than tiles or partial slots.
+int lk_grid(const Plan& p) {
+    const int S = p.lk_slices;
+    const int64_t tiles = (p.n + kLkT - 1) / kLkT;
+    int64_t chunks = device_cu_count() / S;
+    if (chunks >= 8) chunks = chunks / 8 * 8;
+    if (chunks < 1) chunks = 1;
+    if (chunks > tiles) chunks = tiles < 1 ? 1 : tiles;
+    if (chunks * S > p.p_max) chunks = p.p_max / S;
+    return (int)(chunks * S);
+}
+
+gmm_status lk_prepare(const Plan& p, char* ws, const float* pi, const float* mu, const float* var,
+                      hipStream_t s) {
+    LkWs w = lk_ws(p, ws);
+    hipLaunchKernelGGL(k_lk_load, dim3(p.k), dim3(128), 0, s, (int)p.k, (int)p.d,
+                       p.cov == GMM_COV_ISO, pi, mu, var, w.pi, w.mu, w.var, w.flags);
+    return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
+    LkWs w = lk_ws(p, ws);
+    if (refresh_panel(p, w, x, s) != hipSuccess) return GMM_E_HIP;
+    const int G = lk_grid(p);
+    LkArgs a = make_args(p, w, x);
+    if (p.lk_slices == 1) {
+        if (lk_launch(p, a, LK_FUSED_EM, G, s) != hipSuccess) return GMM_E_HIP;
+        return lk_sum(p, w, G, G, ll_out, s);
+    }
+    a.part_lse = w.part_lse;
+    if (lk_launch(p, a, LK_SWEEP1, G, s) != hipSuccess) return GMM_E_HIP;
+    const int M = merge_grid(p);
+    hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
+                       (const int*)nullptr, (const float*)nullptr, w.part_ll, (float*)nullptr,
+                       (int*)nullptr);
+    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
+    a.part_lse = nullptr;
+    a.lse_in = w.part_lse;
+    if (lk_launch(p, a, LK_SWEEP2, G, s) != hipSuccess) return GMM_E_HIP;
+    return lk_sum(p, w, M, G, ll_out, s);
+}
+
+gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var, hipStream_t s) {
+    LkWs w = lk_ws(p, ws);
+    const int G = lk_grid(p);
+    const size_t shm = sizeof(double) * (size_t)p.ncols;
+    hipLaunchKernelGGL(k_lk_reduce, dim3(p.k), dim3(256), shm, s, w.part, G, p.lk_slices, p.n,
+                       (int)p.d, p.cov == GMM_COV_ISO, p.var_floor, w.dsc, w.stats, w.pi, w.mu,
+                       w.var, pi, mu, var, w.flags);
+    return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
+                     int32_t* argmax, hipStream_t s) {
+    LkWs w = lk_ws(p, ws);
+    if (p.n == 0) return lk_sum(p, w, 0, 0, ll_out, s);
+    if (refresh_panel(p, w, x, s) != hipSuccess) return GMM_E_HIP;
+    const int G = lk_grid(p);
+    LkArgs a = make_args(p, w, x);
+    if (p.lk_slices == 1) {
+        a.out_lse = lse;
+        a.out_arg = argmax;
+        if (lk_launch(p, a, LK_FUSED_E, G, s) != hipSuccess) return GMM_E_HIP;
+        return lk_sum(p, w, G, G, ll_out, s);
+    }
+    a.part_lse = w.part_lse;
+    if (argmax) {
+        a.part_arg = w.part_arg;
+        a.part_max = w.part_max;
+    }
+    if (lk_launch(p, a, LK_SWEEP1, G, s) != hipSuccess) return GMM_E_HIP;
+    const int M = merge_grid(p);
+    hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
+                       (const int*)w.part_arg, (const float*)w.part_max, w.part_ll, lse, argmax);
+    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
+    return lk_sum(p, w, M, G, ll_out, s);
+}
+
+}  // namespace gmm

@@ -10,6 +10,7 @@ namespace gmm {
 
 enum Path : int {
     PATH_DIAG_F32 = 0,   // diagonal, fp32 MFMA scores and statistics, K <= 64
+    PATH_LARGEK = 1,     // isotropic / diagonal, X in bf16 or fp16, fp16 MFMA, K <= 4096
 };
 
 struct Plan {
@@ -30,9 +31,14 @@ struct Plan {
     size_t off_part, off_part_ll;     // per-workgroup partial statistics
     size_t off_stats, off_ll;         // reduced statistics and LL
     size_t off_diag;                  // status flags, counters
-    size_t off_chunk;                 // per-(component, dimension chunk) sums
+    size_t off_chunk;                 // per-(component, dimension chunk) sums;
+                                      // large K: per-component score constants
+    size_t off_lse, off_arg;          // large K, two sweeps: per-(slice, point) LSE,
+                                      // argmax and maximum
     size_t total;
     int64_t ncols;                    // statistic columns per component
+    int lk_slices;                    // large K: 256-component slices
+    int lk_kpad;                      // large K: K padded to whole slices
 };
 
 gmm_status make_plan(const gmm_desc* desc, Plan* plan);
@@ -48,5 +54,14 @@ gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* v
 gmm_status diag_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
                        int32_t* argmax, hipStream_t s);
 int device_cu_count();
+
+// Entry points of the large-K family (largek_params.hip, largek.hip).
+gmm_status lk_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
+                      const float* var, hipStream_t s);
+gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s);
+gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var,
+                       hipStream_t s);
+gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
+                     int32_t* argmax, hipStream_t s);
 
 }  // namespace gmm

@@ -36,7 +36,7 @@ class Desc(ctypes.Structure):
 class Diag(ctypes.Structure):
     _fields_ = [("bad_params", ctypes.c_int32), ("not_pd", ctypes.c_int32),
                 ("ridge_retries", ctypes.c_int32), ("empty", ctypes.c_int32),
-                ("nonfinite", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("nonfinite", ctypes.c_int32), ("x_range", ctypes.c_int32), ("ill_cond", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("ll", ctypes.c_double)]
 
 
