@@ -3,15 +3,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Prints ONE JSON line.  A step is one EM iteration over the whole synthetic
-workload, already resident in HBM: the fused E+M kernel over all points,
-then the reduction / M-step / next-iteration preprocessing kernel.
+workload, already resident in HBM: the fused E+M kernel(s) over all points,
+then the reduction / M-step kernel.  Workloads specified as a single EM
+iteration time every step from the initial parameters (gmm_prepare is then
+part of the step); the others chain the iterations.
 
 The default workload is the diagonal fp32 mixture with 1e6 points, D=64,
 K=16.  `value` is EM iterations/s; points*components/s and the achieved HBM
 bandwidth are reported beside it.  `roofline` prices the dominant kernel
-(the fused E+M kernel) with its algorithmic work (8*D*K flops per point for a
-diagonal covariance) against the dense fp32 matrix peak, timed with HIP events
-recorded on the stream the kernel runs on.  `cpu_baseline` times the fp64
+(gmm_em_step: the fused E+M kernel, or for more than 256 components the two
+sweeps and the slice merge, plus the small scan / panel / LL-sum launches) with
+its algorithmic work (8*D*K flops per point diagonal, 4*D*K isotropic)
+against the dense peak of the contraction's operand type (fp32 matrix for the
+fp32 family, fp16 for the large-K family), timed with HIP events recorded on
+the stream the kernels run on.  `cpu_baseline` times the fp64
 oracle on a bounded prefix of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -53,14 +58,15 @@ def cpu_baseline(w, x_dev, theta, target_s=12.0):
     import oracle
     pi, mu, cov = theta
     p = oracle.Params(pi, mu, cov, w.cov)
-    m = 1 << 14
+    # calibration prefix: about 2 s of oracle work (cost ~ points * K * D)
+    m = int(min(1 << 14, max(256, 3e8 / (w.k * w.d))))
     with threadpool_limits(limits=1):
         xs = x_dev[:m].double().cpu().numpy()
         t = time.perf_counter()
         oracle.em_step(xs, p)
         dt = time.perf_counter() - t
         m2 = int(min(w.n, max(m, m * target_s / max(dt, 1e-3))))
-        m2 = max(m, (m2 // 1024) * 1024)
+        m2 = max(m, (m2 // 256) * 256)
         xs = x_dev[:m2].double().cpu().numpy()
         t = time.perf_counter()
         oracle.em_step(xs, p)
@@ -79,6 +85,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="diag-f32-n1e6-d64-k16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--from-init", choices=("auto", "yes", "no"), default="auto",
+                    help="time every step from the initial parameters (prepare + em_step + "
+                         "finalize); auto: for workloads specified as one EM iteration")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy a buffer of the size of X once (a plain copy kernel "
                          "whose HBM counters calibrate FETCH_SIZE / WRITE_SIZE)")
@@ -92,6 +101,7 @@ def main(argv=None):
     from soft_clustering_amd import gmm, synth
 
     w = synth.WORKLOADS[a.workload]
+    from_init = a.from_init == "yes" or (a.from_init == "auto" and w.iters == 1)
     mix = synth.make_mixture(w)
     x = synth.sample_points(w, mix, device="cuda")
     pi0, mu0, cov0 = synth.init_params(w, x)
@@ -105,6 +115,8 @@ def main(argv=None):
     torch.cuda.synchronize()
     gm.prepare(pi, mu, cov)
     for i in range(a.warmup):
+        if from_init:
+            gm.prepare(pi, mu, cov)
         gm.em_step(x, lls[i:i + 1])
         gm.finalize(po, mo, co)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -114,6 +126,8 @@ def main(argv=None):
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(a.steps):
+        if from_init:
+            gm.prepare(pi, mu, cov)
         ev[i][0].record(stream)
         gm.em_step(x, lls[a.warmup + i:a.warmup + i + 1])
         ev[i][1].record(stream)
@@ -127,7 +141,8 @@ def main(argv=None):
     fused_avg = float(np.mean(fused_ms))
 
     flops, nbytes = algorithmic_work(w)
-    peak_key = "f32_matrix" if w.x_dtype == "f32" or w.cov == "diag" and w.k <= 64 else w.x_dtype
+    fp32_path = w.cov == "diag" and w.k <= 64          # fp32 MFMA family
+    peak_key = "f32_matrix" if fp32_path else "f16"    # else fp16 MFMA operands
     achieved_tflops = flops / (fused_avg * 1e-3) / 1e12
     hbm = nbytes / (fused_avg * 1e-3) / 1e9
     t_mfma = flops / (PEAK_TFLOPS[peak_key] * 1e12)
@@ -138,7 +153,15 @@ def main(argv=None):
     else:
         roof = {"bound": "hbm", "achieved": hbm, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": hbm / PEAK_HBM_GBPS, "traffic": None}
-    roof.update({"kernel": "k_diag_fused", "avg_launch_ms": fused_avg,
+    if fp32_path:
+        kname = "k_diag_fused (+ k_sum_ll)"
+    elif w.k <= 256:
+        kname = "k_lk<fused E+M> (+ k_lk_scan, k_lk_centre, k_lk_panel, k_lk_sum)"
+    else:
+        kname = ("k_lk<sweep 1> + k_lk_merge + k_lk<sweep 2> "
+                 "(+ k_lk_scan, k_lk_centre, k_lk_panel, k_lk_sum)")
+    roof.update({"kernel": kname, "timed": "gmm_em_step (all its launches), HIP events on its stream",
+                 "avg_launch_ms": fused_avg,
                  "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
                  "hbm_GBps": hbm, "hbm_frac": hbm / PEAK_HBM_GBPS})
 
@@ -154,10 +177,13 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "f16": "f16"}[w.x_dtype],
+        "dtype": "f32" if fp32_path else "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "d": w.d, "k": w.k, "cov": w.cov,
                    "x_dtype": w.x_dtype, "parallelism": "single-gpu"},
+        "steps_from": "initial parameters (every step)" if from_init else "previous step",
+        "em_step_ms": fused_avg,
+        "finalize_ms": ms_step - fused_avg,
         "points_components_per_s": w.n * w.k * 1000.0 / ms_step,
         "wall_s": wall,
         "ll_first_last": [float(ll_hist[0]), float(ll_hist[-1])],

@@ -84,9 +84,10 @@ typedef struct {
     int32_t ridge_retries;   /* full covariance: largest escalation count */
     int32_t empty;           /* components with s0 < 1e-6 at the last finalize */
     int32_t nonfinite;       /* 1 if the last LL or statistics were NaN/Inf */
-    int32_t x_range;         /* fp16-operand kernels: 1 if the last pass met a
-                                value of X that is NaN or whose scaled square
-                                exceeded the fp16 range (it was clamped) */
+    int32_t x_range;         /* fp16-operand diagonal kernels: 1 if the last
+                                pass met a value of X whose scaled square
+                                exceeded the fp16 range (it was clamped); NaN
+                                in X shows up as a non-finite LL */
     int32_t ill_cond;        /* fp16-operand kernels: components whose expanded
                                 score [x^2, x] . panel is estimated to carry
                                 more than 4 nats of rounding error near their

@@ -35,7 +35,7 @@ FLAGS = [
 
 # Translation units whose kernels never test floats for NaN: IEEE mode off
 # lets max/min fold into DPP forms (one v_max_f32_dpp per reduction step).
-NO_IEEE = {"diag_fused.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+NO_IEEE = {f: ["-mno-amdgpu-ieee", "-fno-honor-nans"] for f in ("diag_fused.hip", "largek.hip")}
 
 
 def _compile(src: str, asm_dir: str | None) -> str:

@@ -29,6 +29,8 @@
 // of the waves' per-point (max, sum).  The slices of one point chunk are
 // mapped to one XCD so X is read from HBM once and re-read from that L2.
 
+#include <type_traits>
+
 #include "largek_internal.h"
 
 namespace gmm {
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
                 for (int fc = 0; fc < DP / 16; ++fc) acc[kb][f][fc] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     double ll2 = 0.0;
-    bool bad = false;
+    float sqmax = 0.0f;   // largest (y')^2 staged (diag): above the fp16 maximum it was clamped
 
     // ---- staging: item (row pair rp, 8-column block cb) per thread
     const bool item_on = tid < Sh::kItems;
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
             raw1 = load8(xb + (p0 + r1) * a.ldx, cc, d, a.vec);
         }
         if constexpr (MODE == LK_SWEEP2) {
-            if (tid < kT) lse_pf = p0 + tid < n ? a.lse_in[p0 + tid] : 0.0f;
+            if (tid < kT) lse_pf = p0 + tid < n ? a.lse_in[p0 + tid] : INFINITY;   // gamma = 0
         }
     };
 
@@ -200,37 +202,42 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
             uint32_t hy[2][4], hq[2][4];
             float yy[2];
             const uint4 rw[2] = {raw0, raw1};
+            // rows beyond N and columns beyond D are zeroed only on ragged tiles
+            auto stage_rows = [&](auto masked) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool row_ok = 2 * rp + h < rows_in;
-                const uint32_t wv[4] = {rw[h].x, rw[h].y, rw[h].z, rw[h].w};
-                float yp[8], ss = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
-                    const float xf = h16_to_f32<BF16>(bits);
-                    const float2 cs = dsc_l[col0 + e];
-                    const float y = (row_ok && col0 + e < d) ? xf - cs.x : 0.0f;
-                    ss = fmaf(y, y, ss);
-                    yp[e] = y * cs.y;
-                }
-                yy[h] = ss;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) hy[h][q] = pack_h2(yp[2 * q], yp[2 * q + 1]);
-                if constexpr (!kIso) {
-                    float y2[8];
+                for (int h = 0; h < 2; ++h) {
+                    const bool row_ok = 2 * rp + h < rows_in;
+                    const uint32_t wv[4] = {rw[h].x, rw[h].y, rw[h].z, rw[h].w};
+                    float yp[8], ss = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float v = yp[e] * yp[e];
-                        bad |= !(v <= kF16Max);
-                        y2[e] = fminf(v, kF16Max);
+                        const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
+                        const float2 cs = dsc_l[col0 + e];
+                        float y = h16_to_f32<BF16>(bits) - cs.x;
+                        if constexpr (decltype(masked)::value) y = (row_ok && col0 + e < d) ? y : 0.0f;
+                        if constexpr (kIso) ss = fmaf(y, y, ss);
+                        yp[e] = y * cs.y;
                     }
+                    yy[h] = ss;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) hq[h][q] = pack_h2(y2[2 * q], y2[2 * q + 1]);
-                } else {
+                    for (int q = 0; q < 4; ++q) hy[h][q] = pack_h2(yp[2 * q], yp[2 * q + 1]);
+                    if constexpr (!kIso) {
+                        float y2[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bad |= !(fabsf(yp[e]) <= kF16Max);
+                        for (int e = 0; e < 8; ++e) {
+                            const float v = yp[e] * yp[e];
+                            sqmax = fmaxf(sqmax, v);
+                            y2[e] = fminf(v, kF16Max);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) hq[h][q] = pack_h2(y2[2 * q], y2[2 * q + 1]);
+                    }
                 }
+            };
+            if (rows_in == kT && d == DP) stage_rows(std::false_type{});
+            else stage_rows(std::true_type{});
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
                 const int r = 2 * rp + h;
                 *reinterpret_cast<uint4*>(rm + r * Sh::kRowRM + col0) =
                     make_uint4(hy[h][0], hy[h][1], hy[h][2], hy[h][3]);
@@ -333,29 +340,36 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
         float lse_me = 0.0f;   // lanes j < 8: point 16 (j >> 2) + 4 g + (j & 3)
         int arg_me = 0;
         const int pt_me = 16 * (j >> 2) + 4 * g + (j & 3);
+        float mw[2][4];   // this wave's per-point shift (fused E+M: reused for gamma)
         if constexpr (kExchange) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float mx = sc[rb][0][r];
-                    int bi = kbase + j;
 #pragma unroll
-                    for (int kb = 1; kb < KB; ++kb) {
-                        if (sc[rb][kb][r] > mx) bi = kbase + 16 * kb + j;
-                        mx = fmaxf(mx, sc[rb][kb][r]);
-                    }
+                    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, sc[rb][kb][r]);
                     const float m = row16_max(mx);
                     const float ms = m == -INFINITY ? 0.0f : m;
+                    mw[rb][r] = ms;
                     float zz = 0.0f;
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) zz += fast_exp2(sc[rb][kb][r] - ms);
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const float e = fast_exp2(sc[rb][kb][r] - ms);
+                        if constexpr (kStats) sc[rb][kb][r] = e;   // exp(S - m_w), reused for gamma
+                        zz += e;
+                    }
                     const float z = row16_sum(zz);
-                    int arg = 0;
-                    if (want_arg) arg = row16_min_i(mx == m ? bi : 0x7FFFFFFF);
-                    if (j == 0) {
-                        wpart[w][16 * rb + 4 * g + r] = make_float2(m, z);
-                        if (want_arg) warg[w][16 * rb + 4 * g + r] = arg;
+                    if (j == 0) wpart[w][16 * rb + 4 * g + r] = make_float2(m, z);
+                    if constexpr (!kStats) {
+                        if (want_arg) {   // lowest component among this wave's maxima
+                            int bi = 0x7FFFFFFF;
+#pragma unroll
+                            for (int kb = KB - 1; kb >= 0; --kb)
+                                if (sc[rb][kb][r] == m) bi = kbase + 16 * kb + j;
+                            const int arg = row16_min_i(bi);
+                            if (j == 0) warg[w][16 * rb + 4 * g + r] = arg;
+                        }
                     }
                 }
             __syncthreads();
@@ -414,15 +428,27 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
 
         // ---- responsibilities and statistics (registers -> MFMA)
         if constexpr (kStats) {
+            if constexpr (MODE == LK_FUSED_EM) {
+                // gamma = exp(S - m_w) * exp(m_w - lse); zero for rows beyond N
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool valid = prow + 16 * rb + 4 * g + r < n;
+                    for (int r = 0; r < 4; ++r) {
+                        const bool valid = prow + 16 * rb + 4 * g + r < n;
+                        const float f = valid ? fast_exp2(mw[rb][r] - lse2[rb][r]) : 0.0f;
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        sc[rb][kb][r] = valid ? fast_exp2(sc[rb][kb][r] - lse2[rb][r]) : 0.0f;
-                }
+                        for (int kb = 0; kb < KB; ++kb) sc[rb][kb][r] *= f;
+                    }
+            } else {
+                // sweep 2: lse is +inf for rows beyond N, so gamma = 0 there
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+                            sc[rb][kb][r] = fast_exp2(sc[rb][kb][r] - lse2[rb][r]);
+            }
             half8 ga[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -460,7 +486,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
     }
 
     // ---- epilogue: per-workgroup partials, one writer per value
-    const int flag = __syncthreads_or(bad ? 1 : 0);
+    const int flag = __syncthreads_or(sqmax > kF16Max ? 1 : 0);
     if (tid == 0) a.part_flag[blockIdx.x] = flag;
     if constexpr (kStats) {
         const int ncol = kIso ? 2 + d : 1 + 2 * d;
