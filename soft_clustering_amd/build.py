@@ -37,10 +37,15 @@ FLAGS = [
 # lets max/min fold into DPP forms (one v_max_f32_dpp per reduction step).
 NO_IEEE = {f: ["-mno-amdgpu-ieee", "-fno-honor-nans"] for f in ("diag_fused.hip", "largek.hip")}
 
+# The full-covariance forward solve must unroll completely (its z vector lives
+# in registers); the default size cap for requested unrolling stops at D = 64.
+EXTRA = {"full_fused.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+
 
 def _compile(src: str, asm_dir: str | None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *NO_IEEE.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    base = os.path.basename(src)
+    cmd = [HIPCC, *FLAGS, *NO_IEEE.get(base, []), *EXTRA.get(base, []), "-c", src, "-o", obj]
     if asm_dir:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)

@@ -7,6 +7,7 @@
 
 #include "common.h"
 #include "diag_internal.h"
+#include "full_internal.h"
 #include "largek_internal.h"
 
 namespace gmm {
@@ -123,6 +124,31 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->total = off;
         return GMM_OK;
     }
+    if (p->cov == GMM_COV_FULL && p->xdt == GMM_F16) {
+        // full covariance: fp16 X / mu / L, fp32 forward solve, fp16 MFMA second moments
+        if (p->d > 64 || p->k > kFullKP) return GMM_E_UNSUPPORTED;
+        int dp = pad_dim(p->d);
+        const int64_t tiles = (p->n + kFullT - 1) / kFullT;
+        p->path = PATH_FULL;
+        p->dp = dp;
+        p->kb = 1;
+        p->p_max = (int)(tiles < 1 ? 1 : (tiles > 256 ? 256 : tiles));
+        p->ncols = 1 + p->d + p->d * p->d;
+        const int64_t ncolp = full_ncolp(p->d);
+        p->off_pi = take(sizeof(float) * p->k);
+        p->off_mu = take(sizeof(float) * p->k * p->d);
+        p->off_cov = take(sizeof(float) * p->k * p->d * p->d);
+        p->off_panel = take(sizeof(uint16_t) * kFullKP * full_l_halves(dp));
+        p->off_shift = take(sizeof(float) * (2 * kFullKP * dp + 2 * kFullKP));
+        p->off_part = take(sizeof(double) * (size_t)p->p_max * kFullKP * ncolp);
+        p->off_part_ll = take(sizeof(double) * kFullLLSlots);
+        p->off_chunk = take(sizeof(double) * p->k * ncolp);
+        p->off_stats = take(sizeof(double) * p->k * p->ncols);
+        p->off_ll = take(sizeof(double));
+        p->off_diag = take(sizeof(int) * (2 * p->k + 4));
+        p->total = off;
+        return GMM_OK;
+    }
     return GMM_E_UNSUPPORTED;
 }
 
@@ -156,6 +182,7 @@ gmm_status gmm_prepare(const gmm_desc* desc, void* ws, size_t ws_bytes, const fl
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (pi == nullptr || mu == nullptr || cov == nullptr) return GMM_E_ARG;
     if (p.path == PATH_LARGEK) return lk_prepare(p, (char*)ws, pi, mu, cov, stream);
+    if (p.path == PATH_FULL) return full_prepare(p, (char*)ws, pi, mu, cov, stream);
     return diag_prepare(p, (char*)ws, pi, mu, cov, stream);
 }
 
@@ -167,6 +194,7 @@ gmm_status gmm_em_step(const gmm_desc* desc, void* ws, size_t ws_bytes, const vo
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (x == nullptr || p.n < 1) return GMM_E_ARG;
     if (p.path == PATH_LARGEK) return lk_em_step(p, (char*)ws, x, ll_out, stream);
+    if (p.path == PATH_FULL) return full_em_step(p, (char*)ws, x, ll_out, stream);
     return diag_em_step(p, (char*)ws, x, ll_out, stream);
 }
 
@@ -178,6 +206,7 @@ gmm_status gmm_finalize(const gmm_desc* desc, void* ws, size_t ws_bytes, float* 
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (p.n < 1) return GMM_E_ARG;
     if (p.path == PATH_LARGEK) return lk_finalize(p, (char*)ws, pi_out, mu_out, cov_out, stream);
+    if (p.path == PATH_FULL) return full_finalize(p, (char*)ws, pi_out, mu_out, cov_out, stream);
     return diag_finalize(p, (char*)ws, pi_out, mu_out, cov_out, stream);
 }
 
@@ -191,6 +220,8 @@ gmm_status gmm_loglik(const gmm_desc* desc, void* ws, size_t ws_bytes, const voi
     if (x == nullptr && p.n > 0) return GMM_E_ARG;
     if (p.path == PATH_LARGEK)
         return lk_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
+    if (p.path == PATH_FULL)
+        return full_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
     return diag_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
 }
 
@@ -209,7 +240,8 @@ gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes, 
     if (s1 && e == hipSuccess)
         e = hipMemcpy2DAsync(s1, sizeof(double) * p.d, base + sizeof(double), pitch,
                              sizeof(double) * p.d, p.k, hipMemcpyDeviceToDevice, stream);
-    const int64_t w2 = p.cov == GMM_COV_ISO ? 1 : p.d;   // iso: sum gamma |x|^2
+    // diag: sum gamma x^2 [D]; iso: sum gamma |x|^2 [1]; full: sum gamma x x^T [D*D]
+    const int64_t w2 = p.cov == GMM_COV_ISO ? 1 : (p.cov == GMM_COV_FULL ? p.d * p.d : p.d);
     if (s2 && e == hipSuccess)
         e = hipMemcpy2DAsync(s2, sizeof(double) * w2, base + sizeof(double) * (1 + p.d), pitch,
                              sizeof(double) * w2, p.k, hipMemcpyDeviceToDevice, stream);

@@ -1,0 +1,317 @@
+// Full-covariance family: batched ridged Cholesky (parameter preparation),
+// reduction of the fused kernel's partials, M-step, and the host entry points.
+//
+// Preparation ([LP-GMM] 3.1 Preprocess; 1.2 route 2; 4.1 ridge; 2.1 storage):
+// per component C~ = C + eps I with eps = ridge_rel |tr C| / D, L = chol(C~)
+// in fp64; on a pivot that is not positive (or not finite) eps becomes
+// max(10 eps, 1e-3 |tr C| / D) and the factorisation is repeated, at most 3
+// times, after which the component is flagged not positive definite and its
+// weight is treated as 0.  L is scaled by 2^-e_k (2^e_k near sqrt(|tr C|/D))
+// and stored in fp16; log|C~| = 2 sum log L_ii is taken from the rounded
+// factor, so the density matches the L the solve uses.  The mean is stored
+// in fp16 as the solve's centre.
+// M-step ([Flash-GMM] Method): pi' = s0/N, mu' = s1/s0,
+// C' = sum gamma (x - mu')(x - mu')^T / s0, here from the second moment
+// about the stored centre: C' = M2/s0 - delta delta^T, delta = mu' - centre.
+// A component with s0 < 1e-6 keeps its mean and covariance.
+
+#include <math.h>
+
+#include "full_internal.h"
+
+namespace gmm {
+
+namespace {
+
+constexpr int kRidgeRetries = 3;
+constexpr double kRidgeEscalate = 1e-3;   // escalation floor, relative to |tr C| / D
+
+__global__ __launch_bounds__(256) void k_full_load(int k_real, int d, const float* pi,
+                                                   const float* mu, const float* cov, float* th_pi,
+                                                   float* th_mu, float* th_cov, int* flags) {
+    const int k = blockIdx.x;
+    for (int i = threadIdx.x; i < d * d; i += blockDim.x)
+        th_cov[(int64_t)k * d * d + i] = cov[(int64_t)k * d * d + i];
+    for (int i = threadIdx.x; i < d; i += blockDim.x) th_mu[(int64_t)k * d + i] = mu[(int64_t)k * d + i];
+    if (threadIdx.x == 0) {
+        const float pk = pi[k];
+        th_pi[k] = pk;
+        flags[k] = (!(pk >= 0.0f) || !isfinite(pk)) ? 1 : 0;
+        flags[k_real + k] = 0;
+        if (k == 0) flags[2 * k_real] = flags[2 * k_real + 1] = 0;
+    }
+}
+
+// One workgroup per padded component (256 threads).  The factorisation is
+// right-looking on the lower triangle of C~ (fp64, LDS), one column per step.
+template <int DP>
+__global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridge_rel,
+                                                   const float* pi, const float* mu,
+                                                   const float* cov, uint16_t* lpk, float* pdiag,
+                                                   float* muh, float* cvec, float* rscale,
+                                                   int* flags) {
+    __shared__ double A[DP][DP + 1];
+    __shared__ double red[256];
+    __shared__ int fail;
+    const int k = blockIdx.x, tid = threadIdx.x;
+    constexpr int LH = full_l_halves(DP);
+    uint16_t* Lk = lpk + (int64_t)k * LH;
+    auto put_identity = [&]() {
+        for (int i = tid; i < LH; i += 256) Lk[i] = 0;
+        for (int i = tid; i < DP; i += 256) pdiag[k * DP + i] = 1.0f;
+    };
+    if (k >= k_real) {   // padding component
+        put_identity();
+        for (int i = tid; i < DP; i += 256) muh[k * DP + i] = 0.0f;
+        if (tid == 0) {
+            cvec[k] = -INFINITY;
+            rscale[k] = 1.0f;
+        }
+        return;
+    }
+    const float* C = cov + (int64_t)k * d * d;
+    // |trace| / D and the bad-parameter check (non-finite entries of the lower triangle)
+    double tr = 0.0, bad = 0.0;
+    for (int i = tid; i < d; i += 256) tr += (double)C[(int64_t)i * d + i];
+    for (int i = tid; i < d * d; i += 256) {
+        const int r = i / d, c = i % d;
+        if (c <= r && !isfinite(C[i])) bad = 1.0;
+    }
+    tr = block_sum_f64(tr, red);
+    bad = block_sum_f64(bad, red);
+    const double scale = fabs(tr) / (double)d;
+    double eps = (double)ridge_rel * scale;
+    int attempt = 0;
+    bool ok = false;
+    for (; attempt <= kRidgeRetries; ++attempt) {
+        for (int i = tid; i < DP * DP; i += 256) {
+            const int r = i / DP, c = i % DP;
+            double v = 0.0;
+            if (c <= r) {
+                if (r < d) v = (double)C[(int64_t)r * d + c] + (r == c ? eps : 0.0);
+                else v = (r == c) ? 1.0 : 0.0;   // padded dimensions: identity
+            }
+            A[r][c] = v;
+        }
+        if (tid == 0) fail = 0;
+        __syncthreads();
+        for (int jc = 0; jc < DP; ++jc) {
+            if (tid == 0) {
+                const double piv = A[jc][jc];
+                if (!(piv > 0.0) || !isfinite(piv)) fail = 1;
+                else A[jc][jc] = sqrt(piv);
+            }
+            __syncthreads();
+            if (fail) break;
+            const double ljj = A[jc][jc];
+            for (int i = jc + 1 + tid; i < DP; i += 256) A[i][jc] /= ljj;
+            __syncthreads();
+            // trailing update of the lower triangle: A[i][c] -= L[i][jc] L[c][jc], jc < c <= i
+            const int m = DP - jc - 1;
+            for (int q = tid; q < m * m; q += 256) {
+                const int i = jc + 1 + q / m, c = jc + 1 + q % m;
+                if (c <= i) A[i][c] -= A[i][jc] * A[c][jc];
+            }
+            __syncthreads();
+        }
+        if (!fail) {
+            ok = true;
+            break;
+        }
+        eps = fmax(10.0 * eps, kRidgeEscalate * scale);
+        __syncthreads();
+    }
+    if (!ok || bad > 0.0) {
+        put_identity();
+        for (int i = tid; i < DP; i += 256) muh[k * DP + i] = 0.0f;
+        if (tid == 0) {
+            cvec[k] = -INFINITY;
+            rscale[k] = 1.0f;
+            flags[k] |= (bad > 0.0 ? 1 : 0) | (ok ? 0 : 2);
+            flags[k_real + k] = attempt > kRidgeRetries ? kRidgeRetries : attempt;
+        }
+        return;
+    }
+    // scale 2^-e with 2^e near sqrt(|tr| / D); fp16 factor, its reciprocal diagonal, log-det
+    int e = 0;
+    if (scale > 0.0 && isfinite(scale)) {
+        e = ilogb(sqrt(scale));
+        e = e < -60 ? -60 : (e > 60 ? 60 : e);
+    }
+    const double sc = ldexp(1.0, -e);
+    double ld = 0.0;
+    for (int i = tid; i < DP; i += 256) {
+        const _Float16 h = (_Float16)(float)(A[i][i] * sc);
+        const float lf = (float)h;
+        pdiag[k * DP + i] = 1.0f / lf;
+        if (i < d) ld += log((double)lf);
+        const float m = i < d ? mu[(int64_t)k * d + i] : 0.0f;
+        muh[k * DP + i] = (float)(_Float16)m;
+        for (int c = 0; c < full_row_halves(i); ++c) {
+            const float v = c < i ? (float)(A[i][c] * sc) : 0.0f;
+            Lk[full_row_off(i) + c] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
+    }
+    ld = block_sum_f64(ld, red);
+    if (tid == 0) {
+        const double logdet = 2.0 * ld + 2.0 * (double)d * (double)e * kLn2;
+        const double lp = log((double)pi[k]);
+        cvec[k] = (float)(kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logdet)));
+        rscale[k] = (float)sc;
+        if (bad > 0.0) flags[k] |= 1;
+        flags[k_real + k] = attempt;
+    }
+}
+
+// Column sums of the partials over the workgroups, fixed order.  Grid
+// (ceil(ncolp / 256), K).
+__global__ __launch_bounds__(256) void k_full_reduce(const double* __restrict__ part, int P,
+                                                     int ncolp, double* __restrict__ colsum) {
+    const int k = blockIdx.y, col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= ncolp) return;
+    const double* src = part + (int64_t)k * ncolp + col;
+    const int64_t stride = (int64_t)kFullKP * ncolp;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int q = 0;
+    for (; q + 3 < P; q += 4) {
+        a0 += src[(int64_t)q * stride];
+        a1 += src[(int64_t)(q + 1) * stride];
+        a2 += src[(int64_t)(q + 2) * stride];
+        a3 += src[(int64_t)(q + 3) * stride];
+    }
+    for (; q < P; ++q) a0 += src[(int64_t)q * stride];
+    colsum[(int64_t)k * ncolp + col] = (a0 + a1) + (a2 + a3);
+}
+
+// M-step per component (grid K, 256 threads) and the raw statistics
+// [s0, s1 (D), sum gamma x x^T (D x D)].
+__global__ __launch_bounds__(256) void k_full_mstep(const double* __restrict__ colsum, int64_t n,
+                                                    int d, int dp, const float* __restrict__ muh,
+                                                    double* __restrict__ stats,
+                                                    float* __restrict__ th_pi,
+                                                    float* __restrict__ th_mu,
+                                                    float* __restrict__ th_cov, float* out_pi,
+                                                    float* out_mu, float* out_cov, int* flags) {
+    __shared__ double red[256];
+    const int k = blockIdx.x, tid = threadIdx.x;
+    const int ncolp = 1 + d + d * (d + 1) / 2;
+    const double* cs = colsum + (int64_t)k * ncolp;
+    const double s0 = cs[0];
+    const bool empty = !(s0 >= kEmptyNk);
+    double* st = stats + (int64_t)k * (1 + d + (int64_t)d * d);
+    double nonfin = isfinite(s0) ? 0.0 : 1.0;
+    for (int i = tid; i < d; i += 256) {
+        const double s1 = cs[1 + i];
+        st[1 + i] = s1;
+        if (!isfinite(s1)) nonfin = 1.0;
+        float mf = th_mu[(int64_t)k * d + i];
+        if (!empty) mf = (float)(s1 / s0);
+        th_mu[(int64_t)k * d + i] = mf;
+        if (out_mu) out_mu[(int64_t)k * d + i] = mf;
+    }
+    for (int q = tid; q < d * d; q += 256) {
+        const int i = q / d, c = q % d;
+        const int r0 = i > c ? i : c, c0 = i > c ? c : i;
+        const double m2 = cs[1 + d + tri_idx(r0, c0)];     // about the stored centre
+        const double ci = muh[k * dp + i], cc = muh[k * dp + c];
+        const double s1i = cs[1 + i], s1c = cs[1 + c];
+        // raw moment: sum g x x^T = M2 + c s1^T + s1 c^T - s0 c c^T
+        st[1 + d + q] = m2 + ci * s1c + s1i * cc - s0 * ci * cc;
+        if (!isfinite(m2)) nonfin = 1.0;
+        float v = th_cov[(int64_t)k * d * d + q];
+        if (!empty) {
+            const double di = s1i / s0 - ci, dc = s1c / s0 - cc;
+            v = (float)(m2 / s0 - di * dc);
+        }
+        th_cov[(int64_t)k * d * d + q] = v;
+        if (out_cov) out_cov[(int64_t)k * d * d + q] = v;
+    }
+    nonfin = block_sum_f64(nonfin, red);
+    if (tid == 0) {
+        st[0] = s0;
+        const float pf = (float)(s0 / (double)n);
+        th_pi[k] = pf;
+        if (out_pi) out_pi[k] = pf;
+        int f = flags[k] & 2;   // not-PD status of the parameters this pass used
+        if (!(pf >= 0.0f) || !isfinite(pf)) f |= 1 | 8;
+        if (nonfin > 0.0) f |= 8;
+        if (empty) f |= 4;
+        flags[k] = f;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_full_sum_ll(const double* part_ll, int P, double* ll_ws,
+                                                     double* ll_out, int* misc) {
+    __shared__ double red[256];
+    double v = 0.0;
+    for (int q = threadIdx.x; q < P; q += 256) v += part_ll[q];
+    v = block_sum_f64(v, red);
+    if (threadIdx.x == 0) {
+        *ll_ws = v;
+        if (ll_out) *ll_out = v;
+        misc[0] = isfinite(v) ? 0 : 1;
+    }
+}
+
+hipError_t chol(const Plan& p, const FullWs& w, hipStream_t s) {
+#define FULL_CHOL(DP_)                                                                            \
+    hipLaunchKernelGGL((k_full_chol<DP_>), dim3(kFullKP), dim3(256), 0, s, (int)p.k, (int)p.d,     \
+                       p.ridge_rel, w.pi, w.mu, w.cov, w.lpk, w.pdiag, w.muh, w.cvec, w.rscale,    \
+                       w.flags)
+    switch (p.dp) {
+        case 16: FULL_CHOL(16); break;
+        case 32: FULL_CHOL(32); break;
+        case 64: FULL_CHOL(64); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef FULL_CHOL
+    return hipGetLastError();
+}
+
+gmm_status sum_ll(const Plan& p, const FullWs& w, int P, double* ll_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_full_sum_ll, dim3(1), dim3(256), 0, s, w.part_ll, P, w.ll, ll_out,
+                       w.flags + 2 * p.k);
+    return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+}  // namespace
+
+gmm_status full_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
+                        const float* cov, hipStream_t s) {
+    FullWs w = full_ws(p, ws);
+    hipLaunchKernelGGL(k_full_load, dim3(p.k), dim3(256), 0, s, (int)p.k, (int)p.d, pi, mu, cov,
+                       w.pi, w.mu, w.cov, w.flags);
+    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
+    return chol(p, w, s) == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+gmm_status full_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
+    FullWs w = full_ws(p, ws);
+    const int G = full_grid(p);
+    if (full_launch_fused(p, w, x, true, G, nullptr, nullptr, s) != hipSuccess) return GMM_E_HIP;
+    return sum_ll(p, w, G, ll_out, s);
+}
+
+gmm_status full_finalize(const Plan& p, char* ws, float* pi, float* mu, float* cov,
+                         hipStream_t s) {
+    FullWs w = full_ws(p, ws);
+    const int G = full_grid(p);
+    const int ncolp = (int)full_ncolp(p.d);
+    hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 255) / 256, p.k), dim3(256), 0, s, w.part, G,
+                       ncolp, w.colsum);
+    hipLaunchKernelGGL(k_full_mstep, dim3(p.k), dim3(256), 0, s, w.colsum, p.n, (int)p.d, p.dp,
+                       w.muh, w.stats, w.pi, w.mu, w.cov, pi, mu, cov, w.flags);
+    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
+    return chol(p, w, s) == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
+                       int32_t* argmax, hipStream_t s) {
+    FullWs w = full_ws(p, ws);
+    if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
+    const int G = full_grid(p);
+    if (full_launch_fused(p, w, x, false, G, lse, argmax, s) != hipSuccess) return GMM_E_HIP;
+    return sum_ll(p, w, G, ll_out, s);
+}
+
+}  // namespace gmm

@@ -11,6 +11,7 @@ namespace gmm {
 enum Path : int {
     PATH_DIAG_F32 = 0,   // diagonal, fp32 MFMA scores and statistics, K <= 64
     PATH_LARGEK = 1,     // isotropic / diagonal, X in bf16 or fp16, fp16 MFMA, K <= 4096
+    PATH_FULL = 2,       // full covariance, X in fp16, fp16 L, fp32 solve, K <= 16, D <= 64
 };
 
 struct Plan {
@@ -63,5 +64,14 @@ gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var
                        hipStream_t s);
 gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
                      int32_t* argmax, hipStream_t s);
+
+// Entry points of the full-covariance family (full_params.hip, full_fused.hip).
+gmm_status full_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
+                        const float* cov, hipStream_t s);
+gmm_status full_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s);
+gmm_status full_finalize(const Plan& p, char* ws, float* pi, float* mu, float* cov,
+                         hipStream_t s);
+gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
+                       int32_t* argmax, hipStream_t s);
 
 }  // namespace gmm

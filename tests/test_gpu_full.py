@@ -1,0 +1,278 @@
+"""Parity of the full-covariance HIP path (X, mu and the Cholesky factor
+stored in fp16; forward solve, exp / log / normalisers and statistics in
+fp32) against the fp64 oracle.
+
+Gate for reduced-precision storage (the operator write-up's acceptance bar,
+section 2.3): LL(theta_t) relative error <= 9e-3 and argmax agreement
+>= 99.5%; parameters within loose SANITY bounds for components holding at
+least MIN_MASS points.  Both sides add the same ridge eps = ridge_rel |tr C|/D
+to the diagonal before factorising ([LP-GMM] 4.1).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from soft_clustering_amd import synth
+from tests import metrics
+from tests.gpu_common import params64, to_dev, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+LL_TOL = 9e-3
+ARGMAX_MIN = 0.995
+SANITY = {"s0": 1e-2, "pi": 1e-2, "mu": 2e-2, "cov": 5e-2}
+MIN_MASS = 20.0
+
+
+def gpu_step(gm, x, pi, mu, cov, prepare=True):
+    if prepare:
+        gm.prepare(pi, mu, cov)
+    ll = torch.zeros(1, dtype=torch.float64, device="cuda")
+    gm.em_step(x, ll)
+    po, mo, co = torch.empty_like(pi), torch.empty_like(mu), torch.empty_like(cov)
+    gm.finalize(po, mo, co)
+    st = gm.get_stats()
+    torch.cuda.synchronize()
+    return float(ll.item()), st, (po, mo, co)
+
+
+def gpu_loglik(gm, x, th):
+    gm.prepare(*th)
+    ll = torch.zeros(1, dtype=torch.float64, device="cuda")
+    lse = torch.full((gm.n,), float("nan"), device="cuda")
+    arg = torch.full((gm.n,), -1, dtype=torch.int32, device="cuda")
+    gm.loglik(x, ll, lse, arg)
+    torch.cuda.synchronize()
+    return float(ll.item()), lse.cpu().numpy(), arg.cpu().numpy()
+
+
+def check_reduced(ref, ll, st, theta, what=""):
+    heavy = np.asarray(ref.nk) >= MIN_MASS
+    cov_g = theta[2].cpu().numpy()
+    errs = {
+        "ll": metrics.rel(ll, ref.ll),
+        "s0": metrics.rel_inf(st.s0.cpu().numpy(), ref.nk),
+        "pi": metrics.rel_inf(theta[0].cpu().numpy(), ref.params.pi),
+        "mu": metrics.rel_inf(theta[1].cpu().numpy()[heavy], ref.params.mu[heavy]) if heavy.any() else 0.0,
+        "cov": max((metrics.rel_inf(cov_g[k], ref.params.cov[k]) for k in np.nonzero(heavy)[0]),
+                   default=0.0),
+        "s1": metrics.rel_inf(st.s1.cpu().numpy(), ref.s1),
+        "s2": metrics.rel_inf(st.s2.cpu().numpy(), ref.s2),
+    }
+    print(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if (k == "ll" and not v <= LL_TOL) or
+           (k in SANITY and not v <= SANITY[k])}
+    assert not bad, (what, bad)
+    return errs
+
+
+def check_argmax(xd, p, arg, lse=None, what="", ridge_rel=1e-3):
+    _, lse_ref, arg_ref = oracle.loglik(xd, p, ridge_rel=ridge_rel)
+    agree = float(np.mean(arg == arg_ref))
+    msg = f"argmax agreement {agree * 100:.3f}%"
+    if lse is not None:
+        msg += f", per-point lse max abs err {np.max(np.abs(lse - lse_ref)):.3e}"
+    print(what, msg, flush=True)
+    assert agree >= ARGMAX_MIN, (what, agree)
+
+
+def check_next_step(gm, xg, xd, th1, what="  second step"):
+    """Second iteration from the GPU's theta_1.  Components whose covariance
+    the oracle's ridged Cholesky cannot factorise (e.g. one that collapsed onto
+    a single point: C' = 0 and a zero ridge) must be the ones the library
+    reports as not positive definite; they carry weight 0 on the GPU, so the
+    reference is the oracle's step over the remaining components."""
+    covs = th1[2].double().cpu().numpy()
+    fail = []
+    for k in range(covs.shape[0]):
+        try:
+            oracle.ridged_cholesky(covs[k], 1e-3)
+        except oracle.NotPositiveDefinite:
+            fail.append(k)
+    dg = gm.diagnostics()   # flags of the factorisation of theta_1
+    print(f"{what}: not_pd gpu {dg.not_pd}, oracle failures {fail}", flush=True)
+    assert dg.not_pd == len(fail) and dg.nonfinite == 0 and dg.bad_params == 0
+    ll2, st2, th2 = gpu_step(gm, xg, *th1, prepare=False)
+    keep = np.array([k for k in range(covs.shape[0]) if k not in fail])
+    p1 = oracle.Params(*(t.double().cpu().numpy()[keep] for t in th1), "full")
+    ref2 = oracle.em_step(xd, p1)
+    st_k = type(st2)(st2.s0[keep], st2.s1[keep], st2.s2[keep])
+    check_reduced(ref2, ll2, st_k, tuple(t[keep] for t in th2), what=what)
+
+
+def _spd(rng, d, lo=-1.5, hi=1.5):
+    a = rng.standard_normal((d, d))
+    q, r = np.linalg.qr(a)
+    q = q * np.sign(np.diag(r))[None, :]
+    lam = 10.0 ** rng.uniform(lo, hi, size=d)
+    c = (q * lam) @ q.T
+    return 0.5 * (c + c.T)
+
+
+def _make(n, d, k, ldx_pad, misalign, seed):
+    rng = np.random.default_rng(seed)
+    kt = max(1, min(k, 16))
+    mu_t = rng.normal(0.0, 5.0, size=(kt, d))
+    covs = [_spd(rng, d) for _ in range(kt)]
+    z = rng.integers(0, kt, size=n)
+    xf = np.empty((n, d))
+    for c in range(kt):
+        idx = np.nonzero(z == c)[0]
+        xf[idx] = rng.multivariate_normal(mu_t[c], covs[c], size=idx.size)
+    ldx = d + ldx_pad
+    off = 1 if misalign else 0
+    buf = torch.zeros(n * ldx + off + 8, dtype=torch.float16)
+    xs = torch.as_strided(buf, (n, d), (ldx, 1), off)
+    xs.copy_(torch.from_numpy(xf.astype(np.float32)).to(torch.float16))
+    xg = torch.as_strided(buf.cuda(), (n, d), (ldx, 1), off)
+    idx = rng.choice(n, size=k, replace=(k > n))
+    mu0 = xs[torch.as_tensor(idx)].float().numpy()
+    pi0 = rng.dirichlet(np.ones(k)).astype(np.float32)
+    cov0 = np.stack([covs[i % kt] * rng.uniform(0.7, 1.5) for i in range(k)]).astype(np.float32)
+    return xs.double().numpy(), xg, ldx, (pi0, mu0, cov0)
+
+
+CASES = [
+    # n, d, k, ldx_pad, misalign
+    (1, 4, 1, 0, False),
+    (300, 8, 3, 0, False),
+    (2000, 17, 5, 3, True),
+    (5000, 32, 16, 0, False),
+    (4097, 64, 16, 0, False),
+    (3000, 64, 7, 8, False),
+    (2500, 48, 12, 0, True),
+]
+
+
+@pytest.mark.parametrize("n,d,k,ldx_pad,misalign", CASES,
+                         ids=[f"n{a}-d{b}-k{c}-pad{e}-mis{int(f)}" for a, b, c, e, f in CASES])
+def test_ragged_shapes(gmm_lib, n, d, k, ldx_pad, misalign):
+    xd, xg, ldx, th0 = _make(n, d, k, ldx_pad, misalign, seed=n * 7 + d * 3 + k)
+    gm = gmm_lib.Gmm(n, d, k, "full", "f16", ldx=ldx)
+    th = to_dev(*th0)
+    p = params64("full", *th)
+    ll_e, lse, arg = gpu_loglik(gm, xg, th)
+    check_argmax(xd, p, arg, lse, what=f"n{n} d{d} k{k} loglik")
+    ll, st, th1 = gpu_step(gm, xg, *th)
+    ref = oracle.em_step(xd, p)
+    check_reduced(ref, ll, st, th1, what="  em step")
+    assert abs(st.s0.sum().item() - n) <= 1e-3 * n
+    assert abs(ll_e - ll) <= 1e-6 * abs(ll) + 1e-6
+    if n <= d:   # the updated covariance is singular by construction (no ridge on 0)
+        return
+    check_next_step(gm, xg, xd, th1)
+
+
+def test_workload_shape_subset(gmm_lib):
+    """The full-covariance benchmark mixture (D=64, K=16, condition number up
+    to 1e3) on 20000 points: E-step argmax, one step, a second step."""
+    w, x, th0 = workload_inputs("full-f16-n1e6-d64-k16", n=20_000)
+    xd = x.double().numpy()
+    xg = x.cuda()
+    gm = gmm_lib.Gmm(w.n, w.d, w.k, "full", "f16")
+    th = to_dev(*th0)
+    p = params64("full", *th)
+    _, lse, arg = gpu_loglik(gm, xg, th)
+    check_argmax(xd, p, arg, lse, what="full subset loglik")
+    ll, st, th1 = gpu_step(gm, xg, *th)
+    check_reduced(oracle.em_step(xd, p), ll, st, th1, what="  em step")
+    check_next_step(gm, xg, xd, th1)
+
+
+def test_ridge_retry_and_not_pd(gmm_lib):
+    """Ridge escalation: with ridge_rel = 0 a covariance with a zero variance
+    fails its first pivot and factorises after one escalation, as the oracle's ridged
+    Cholesky does.  An indefinite covariance stays not positive definite after
+    three escalations: it is reported and its weight is treated as 0."""
+    rng = np.random.default_rng(21)
+    n, d, k = 3000, 16, 3
+    xd, xg, ldx, (pi0, mu0, cov0) = _make(n, d, k, 0, False, seed=21)
+    dv = rng.uniform(0.5, 2.0, size=d)
+    dv[3] = 0.0                                         # a zero variance: pivot exactly 0
+    cov0[1] = np.diag(dv).astype(np.float32)
+    th = to_dev(pi0, mu0, cov0)
+    gm = gmm_lib.Gmm(n, d, k, "full", "f16", ridge_rel=0.0)
+    gm.prepare(*th)
+    dg = gm.diagnostics()   # the factorisation of theta_0 (finalize refactorises theta_1)
+    ll, st, th1 = gpu_step(gm, xg, *th)
+    _, _, retries = oracle.ridged_cholesky(cov0[1].astype(np.float64), 0.0)
+    print("ridge retries gpu", dg.ridge_retries, "oracle", retries, flush=True)
+    assert retries == 1 and dg.ridge_retries == retries and dg.not_pd == 0
+    ref = oracle.em_step(xd, params64("full", *th), ridge_rel=0.0)
+    assert metrics.rel(ll, ref.ll) <= LL_TOL
+    # indefinite component 2: weight treated as 0
+    cov_bad = cov0.copy()
+    ev = np.ones(d, dtype=np.float32)
+    ev[5] = -5.0          # |tr|/D = 0.625: still indefinite with the largest ridge (|tr|/D)
+    cov_bad[2] = np.diag(ev)
+    th_bad = to_dev(pi0, mu0, cov_bad)
+    gm2 = gmm_lib.Gmm(n, d, k, "full", "f16")
+    ll_b, _, _ = gpu_loglik(gm2, xg, th_bad)
+    dg2 = gm2.diagnostics()
+    assert dg2.not_pd == 1 and dg2.ridge_retries == 3
+    keep = np.array([0, 1])
+    p_keep = oracle.Params(pi0[keep].astype(np.float64), mu0[keep].astype(np.float64),
+                           cov0[keep].astype(np.float64), "full")
+    ll_ref, _, _ = oracle.loglik(xd, p_keep)
+    print("not-PD LL gpu", ll_b, "oracle without the component", ll_ref, flush=True)
+    assert metrics.rel(ll_b, ll_ref) <= LL_TOL
+
+
+def test_single_component_closed_form(gmm_lib):
+    """K = 1: mu' is the sample mean and C' the population covariance."""
+    rng = np.random.default_rng(22)
+    n, d = 4000, 24
+    c = _spd(rng, d)
+    xf = rng.multivariate_normal(rng.normal(0, 3, d), c, size=n)
+    xb = torch.from_numpy(xf.astype(np.float32)).to(torch.float16)
+    xd = xb.double().numpy()
+    gm = gmm_lib.Gmm(n, d, 1, "full", "f16")
+    ll, st, th = gpu_step(gm, xb.cuda(), *to_dev(np.ones(1), np.zeros((1, d)), np.eye(d)[None]))
+    np.testing.assert_allclose(th[1].cpu().numpy()[0], xd.mean(0), rtol=1e-4, atol=1e-4)
+    emp = np.cov(xd.T, bias=True)
+    err = metrics.rel_inf(th[2].cpu().numpy()[0], emp)
+    print("K=1 covariance rel err", err, flush=True)
+    assert err <= 5e-3
+    assert th[0].item() == 1.0
+
+
+def test_determinism_bitwise(gmm_lib):
+    w, x, th0 = workload_inputs("full-f16-n1e6-d64-k16", n=100_003)
+    xg = x.cuda()
+    gm = gmm_lib.Gmm(w.n, w.d, w.k, "full", "f16")
+    out = []
+    for _ in range(2):
+        ll, st, th = gpu_step(gm, xg, *to_dev(*th0))
+        out.append((ll, st.s0.cpu(), st.s1.cpu(), st.s2.cpu(), *[t.cpu() for t in th]))
+    assert out[0][0] == out[1][0]
+    for a, b in zip(out[0][1:], out[1][1:]):
+        assert torch.equal(a, b)
+
+
+def test_full_size_workload(gmm_lib):
+    """1e6 points, D=64, K=16 in the benchmark's configuration: sum of s0 = N,
+    fused and E-only LL agree, per-point LSE / argmax on sampled points
+    against the oracle, at theta_0 and at theta_1."""
+    w = synth.WORKLOADS["full-f16-n1e6-d64-k16"]
+    mix = synth.make_mixture(w)
+    xg = synth.sample_points(w, mix, device="cuda")
+    th0 = synth.init_params(w, xg)
+    gm = gmm_lib.Gmm(w.n, w.d, w.k, "full", "f16")
+    th = to_dev(*th0)
+    ll, st, th1 = gpu_step(gm, xg, *th)
+    assert abs(st.s0.sum().item() - w.n) <= 1e-4 * w.n
+    idx = np.sort(np.random.default_rng(0).choice(w.n, 3000, replace=False))
+    xs = xg[torch.as_tensor(idx, device="cuda")].double().cpu().numpy()
+    for name, t in (("theta_0", th), ("theta_1", th1)):
+        ll_e, lse, arg = gpu_loglik(gm, xg, t)
+        if name == "theta_0":
+            assert metrics.rel(ll_e, ll) <= 1e-6
+        assert metrics.rel(np.sum(lse, dtype=np.float64), ll_e) <= 1e-5
+        ll_s, lse_ref, arg_ref = oracle.loglik(xs, params64("full", *t))
+        agree = float(np.mean(arg[idx] == arg_ref))
+        print(f"{name}: sampled LL rel {metrics.rel(np.sum(lse[idx], dtype=np.float64), ll_s):.2e}, "
+              f"lse max abs {np.max(np.abs(lse[idx] - lse_ref)):.3e}, argmax {agree * 100:.2f}%",
+              flush=True)
+        assert metrics.rel(np.sum(lse[idx], dtype=np.float64), ll_s) <= LL_TOL
+        assert agree >= ARGMAX_MIN
