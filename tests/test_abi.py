@@ -43,9 +43,18 @@ def test_bad_descriptors(kw):
     assert e.value.status == gmm.GMM_E_ARG
 
 
-def test_unsupported_shapes():
+@pytest.mark.parametrize("kw", [
+    dict(n=10, d=129, k=8),                                   # D > 128
+    dict(n=10, d=64, k=65),                                   # diagonal K > 64 with fp32 storage
+    dict(n=10, d=64, k=8, cov="iso"),                         # isotropic with fp32 storage
+    dict(n=10, d=64, k=4097, cov="diag", x_dtype="bf16"),     # K above the large-K limit
+    dict(n=10, d=65, k=8, cov="full", x_dtype="f16"),         # full covariance, D > 64
+    dict(n=10, d=64, k=17, cov="full", x_dtype="f16"),        # full covariance, K > 16
+    dict(n=10, d=16, k=4, cov="full", x_dtype="f32"),         # full covariance, fp32 storage
+])
+def test_unsupported_shapes(kw):
     with pytest.raises(gmm.GmmError) as e:
-        gmm.workspace_bytes(gmm.make_desc(10, 129, 8))
+        gmm.workspace_bytes(gmm.make_desc(**kw))
     assert e.value.status == gmm.GMM_E_UNSUPPORTED
 
 
@@ -57,6 +66,29 @@ def test_workspace_has_no_nk_term():
         sizes = [gmm.workspace_bytes(gmm.make_desc(n, d, k)) for n in (1 << 16, 10 ** 6, 10 ** 8, 10 ** 10)]
         assert len(set(sizes)) == 1, sizes
         assert sizes[0] < 10 ** 6 * k * 4 / 4
+
+
+@pytest.mark.parametrize("cov,x_dtype,n,d,k", [
+    ("iso", "bf16", 10 ** 7, 128, 256),        # large K, one sweep
+    ("diag", "bf16", 2 * 10 ** 8, 128, 1024),  # large K, two sweeps
+    ("full", "f16", 10 ** 6, 64, 16),          # full covariance
+])
+def test_workspace_far_below_nk(cov, x_dtype, n, d, k):
+    """The benchmark workloads' workspaces: the single-sweep and full paths
+    do not grow with N (per-workgroup partial slots are capped); the two-sweep
+    path keeps 12 bytes per point and 256-component slice, a small fraction of
+    the fp32 N x K matrix it replaces."""
+    ws = gmm.workspace_bytes(gmm.make_desc(n, d, k, cov, x_dtype))
+    if cov == "full":   # O(P K D^2): 256 partial slots of 16 x (1 + D + D(D+1)/2) fp64
+        assert ws <= 256 * 16 * (1 + d + d * (d + 1) // 2) * 8 + (8 << 20), ws
+    else:
+        assert ws < n * k * 4 / 20, (ws, n * k * 4)
+    ws10 = gmm.workspace_bytes(gmm.make_desc(10 * n, d, k, cov, x_dtype))
+    if k <= 256:
+        assert ws10 == ws
+    else:
+        slices = (k + 255) // 256
+        assert ws10 - ws == 9 * n * 12 * slices + (ws10 - ws) % 256   # linear in N, 12 B/point/slice
 
 
 def test_null_arguments_rejected_before_launch():
