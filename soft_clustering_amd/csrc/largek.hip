@@ -21,9 +21,10 @@
 // rounded to fp16; s0 (and the isotropic sum gamma |y|^2) in fp32 on the
 // vector unit from the unrounded gamma.
 //
-// Work split: a workgroup has four waves; each wave owns 64 components and
-// keeps their panel in registers, so a workgroup owns a slice of 256
-// components.  32-point tiles are staged once per workgroup into LDS (row-
+// Work split: a workgroup owns a slice of 256 components, split over its
+// waves (4 waves x 64 components, or 8 waves x 32 so that two waves share each
+// SIMD within the register budget); each wave keeps its components' panel in
+// registers.  32-point tiles are staged once per workgroup into LDS (row-
 // major y' / y'^2 for the score operand, transposed copies for the statistics
 // operand), double buffered, one barrier per tile plus one for the exchange
 // of the waves' per-point (max, sum).  The slices of one point chunk are
@@ -41,8 +42,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kT = kLkT;
-constexpr int KW = kLkKW;
-constexpr int KB = KW / 16;
 constexpr float kLn2f = 0.69314718055994530942f;
 
 template <int COV, int DP>
@@ -92,7 +91,11 @@ __device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ row, int col
 }
 
 template <int COV, int DP, int MODE, bool BF16>
-__global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
+__global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void k_lk(const LkArgs a) {
+    constexpr int WV = lk_waves(MODE, COV);          // waves per workgroup
+    constexpr int KW = kLkSlice / WV;           // components per wave
+    constexpr int KB = KW / 16;                 // 16-component blocks per wave
+    constexpr int NT = 64 * WV;                 // threads per workgroup
     using Sh = LkShape<COV, DP>;
     constexpr bool kIso = Sh::kIso;
     constexpr int KS = Sh::kKS, NF = Sh::kNF;
@@ -103,9 +106,9 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
     __shared__ float2 dsc_l[DP];
     __shared__ __attribute__((aligned(16))) float nx2[2][kT];     // |y|^2 per point (isotropic)
     __shared__ __attribute__((aligned(16))) float lse_t[2][kT];   // merged base-2 LSE (sweep 2)
-    __shared__ float2 wpart[kLkWaves][kT];   // per-wave (max, sum) of each point
-    __shared__ int warg[kLkWaves][kT];
-    __shared__ double llred[256];
+    __shared__ float2 wpart[WV][kT];   // per-wave (max, sum) of each point
+    __shared__ int warg[WV][kT];
+    __shared__ double llred[NT];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
     const int G = gridDim.x, S = a.S;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
         fs[kb] = a.fsc[k];
         pv[kb] = kIso ? a.pvec[k] : 0.0f;
     }
-    for (int i = tid; i < DP; i += 256) dsc_l[i] = a.dsc[i];
+    for (int i = tid; i < DP; i += NT) dsc_l[i] = a.dsc[i];
 
     // ---- this chunk's tiles
     const int64_t tiles = (n + kT - 1) / kT;
@@ -376,11 +379,11 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
             if (j < 8) {
                 float M = wpart[0][pt_me].x;
 #pragma unroll
-                for (int w2 = 1; w2 < kLkWaves; ++w2) M = fmaxf(M, wpart[w2][pt_me].x);
+                for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w2][pt_me].x);
                 const float Ms = M == -INFINITY ? 0.0f : M;
                 float Z = 0.0f;
 #pragma unroll
-                for (int w2 = 0; w2 < kLkWaves; ++w2) {
+                for (int w2 = 0; w2 < WV; ++w2) {
                     const float2 mz = wpart[w2][pt_me];
                     Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
                 }
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
                 if (want_arg) {
                     arg_me = 0x7FFFFFFF;
 #pragma unroll
-                    for (int w2 = kLkWaves - 1; w2 >= 0; --w2)
+                    for (int w2 = WV - 1; w2 >= 0; --w2)
                         if (wpart[w2][pt_me].x == M) arg_me = warg[w2][pt_me];
                 }
             }
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
                     if (want_arg) {
                         float M = wpart[0][pt_me].x;
 #pragma unroll
-                        for (int w2 = 1; w2 < kLkWaves; ++w2) M = fmaxf(M, wpart[w2][pt_me].x);
+                        for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w2][pt_me].x);
                         a.part_arg[(int64_t)slice * n + p] = arg_me;
                         a.part_max[(int64_t)slice * n + p] = M;
                     }
@@ -498,8 +501,8 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
             sred[((w * 4 + g) * KW + 16 * kb + j) * 2 + 1] = s2acc[kb];
         }
         __syncthreads();
-        {
-            const int kl = lane;   // one component per lane (KW == 64)
+        if (lane < KW) {
+            const int kl = lane;   // one component per lane
             const float* s = sred + (w * 4 * KW + kl) * 2;
             const double s0 = ((double)s[0] + (double)s[2 * KW]) + ((double)s[4 * KW] + (double)s[6 * KW]);
             double* o = dst + (int64_t)(w * KW + kl) * ncol;
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
     if constexpr (MODE == LK_FUSED_EM || MODE == LK_FUSED_E) {
         llred[tid] = ll2;
         __syncthreads();
-        for (int s2 = 128; s2 > 0; s2 >>= 1) {
+        for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
             if (tid < s2) llred[tid] += llred[tid + s2];
             __syncthreads();
         }
@@ -537,9 +540,9 @@ __global__ __launch_bounds__(256, 1) void k_lk(const LkArgs a) {
 template <int COV, int DP, int MODE>
 hipError_t launch3(const Plan& p, const LkArgs& a, int grid, hipStream_t s) {
     if (p.xdt == GMM_BF16)
-        hipLaunchKernelGGL((k_lk<COV, DP, MODE, true>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_lk<COV, DP, MODE, true>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
     else
-        hipLaunchKernelGGL((k_lk<COV, DP, MODE, false>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_lk<COV, DP, MODE, false>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
     return hipGetLastError();
 }
 

@@ -8,12 +8,9 @@
 
 namespace gmm {
 
-// Points per tile and waves per workgroup of the fused kernel.
+// Points per tile and components per workgroup (slice) of the fused kernel.
 constexpr int kLkT = 32;
-constexpr int kLkWaves = 4;
-// Components per wave: the wave keeps their score panel in registers.
-constexpr int kLkKW = 64;
-constexpr int kLkSlice = kLkWaves * kLkKW;   // components per workgroup (slice)
+constexpr int kLkSlice = 256;
 
 // Fused-kernel variants.
 enum LkMode : int {
@@ -107,9 +104,28 @@ struct LkArgs {
 // Statistic columns per component: diag [s0, s1(D), s2(D)], iso [s0, s1(D), s2].
 inline int64_t lk_ncols(int cov, int64_t d) { return cov == GMM_COV_ISO ? 2 + d : 1 + 2 * d; }
 
-// Workgroups of the fused kernel (chunks x slices), a function of the plan
-// and the device only.
-int lk_grid(const Plan& p);
+// Waves per workgroup of the fused kernel.  The isotropic statistics modes
+// split the slice over 8 waves of 32 components (under 256 registers per
+// lane, so two waves share a SIMD): 4.10 -> 3.71 ms on 1e7 x 128 x 256.  The
+// diagonal statistics modes keep 4 waves of 64 components: at D = 128 the
+// 8-wave variant spills and was slower (sweep 2 of 2e8 x 128 x 1024:
+// 362 -> 474 ms).  The modes without statistics use 4 waves and run two
+// workgroups per CU.
+__host__ __device__ constexpr int lk_waves(int mode, int cov) {
+    return ((mode == LK_FUSED_EM || mode == LK_SWEEP2) && cov == GMM_COV_ISO) ? 8 : 4;
+}
+
+// Workgroups per CU of the fused kernel: the modes without statistics
+// accumulators fit two workgroups (two waves per SIMD, so one wave's MFMAs
+// overlap the other's vector work and latencies); the statistics modes need
+// up to 512 registers per lane and run one.
+__host__ __device__ constexpr int lk_wg_per_cu(int mode) {
+    return (mode == LK_SWEEP1 || mode == LK_FUSED_E) ? 2 : 1;
+}
+
+// Workgroups of the fused kernel in `mode` (chunks x slices), a function of
+// the plan and the device only.
+int lk_grid(const Plan& p, int mode);
 
 // Launch the fused kernel in `mode` (largek.hip).
 hipError_t lk_launch(const Plan& p, const LkArgs& a, int mode, int grid, hipStream_t s);

@@ -422,16 +422,19 @@ gmm_status lk_sum(const Plan& p, const LkWs& w, int P, int Pf, double* ll_out, h
 
 }  // namespace
 
-// Grid: one workgroup per CU, chunks a multiple of 8 so that each chunk's
-// slices share an XCD; never more chunks than tiles or partial slots.
-int lk_grid(const Plan& p) {
+// Grid: lk_wg_per_cu(mode) workgroups per CU, chunks a multiple of 8 so that
+// each chunk's slices share an XCD; never more chunks than tiles, partial
+// slots (statistics modes) or LL / flag slots.
+int lk_grid(const Plan& p, int mode) {
     const int S = p.lk_slices;
     const int64_t tiles = (p.n + kLkT - 1) / kLkT;
-    int64_t chunks = device_cu_count() / S;
+    int64_t chunks = (int64_t)lk_wg_per_cu(mode) * device_cu_count() / S;
     if (chunks >= 8) chunks = chunks / 8 * 8;
     if (chunks < 1) chunks = 1;
     if (chunks > tiles) chunks = tiles < 1 ? 1 : tiles;
-    if (chunks * S > p.p_max) chunks = p.p_max / S;
+    const bool stats = mode == LK_FUSED_EM || mode == LK_SWEEP2;
+    const int64_t slots = stats ? p.p_max : kLkLLSlots;
+    if (chunks * S > slots) chunks = slots / S;
     return (int)(chunks * S);
 }
 
@@ -446,14 +449,15 @@ gmm_status lk_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
 gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
     LkWs w = lk_ws(p, ws);
     if (refresh_panel(p, w, x, s) != hipSuccess) return GMM_E_HIP;
-    const int G = lk_grid(p);
     LkArgs a = make_args(p, w, x);
     if (p.lk_slices == 1) {
+        const int G = lk_grid(p, LK_FUSED_EM);
         if (lk_launch(p, a, LK_FUSED_EM, G, s) != hipSuccess) return GMM_E_HIP;
         return lk_sum(p, w, G, G, ll_out, s);
     }
+    const int G1 = lk_grid(p, LK_SWEEP1), G = lk_grid(p, LK_SWEEP2);
     a.part_lse = w.part_lse;
-    if (lk_launch(p, a, LK_SWEEP1, G, s) != hipSuccess) return GMM_E_HIP;
+    if (lk_launch(p, a, LK_SWEEP1, G1, s) != hipSuccess) return GMM_E_HIP;
     const int M = merge_grid(p);
     hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
                        (const int*)nullptr, (const float*)nullptr, w.part_ll, (float*)nullptr,
@@ -462,12 +466,13 @@ gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hi
     a.part_lse = nullptr;
     a.lse_in = w.part_lse;
     if (lk_launch(p, a, LK_SWEEP2, G, s) != hipSuccess) return GMM_E_HIP;
-    return lk_sum(p, w, M, G, ll_out, s);
+    // range flags: sweep 1 wrote slots [0, G1), sweep 2 rewrote [0, G)
+    return lk_sum(p, w, M, G1 > G ? G1 : G, ll_out, s);
 }
 
 gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var, hipStream_t s) {
     LkWs w = lk_ws(p, ws);
-    const int G = lk_grid(p);
+    const int G = lk_grid(p, p.lk_slices == 1 ? LK_FUSED_EM : LK_SWEEP2);
     const size_t shm = sizeof(double) * (size_t)p.ncols;
     hipLaunchKernelGGL(k_lk_reduce, dim3(p.k), dim3(256), shm, s, w.part, G, p.lk_slices, p.n,
                        (int)p.d, p.cov == GMM_COV_ISO, p.var_floor, w.dsc, w.stats, w.pi, w.mu,
@@ -480,7 +485,7 @@ gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, flo
     LkWs w = lk_ws(p, ws);
     if (p.n == 0) return lk_sum(p, w, 0, 0, ll_out, s);
     if (refresh_panel(p, w, x, s) != hipSuccess) return GMM_E_HIP;
-    const int G = lk_grid(p);
+    const int G = lk_grid(p, p.lk_slices == 1 ? LK_FUSED_E : LK_SWEEP1);
     LkArgs a = make_args(p, w, x);
     if (p.lk_slices == 1) {
         a.out_lse = lse;
