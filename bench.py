@@ -41,6 +41,59 @@ PEAK_TFLOPS = {                 # MI355X dense peaks, published
 }
 METRIC = "GMM EM iterations/sec & points·components/s at N,D,K; % of HBM or MFMA roofline"
 
+# HBM traffic of one gmm_em_step (every launch it makes), measured with two
+# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
+#   bench.py --workload W --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+# summed over the em_step kernels' per-dispatch averages (KiB).  The same run
+# copies a buffer of the size of X once (torch's copy kernel: reads and writes
+# copy_bytes), and each counter is scaled by copy_bytes / (what it read for
+# that copy).  "sources" is a digest of the kernel sources the figures were
+# taken on: once they change, the figures are stale and traffic is reported
+# as null.
+TRAFFIC = {
+    "diag-f32-n1e6-d64-k16": dict(
+        sources="576ef807722c42b7", fetch_kib=125146.0, write_kib=4136.1,
+        copy_bytes=256e6, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
+    "iso-bf16-n1e7-d128-k256": dict(
+        sources="c3778c4a0ec42d7b", fetch_kib=1251131.4, write_kib=67606.9,
+        copy_bytes=2.56e9, copy_fetch_kib=1250036.5625, copy_write_kib=2500000.0),
+    "diag-bf16-n2e8-d128-k1024": dict(
+        sources="c3778c4a0ec42d7b", fetch_kib=67521923.1, write_kib=4042020.4,
+        copy_bytes=51.2e9, copy_fetch_kib=25000259.0, copy_write_kib=50000000.0),
+    "full-f16-n1e6-d64-k16": dict(
+        sources="b7e702597b0ed2e8", fetch_kib=63186.0, write_kib=68703.5,
+        copy_bytes=128e6, copy_fetch_kib=62514.1875, copy_write_kib=125000.0),
+}
+_SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
+FAMILY_SOURCES = {
+    "diag_f32": ("diag_fused.hip", "diag_params.hip", "diag_internal.h") + _SHARED_SOURCES,
+    "largek": ("largek.hip", "largek_params.hip", "largek_internal.h") + _SHARED_SOURCES,
+    "full": ("full_fused.hip", "full_params.hip", "full_internal.h") + _SHARED_SOURCES,
+}
+
+
+def sources_digest(family):
+    """SHA-256 (first 16 hex digits) over the family's kernel sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in FAMILY_SOURCES[family]:
+        with open(os.path.join(ROOT, "soft_clustering_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(w, family):
+    """Calibrated HBM bytes per gmm_em_step, or None when no figures exist for
+    this workload or the kernel sources changed since they were taken."""
+    t = TRAFFIC.get(w.name)
+    if t is None or t["sources"] != sources_digest(family):
+        return None
+    fetch = t["fetch_kib"] * t["copy_bytes"] / t["copy_fetch_kib"]
+    write = t["write_kib"] * t["copy_bytes"] / t["copy_write_kib"]
+    return {"bytes": fetch + write, "read_bytes": fetch, "write_bytes": write,
+            "fetch_scale": t["copy_bytes"] / (1024 * t["copy_fetch_kib"]),
+            "write_scale": t["copy_bytes"] / (1024 * t["copy_write_kib"])}
+
 
 def algorithmic_work(w):
     """(flops, bytes) of one fused E+M pass: X read once; flops per point:
@@ -151,16 +204,19 @@ def main(argv=None):
     hbm = nbytes / (fused_avg * 1e-3) / 1e9
     t_mfma = flops / (PEAK_TFLOPS[peak_key] * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    family = "diag_f32" if fp32_path else ("full" if full_path else "largek")
+    traffic = measured_traffic(w, family)
     if t_mfma >= t_hbm:
         roof = {"bound": "alu" if full_path else "mfma", "achieved": achieved_tflops,
                 "peak": PEAK_TFLOPS[peak_key], "unit": "TFLOP/s",
-                "frac": achieved_tflops / PEAK_TFLOPS[peak_key], "traffic": None}
+                "frac": achieved_tflops / PEAK_TFLOPS[peak_key],
+                "traffic": None if traffic is None else traffic["bytes"]}
         if full_path:   # packed fp32 instructions are not used: half the published rate
             roof["peak_unpacked_fma"] = PEAK_TFLOPS[peak_key] / 2
             roof["frac_unpacked_fma"] = achieved_tflops / (PEAK_TFLOPS[peak_key] / 2)
     else:
         roof = {"bound": "hbm", "achieved": hbm, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": hbm / PEAK_HBM_GBPS, "traffic": None}
+                "frac": hbm / PEAK_HBM_GBPS, "traffic": None if traffic is None else traffic["bytes"]}
     if fp32_path:
         kname = "k_diag_fused (+ k_sum_ll)"
     elif full_path:
@@ -173,7 +229,11 @@ def main(argv=None):
     roof.update({"kernel": kname, "timed": "gmm_em_step (all its launches), HIP events on its stream",
                  "avg_launch_ms": fused_avg,
                  "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
-                 "hbm_GBps": hbm, "hbm_frac": hbm / PEAK_HBM_GBPS})
+                 "hbm_GBps": hbm, "hbm_frac": hbm / PEAK_HBM_GBPS,
+                 "traffic_unit": "bytes per gmm_em_step (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                 "copy-calibrated)",
+                 "traffic_detail": traffic,
+                 "sources_digest": sources_digest(family)})
 
     ll_hist = lls.cpu().numpy()
     out = {

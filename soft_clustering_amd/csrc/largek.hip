@@ -305,19 +305,28 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            // A operands (LDS) read two steps ahead of the MFMAs that use them;
+            // step i = (pa, ks, rb); diag: y'^2 x A (pa 0), then y' x B (pa 1)
+            constexpr int NA = Sh::kNPA * KS * 2;
+            auto a_ptr = [&](int i) {
+                const int pa = i / (2 * KS), ks = (i / 2) % KS, rb = i % 2;
+                const int fb = kIso ? 0 : (pa == 0 ? 1 : 0);
+                return reinterpret_cast<const uint4*>(rm + (fb * kT + 16 * rb + j) * Sh::kRowRM +
+                                                      32 * ks + 8 * g);
+            };
+            uint4 a0 = *a_ptr(0), a1 = NA > 1 ? *a_ptr(1) : a0;
 #pragma unroll
-        for (int pa = 0; pa < Sh::kNPA; ++pa) {
-            const int fb = kIso ? 0 : (pa == 0 ? 1 : 0);   // diag: y'^2 x A, then y' x B
+            for (int i = 0; i < NA; ++i) {
+                const uint4 acur = a0;
+                a0 = a1;
+                if (i + 2 < NA) a1 = *a_ptr(i + 2);
+                const int pa = i / (2 * KS), ks = (i / 2) % KS, rb = i % 2;
+                const half8 av = __builtin_bit_cast(half8, acur);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    const half8 av = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(
-                        rm + (fb * kT + 16 * rb + j) * Sh::kRowRM + 32 * ks + 8 * g));
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        sc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pw[pa][ks][kb], sc[rb][kb], 0, 0, 0);
-                }
+                for (int kb = 0; kb < KB; ++kb)
+                    sc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pw[pa][ks][kb], sc[rb][kb], 0, 0, 0);
+            }
         }
         float yyv[2][4];
         if constexpr (kIso) {
@@ -470,18 +479,24 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                     half8, make_uint4(pack_h2(sc[0][kb][0], sc[0][kb][1]), pack_h2(sc[0][kb][2], sc[0][kb][3]),
                                       pack_h2(sc[1][kb][0], sc[1][kb][1]), pack_h2(sc[1][kb][2], sc[1][kb][3])));
             }
+            // B operands (transposed LDS rows) read one step ahead; step i = (f, fc)
+            constexpr int NB = NF * (DP / 16);
+            auto b_read = [&](int i) {
+                const uint16_t* row = trp + (i * 16 + j) * Sh::kRowT;   // feature row f*DP + 16fc + j
+                const uint2 b0 = *reinterpret_cast<const uint2*>(row + 4 * g);
+                const uint2 b1 = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
+                return make_uint4(b0.x, b0.y, b1.x, b1.y);
+            };
+            uint4 bnext = b_read(0);
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
+            for (int i = 0; i < NB; ++i) {
+                const half8 bv = __builtin_bit_cast(half8, bnext);
+                if (i + 1 < NB) bnext = b_read(i + 1);
+                const int f = i / (DP / 16), fc = i % (DP / 16);
 #pragma unroll
-                for (int fc = 0; fc < DP / 16; ++fc) {
-                    const uint16_t* row = trp + (f * DP + 16 * fc + j) * Sh::kRowT;
-                    const uint2 b0 = *reinterpret_cast<const uint2*>(row + 4 * g);
-                    const uint2 b1 = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
-                    const half8 bv = __builtin_bit_cast(half8, make_uint4(b0.x, b0.y, b1.x, b1.y));
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        acc[kb][f][fc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga[kb], bv, acc[kb][f][fc], 0, 0, 0);
-                }
+                for (int kb = 0; kb < KB; ++kb)
+                    acc[kb][f][fc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga[kb], bv, acc[kb][f][fc], 0, 0, 0);
+            }
         }
 
         if (t + 1 < t1) store_tile(cur ^ 1);
