@@ -110,8 +110,9 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_mu = take(sizeof(float) * p->k * p->d);
         p->off_cov = take(sizeof(float) * p->k * (iso ? 1 : p->d));
         p->off_shift = take(sizeof(float) * (2 + 3 * kLkScanWgs) * dp);
-        p->off_panel = take((size_t)(iso ? 1 : 2) * (dp / 32) * (p->lk_kpad / 16) * 64 * 16);
-        p->off_chunk = take(sizeof(float) * 3 * p->lk_kpad);
+        // panel: (features + 16 bias slots) / 16 MFMA steps x Kpad / 32 blocks x 64 lanes x 16 B
+        p->off_panel = take((size_t)(((iso ? 1 : 2) * dp + 16) / 16) * (p->lk_kpad / 32) * 64 * 16);
+        p->off_chunk = take(sizeof(float) * (p->lk_kpad + 4));
         if (S > 1) {
             p->off_lse = take(sizeof(float) * (size_t)S * p->n);
             p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)S * p->n);

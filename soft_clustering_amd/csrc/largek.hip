@@ -1,6 +1,6 @@
 // Large-K Gaussian mixtures (isotropic or diagonal covariance, X stored in
 // bf16 or fp16): fused E-step + M-step statistics on fp16 MFMA
-// (v_mfma_f32_16x16x32_f16, fp32 accumulation), fp32 softmax.
+// (v_mfma_f32_32x32x16_f16, fp32 accumulation), fp32 softmax.
 //
 // Method: [Flash-GMM] Method, fused E-M step (tiles of X, softmax over K on
 // chip, s0 / s1 / s2 accumulated without writing the N x K matrix).  When K
@@ -12,25 +12,31 @@
 // Scores, base 2, from the expanded quadratic form ([LP-GMM] 3.1 panel):
 //   y'_d = (x_d - c_d) s_d   (c: a centre, s_d = 2^-e_d: a power-of-two scale
 //                             that keeps y' and y'^2 inside the fp16 range)
-//   diag: S_k = 2^f_k (y'^2 . A_k + y' . B_k) + C_k
-//   iso:  S_k = 2^f_k (y' . W_k + P_k |y|^2) + C_k
-// with the fp16 panel (A, B, W) scaled per component by 2^-f_k so its
-// entries stay in range; |y|^2 is fp32.  y' and y'^2 are rounded to fp16
-// once, at staging; y'^2 above the fp16 maximum is clamped and reported.
-// Statistics: [s1' | s2'] += gamma^T [y' | y'^2] on fp16 MFMA with gamma
-// rounded to fp16; s0 (and the isotropic sum gamma |y|^2) in fp32 on the
-// vector unit from the unrounded gamma.
+//   diag: S_k = F (y'^2 . A_k + y' . B_k + C_k)
+//   iso:  S_k = F (y' . W_k + P_k |y|^2 2^-g + C_k)
+// with one power-of-two panel scale F for all components.  The contraction
+// runs over [y'^2 | y' | 16 bias slots] (diag) or [y' | 16 bias slots] (iso):
+// the bias slots hold C_k (and P_k) split into fp16 high and low parts
+// against constant ones (and |y|^2 2^-g split the same way, fp32 accurate), so
+// the MFMA returns the whole score and the vector unit only forms exp2.
 //
-// Work split: a workgroup owns a slice of 256 components, split over its
-// waves (4 waves x 64 components, or 8 waves x 32 so that two waves share each
-// SIMD within the register budget); each wave keeps its components' panel in
-// registers.  32-point tiles are staged once per workgroup into LDS (row-
-// major y' / y'^2 for the score operand, transposed copies for the statistics
-// operand), double buffered, one barrier per tile plus one for the exchange
-// of the waves' per-point (max, sum).  The slices of one point chunk are
-// mapped to one XCD so X is read from HBM once and re-read from that L2.
-
-#include <type_traits>
+// Layout: the score MFMA has the components as rows and the 32 points of a
+// tile as columns, so each lane holds one point's scores for 16 components
+// per block and the per-point max / sum is mostly lane-local (one exchange
+// between the two wave halves).  Responsibilities go through a wave-private
+// LDS tile [point][component] and come back, with ds_read_b64_tr_b16, as the
+// components-by-points A operand of the statistics MFMA; the B operand
+// (points by features) is read the same way from the row-major tile of X.
+// s0 (and the isotropic sum gamma |y|^2) come from one v_mfma_f32_16x16x32_f16
+// per 16 components against a [1, |y|^2] column pair.
+//
+// Work split: a workgroup owns a slice of 256 components, 64 per wave; each
+// wave keeps its components' panel in registers.  32-point tiles are staged
+// once per workgroup into LDS (y', y'^2 and the bias slots, row-major),
+// double buffered: one barrier per tile plus one for the exchange of the
+// waves' per-point (max, sum) in the modes that normalise.  The slices of one
+// point chunk are mapped to one XCD so X is read from HBM once and re-read
+// from that L2.
 
 #include "largek_internal.h"
 
@@ -40,33 +46,52 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr int kT = kLkT;
 constexpr float kLn2f = 0.69314718055994530942f;
 
+// LDS layouts, chosen by measuring bank conflicts on gfx950 (SQ_LDS_BANK_CONFLICT
+// over each access pattern): tile of X: rows at a pitch of an odd multiple of
+// 16 bytes (mod 256), which keeps the 16-byte score-operand reads of 32 rows
+// and the staging writes conflict-free; responsibility tile: 64 components
+// (128 bytes) per point with the 8-byte units XOR-swizzled by
+// ((r & 3) << 2 | (r >> 2) & 3), conflict-free for the 32-row unit writes and
+// the transposed reads.
+constexpr int row_pad(int inner) { return (24 - inner % 128 + 128) % 128; }
+
+template <int KW>
+__device__ __forceinline__ int g_swz(int r) {
+    if constexpr (KW == 64) return ((r & 3) << 2) | ((r >> 2) & 3);
+    // 32 components (64-byte rows, 8 units): bits 2..4 of r, bit 3 in the top
+    return (((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
+}
+
 template <int COV, int DP>
 struct LkShape {
     static constexpr bool kIso = COV == GMM_COV_ISO;
-    static constexpr int kNF = kIso ? 1 : 2;             // feature blocks: y' (, y'^2)
-    static constexpr int kNPA = kIso ? 1 : 2;            // panel arrays: W (; A, B)
-    static constexpr int kRowRM = DP + 8;                // halves per row-major row
-    static constexpr int kRowT = kT + 4;                 // halves per transposed row
-    static constexpr int kRM = kNF * kT * kRowRM;
-    static constexpr int kTR = kNF * DP * kRowT;
-    static constexpr int kBuf = kRM + kTR;               // halves per tile buffer
-    static constexpr int kKS = DP / 32;                  // 32-dim MFMA steps
-    static constexpr int kCB = DP / 8;                   // 8-column blocks per row
-    static constexpr int kItems = (kT / 2) * kCB;        // staging items (row pair, col block)
+    static constexpr int kFeat = kIso ? DP : 2 * DP;     // statistics features
+    static constexpr int kInner = kFeat + 16;            // + bias slots
+    static constexpr int kKS = kInner / 16;              // 32x32x16 steps per score
+    static constexpr int kRowY = kInner + row_pad(kInner);
+    static constexpr int kNFB = kFeat / 32;              // 32-feature blocks
+    static constexpr int kCB = DP / 8;                   // 8-column blocks per row of X
+    static constexpr int kItems = kT * kCB;
+    static constexpr int kFCh = kFeat / 8;               // 16-byte feature chunks per row
+    // halves offset of 16-byte chunk c of row r
+    static __device__ __forceinline__ int ych(int r, int c) { return r * kRowY + 8 * c; }
 };
+
+// halves offset of 4-half unit u of row r in the responsibility tile (KW components per row)
+template <int KW>
+__device__ __forceinline__ int gch(int r, int u) { return r * KW + 4 * (u ^ g_swz<KW>(r)); }
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     const half2v h = {(_Float16)lo, (_Float16)hi};       // v_cvt_pk_f16_f32, round to nearest even
     return __builtin_bit_cast(uint32_t, h);
-}
-
-template <int N>
-__device__ __forceinline__ float dpp_bcast(float v) {    // row_newbcast: lane N of each 16-lane row
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
 }
 
 template <bool BF16>
@@ -90,27 +115,47 @@ __device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ row, int col
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i' reads 4 halves of
+// row (i' / 4) at column 4 (i' % 4) (addresses as given); lane i receives
+// column i of the 4 rows.  Two such reads give the 8 consecutive K values of
+// an MFMA operand for rows of K stored contiguously along the M/N index.
+__device__ __forceinline__ uint2 tr16(const uint16_t* p) {
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_u16*)p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 template <int COV, int DP, int MODE, bool BF16>
 __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void k_lk(const LkArgs a) {
-    constexpr int WV = lk_waves(MODE, COV);          // waves per workgroup
+    constexpr int WV = lk_waves(MODE, COV);     // waves per workgroup
     constexpr int KW = kLkSlice / WV;           // components per wave
-    constexpr int KB = KW / 16;                 // 16-component blocks per wave
+    constexpr int CB = KW / 32;                 // 32-component blocks per wave
     constexpr int NT = 64 * WV;                 // threads per workgroup
     using Sh = LkShape<COV, DP>;
     constexpr bool kIso = Sh::kIso;
-    constexpr int KS = Sh::kKS, NF = Sh::kNF;
+    constexpr int KS = Sh::kKS, NFB = Sh::kNFB, RY = Sh::kRowY;
+    static_assert(KW == 64 || KW == 32, "responsibility tile layout: 32 or 64 components per wave");
+    constexpr int RG = KW;                      // halves per row of the responsibility tile
+    constexpr int IPT = (Sh::kItems + NT - 1) / NT;   // staging items per thread
     constexpr bool kStats = MODE == LK_FUSED_EM || MODE == LK_SWEEP2;
     constexpr bool kExchange = MODE != LK_SWEEP2;
+    // diagonal statistics at D = 128: the accumulators fill the AGPRs, so the
+    // y'^2 half of the panel (KL steps) is kept in LDS instead of registers
+    constexpr bool kTight = kStats && !kIso && DP == 128;
+    constexpr int KL = kTight ? DP / 16 : 0;   // panel steps [0, KL) and the bias step in LDS
+    constexpr int KR = KS - 1 - KL;            // panel steps in registers: [KL, KS - 1)
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Sh::kBuf];
-    __shared__ float2 dsc_l[DP];
-    __shared__ __attribute__((aligned(16))) float nx2[2][kT];     // |y|^2 per point (isotropic)
-    __shared__ __attribute__((aligned(16))) float lse_t[2][kT];   // merged base-2 LSE (sweep 2)
-    __shared__ float2 wpart[WV][kT];   // per-wave (max, sum) of each point
+    __shared__ __attribute__((aligned(16))) uint16_t ybuf[2][kT * RY];
+    __shared__ __attribute__((aligned(16))) uint16_t gbuf[kStats ? WV : 1][kStats ? kT * RG : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t yh_t[2][kT];   // iso: |y|^2 2^-g, fp16
+    __shared__ uint4 plds[WV][CB][KL + 1][64];   // LDS-resident steps of each wave's panel
+    __shared__ float2 dsc_l[DP];       // [e][8-column block]: (c, s) of column 8 block + e
+    __shared__ float2 wpart[WV][kT];   // per-wave (max, sum) of each point, base-2 score units
     __shared__ int warg[WV][kT];
     __shared__ double llred[NT];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int pn = lane & 31, hf = lane >> 5;           // point column, wave half
+    const int gq = lane >> 4, gi = lane & 15;           // 16-lane group, lane in group
     const int G = gridDim.x, S = a.S;
     int slice, chunk;
     {
@@ -128,28 +173,25 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     const int kbase = slice * kLkSlice + w * KW;
     const int64_t n = a.n;
     const int d = a.d;
+    const float F = a.prm[0];                   // panel scale 2^f
+    const float ysc = a.prm[1];                 // |y|^2 scale 2^-g (isotropic)
     const bool want_arg = (MODE == LK_SWEEP1 && a.part_arg != nullptr) ||
                           (MODE == LK_FUSED_E && a.out_arg != nullptr);
 
-    // ---- this wave's panel (registers), per-lane component constants
-    half8 pw[Sh::kNPA][KS][KB];
+    // ---- this wave's panel: A operand, row = component, K = inner; steps
+    // [KL, KS - 1) in registers, the others (the bias step, and at KL > 0 the
+    // y'^2 half) in LDS, read once per tile
+    half8 pnl[CB][KR > 0 ? KR : 1];
 #pragma unroll
-    for (int pa = 0; pa < Sh::kNPA; ++pa)
+    for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                pw[pa][ks][kb] = __builtin_bit_cast(
-                    half8, a.panel[((int64_t)(pa * KS + ks) * a.nblk + kbase / 16 + kb) * 64 + lane]);
-    float cv[KB], fs[KB], pv[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        const int k = kbase + 16 * kb + j;
-        cv[kb] = a.cvec[k];   // -inf for padding components
-        fs[kb] = a.fsc[k];
-        pv[kb] = kIso ? a.pvec[k] : 0.0f;
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 v = a.panel[((int64_t)ks * a.nblk + kbase / 32 + cb) * 64 + lane];
+            if (ks >= KL && ks < KS - 1) pnl[cb][ks - KL] = __builtin_bit_cast(half8, v);
+            else plds[w][cb][ks < KL ? ks : KL][lane] = v;
+        }
     }
-    for (int i = tid; i < DP; i += NT) dsc_l[i] = a.dsc[i];
+    for (int i = tid; i < DP; i += NT) dsc_l[(i % 8) * Sh::kCB + i / 8] = a.dsc[i];
 
     // ---- this chunk's tiles
     const int64_t tiles = (n + kT - 1) / kT;
@@ -157,28 +199,27 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     const int64_t t0 = chunk * tb + (chunk < tr ? chunk : tr);
     const int64_t t1 = t0 + tb + (chunk < tr ? 1 : 0);
 
-    f32x4 acc[kStats ? KB : 1][kStats ? NF : 1][kStats ? DP / 16 : 1];
-    float s0acc[KB], s2acc[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s0acc[kb] = s2acc[kb] = 0.0f;
+    f32x16 acc[kStats ? CB : 1][kStats ? NFB : 1];
+    f32x4 aux[kStats ? KW / 16 : 1];
     if constexpr (kStats) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
+            for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-                for (int fc = 0; fc < DP / 16; ++fc) acc[kb][f][fc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < 16; ++r) acc[cb][fb][r] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < KW / 16; ++b) aux[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     double ll2 = 0.0;
-    float sqmax = 0.0f;   // largest (y')^2 staged (diag): above the fp16 maximum it was clamped
+    float rng = 0.0f;   // diag: largest (y')^2 staged; iso: largest |y|^2 2^-g (clamped above fp16 max)
 
-    // ---- staging: item (row pair rp, 8-column block cb) per thread
-    const bool item_on = tid < Sh::kItems;
-    const int rp = tid / Sh::kCB, cb = tid % Sh::kCB;
-    const int col0 = 8 * cb;
-    const bool col_ok = col0 < d;
+    // ---- staging: item (row, 8-column block); the kCB items of a row sit in
+    // consecutive lanes
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
-    uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = raw0;
+    uint4 raw[IPT];
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) raw[q] = make_uint4(0, 0, 0, 0);
     float lse_pf = 0.0f;
     int rows_in = 0;
 
@@ -186,102 +227,83 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
         const int64_t p0 = t * kT;
         const int64_t left = n - p0;
         rows_in = left >= kT ? kT : (int)left;
-        if (item_on) {
-            const int r0 = 2 * rp < rows_in ? 2 * rp : rows_in - 1;
-            const int r1 = 2 * rp + 1 < rows_in ? 2 * rp + 1 : rows_in - 1;
-            const int cc = col_ok ? col0 : 0;
-            raw0 = load8(xb + (p0 + r0) * a.ldx, cc, d, a.vec);
-            raw1 = load8(xb + (p0 + r1) * a.ldx, cc, d, a.vec);
+#pragma unroll
+        for (int q = 0; q < IPT; ++q) {
+            const int it = tid + NT * q;
+            if (it < Sh::kItems) {
+                const int r = it / Sh::kCB, col0 = 8 * (it % Sh::kCB);
+                const int rr = r < rows_in ? r : rows_in - 1;
+                raw[q] = load8(xb + (p0 + rr) * a.ldx, col0 < d ? col0 : 0, d, a.vec);
+            }
         }
-        if constexpr (MODE == LK_SWEEP2) {
-            if (tid < kT) lse_pf = p0 + tid < n ? a.lse_in[p0 + tid] : INFINITY;   // gamma = 0
-        }
+        if constexpr (MODE == LK_SWEEP2) lse_pf = p0 + pn < n ? a.lse_in[p0 + pn] : INFINITY;   // gamma = 0
     };
 
     auto store_tile = [&](int buf) {
-        uint16_t* rm = lds + buf * Sh::kBuf;
-        uint16_t* trp = rm + Sh::kRM;
-        if (item_on) {
-            uint32_t hy[2][4], hq[2][4];
-            float yy[2];
-            const uint4 rw[2] = {raw0, raw1};
-            // rows beyond N and columns beyond D are zeroed only on ragged tiles
-            auto stage_rows = [&](auto masked) {
+        uint16_t* yb = ybuf[buf];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bool row_ok = 2 * rp + h < rows_in;
-                    const uint32_t wv[4] = {rw[h].x, rw[h].y, rw[h].z, rw[h].w};
-                    float yp[8], ss = 0.0f;
+        for (int q = 0; q < IPT; ++q) {
+            const int it = tid + NT * q;
+            if (Sh::kItems % NT != 0 && it >= Sh::kItems) continue;   // whole waves idle
+            const int r = it / Sh::kCB, cbk = it % Sh::kCB, col0 = 8 * cbk;
+            const bool row_ok = r < rows_in;
+            const uint32_t wv[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+            float yp[8], ss = 0.0f;
+            const bool full = rows_in == kT && d == DP;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
-                        const float2 cs = dsc_l[col0 + e];
-                        float y = h16_to_f32<BF16>(bits) - cs.x;
-                        if constexpr (decltype(masked)::value) y = (row_ok && col0 + e < d) ? y : 0.0f;
-                        if constexpr (kIso) ss = fmaf(y, y, ss);
-                        yp[e] = y * cs.y;
-                    }
-                    yy[h] = ss;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) hy[h][q] = pack_h2(yp[2 * q], yp[2 * q + 1]);
-                    if constexpr (!kIso) {
-                        float y2[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float v = yp[e] * yp[e];
-                            sqmax = fmaxf(sqmax, v);
-                            y2[e] = fminf(v, kF16Max);
-                        }
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) hq[h][q] = pack_h2(y2[2 * q], y2[2 * q + 1]);
-                    }
-                }
-            };
-            if (rows_in == kT && d == DP) stage_rows(std::false_type{});
-            else stage_rows(std::true_type{});
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int r = 2 * rp + h;
-                *reinterpret_cast<uint4*>(rm + r * Sh::kRowRM + col0) =
-                    make_uint4(hy[h][0], hy[h][1], hy[h][2], hy[h][3]);
-                if constexpr (!kIso)
-                    *reinterpret_cast<uint4*>(rm + (kT + r) * Sh::kRowRM + col0) =
-                        make_uint4(hq[h][0], hq[h][1], hq[h][2], hq[h][3]);
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
+                const float2 cs = dsc_l[e * Sh::kCB + cbk];
+                float y = h16_to_f32<BF16>(bits) - cs.x;
+                if (!full) y = (row_ok && col0 + e < d) ? y : 0.0f;
+                if constexpr (kIso) ss = fmaf(y, y, ss);
+                yp[e] = y * cs.y;
             }
-            if constexpr (kStats) {
-                // transposed: feature row (col0 + e), points (2rp, 2rp + 1) as one dword
+            const int off_y = kIso ? 0 : DP;
+            *reinterpret_cast<uint4*>(yb + Sh::ych(r, (off_y + col0) / 8)) =
+                make_uint4(pack_h2(yp[0], yp[1]), pack_h2(yp[2], yp[3]), pack_h2(yp[4], yp[5]),
+                           pack_h2(yp[6], yp[7]));
+            if constexpr (!kIso) {
+                float y2[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int q = e >> 1;
-                    const uint32_t v = (e & 1) ? ((hy[0][q] >> 16) | (hy[1][q] & 0xFFFF0000u))
-                                               : ((hy[0][q] & 0xFFFFu) | (hy[1][q] << 16));
-                    *reinterpret_cast<uint32_t*>(trp + (col0 + e) * Sh::kRowT + 2 * rp) = v;
-                    if constexpr (!kIso) {
-                        const uint32_t u = (e & 1) ? ((hq[0][q] >> 16) | (hq[1][q] & 0xFFFF0000u))
-                                                   : ((hq[0][q] & 0xFFFFu) | (hq[1][q] << 16));
-                        *reinterpret_cast<uint32_t*>(trp + (DP + col0 + e) * Sh::kRowT + 2 * rp) = u;
-                    }
+                    const float v = yp[e] * yp[e];
+                    rng = fmaxf(rng, v);
+                    y2[e] = fminf(v, kF16Max);
                 }
+                *reinterpret_cast<uint4*>(yb + Sh::ych(r, col0 / 8)) =
+                    make_uint4(pack_h2(y2[0], y2[1]), pack_h2(y2[2], y2[3]), pack_h2(y2[4], y2[5]),
+                               pack_h2(y2[6], y2[7]));
+            } else {
+                // |y|^2 of the row: the kCB lanes of a row are consecutive
+                if constexpr (Sh::kCB >= 2) ss += dpp<kDppXor1>(ss);
+                if constexpr (Sh::kCB >= 4) ss += dpp<kDppXor2>(ss);
+                if constexpr (Sh::kCB >= 8) ss += dpp<kDppHalfMirror>(ss);
+                if constexpr (Sh::kCB >= 16) ss += dpp<kDppMirror>(ss);
             }
-            if constexpr (kIso) {
-                // |y|^2 of the two rows: the kCB lanes of a row pair are consecutive
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float s = yy[h];
-                    if constexpr (Sh::kCB >= 2) s += dpp<kDppXor1>(s);
-                    if constexpr (Sh::kCB >= 4) s += dpp<kDppXor2>(s);
-                    if constexpr (Sh::kCB >= 8) s += dpp<kDppHalfMirror>(s);
-                    if constexpr (Sh::kCB >= 16) s += dpp<kDppMirror>(s);
-                    yy[h] = s;
+            if (cbk == 0) {
+                // bias slots: diag [1, 1]; iso [yh, yl, yh, 1, 1] with yh + yl = |y|^2 2^-g
+                uint32_t bw[4];
+                if constexpr (kIso) {
+                    const float v = ss * ysc;
+                    rng = fmaxf(rng, v);
+                    const float vc = fminf(v, kF16Max);
+                    const _Float16 yh = (_Float16)vc;
+                    const float yl = vc - (float)yh;
+                    const uint32_t hb = __builtin_bit_cast(uint16_t, yh);
+                    bw[0] = hb | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)yl) << 16);
+                    bw[1] = hb | (0x3C00u << 16);
+                    bw[2] = 0x3C00u;
+                    bw[3] = 0u;
+                    yh_t[buf][r] = (uint16_t)hb;
+                } else {
+                    bw[0] = 0x3C003C00u;
+                    bw[1] = bw[2] = bw[3] = 0u;
                 }
-                if (cb == 0) {
-                    nx2[buf][2 * rp] = yy[0];
-                    nx2[buf][2 * rp + 1] = yy[1];
-                }
+                uint4* bias = reinterpret_cast<uint4*>(yb + Sh::ych(r, Sh::kFCh));
+                bias[0] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+                bias[1] = make_uint4(0, 0, 0, 0);
             }
-        }
-        if constexpr (MODE == LK_SWEEP2) {
-            if (tid < kT) lse_t[buf][tid] = lse_pf;
         }
     };
 
@@ -294,252 +316,268 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
 
     for (int64_t t = t0; t < t1; ++t) {
         const int cur = (int)((t - t0) & 1);
-        const uint16_t* rm = lds + cur * Sh::kBuf;
-        const uint16_t* trp = rm + Sh::kRM;
+        const uint16_t* yb = ybuf[cur];
         const int64_t prow = t * kT;
+        const bool pvalid = prow + pn < n;
+        float lse_cur = 0.0f;
+        if constexpr (MODE == LK_SWEEP2) lse_cur = lse_pf;
         if (t + 1 < t1) load_tile(t + 1);
 
-        // ---- scores: 32 points x this wave's 64 components
-        f32x4 sc[2][KB];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // ---- scores (acc units; S = F acc), one 32-component block at a time:
+        // lane (pn, hf), register r of block cb holds point pn and component
+        // kbase + 32 cb + 8 (r / 4) + 4 hf + r % 4
+        uint16_t* gw = gbuf[kStats ? w : 0];
+        float mcb[CB], zcb[CB];                 // per block: max (acc units), sum of exp2(F (acc - max))
+        int acb[CB];                            // per block: lowest component at the max
+        half2v eh[MODE == LK_FUSED_EM ? CB : 1][8];   // fused E+M: exp2(F (acc - max)), fp16 pairs
+        f32x16 scb[CB];
         {
-            // A operands (LDS) read two steps ahead of the MFMAs that use them;
-            // step i = (pa, ks, rb); diag: y'^2 x A (pa 0), then y' x B (pa 1)
-            constexpr int NA = Sh::kNPA * KS * 2;
-            auto a_ptr = [&](int i) {
-                const int pa = i / (2 * KS), ks = (i / 2) % KS, rb = i % 2;
-                const int fb = kIso ? 0 : (pa == 0 ? 1 : 0);
-                return reinterpret_cast<const uint4*>(rm + (fb * kT + 16 * rb + j) * Sh::kRowRM +
-                                                      32 * ks + 8 * g);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) scb[cb][r] = 0.0f;
+            // operands read kPF steps ahead of their MFMAs: the tile (B, K = inner)
+            // and the LDS-resident panel steps (A)
+            constexpr int kPF = kTight ? 2 : 4;
+            constexpr auto in_lds = [](int ks) { return ks < KL || ks == KS - 1; };
+            half8 yq[KS];
+            half8 pq[CB][KS];
+            auto issue = [&](int ks) {
+                yq[ks] = *reinterpret_cast<const half8*>(yb + Sh::ych(pn, 2 * ks + hf));
+                if (in_lds(ks))
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        pq[cb][ks] = __builtin_bit_cast(half8, plds[w][cb][ks < KL ? ks : KL][lane]);
             };
-            uint4 a0 = *a_ptr(0), a1 = NA > 1 ? *a_ptr(1) : a0;
 #pragma unroll
-            for (int i = 0; i < NA; ++i) {
-                const uint4 acur = a0;
-                a0 = a1;
-                if (i + 2 < NA) a1 = *a_ptr(i + 2);
-                const int pa = i / (2 * KS), ks = (i / 2) % KS, rb = i % 2;
-                const half8 av = __builtin_bit_cast(half8, acur);
+            for (int ks = 0; ks < kPF && ks < KS; ++ks) issue(ks);
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    sc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pw[pa][ks][kb], sc[rb][kb], 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kPF < KS) issue(ks + kPF);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const half8 pa = in_lds(ks) ? pq[cb][ks] : pnl[cb][in_lds(ks) ? 0 : ks - KL];
+                    scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
+                }
+            }
+            constexpr int kFirst = kPF + CB * (kPF < KL ? kPF : KL);   // reads issued up front
+            __builtin_amdgcn_sched_group_barrier(0x100, kFirst, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kPF < KS) {
+                    if (in_lds(ks + kPF)) __builtin_amdgcn_sched_group_barrier(0x100, 1 + CB, 0);
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
             }
         }
-        float yyv[2][4];
-        if constexpr (kIso) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const float4 v = *reinterpret_cast<const float4*>(&nx2[cur][16 * rb + 4 * g]);
-                yyv[rb][0] = v.x; yyv[rb][1] = v.y; yyv[rb][2] = v.z; yyv[rb][3] = v.w;
-            }
-        }
+        for (int cb = 0; cb < CB; ++cb) {
+            f32x16& sc = scb[cb];
+            if constexpr (kExchange) {
+                float m = sc[0];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+                for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
+                m = fmaxf(m, __shfl_xor(m, 32, 64));
+                const float nmf = m == -INFINITY ? 0.0f : -F * m;
+                float z = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = sc[rb][kb][r];
-                    if constexpr (kIso) v = fmaf(pv[kb], yyv[rb][r], v);
-                    sc[rb][kb][r] = fmaf(v, fs[kb], cv[kb]);
-                }
-
-        // ---- per point: base-2 LSE (and argmax) over the components
-        float lse2[2][4];
-        float lse_me = 0.0f;   // lanes j < 8: point 16 (j >> 2) + 4 g + (j & 3)
-        int arg_me = 0;
-        const int pt_me = 16 * (j >> 2) + 4 * g + (j & 3);
-        float mw[2][4];   // this wave's per-point shift (fused E+M: reused for gamma)
-        if constexpr (kExchange) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float mx = sc[rb][0][r];
-#pragma unroll
-                    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, sc[rb][kb][r]);
-                    const float m = row16_max(mx);
-                    const float ms = m == -INFINITY ? 0.0f : m;
-                    mw[rb][r] = ms;
-                    float zz = 0.0f;
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const float e = fast_exp2(sc[rb][kb][r] - ms);
-                        if constexpr (kStats) sc[rb][kb][r] = e;   // exp(S - m_w), reused for gamma
-                        zz += e;
+                for (int r = 0; r < 16; ++r) {
+                    const float e = fast_exp2(fmaf(sc[r], F, nmf));
+                    if constexpr (MODE == LK_FUSED_EM) {
+                        if (r & 1) eh[cb][r >> 1] = half2v{(_Float16)sc[r - 1], (_Float16)e};
+                        else sc[r] = e;
                     }
-                    const float z = row16_sum(zz);
-                    if (j == 0) wpart[w][16 * rb + 4 * g + r] = make_float2(m, z);
-                    if constexpr (!kStats) {
-                        if (want_arg) {   // lowest component among this wave's maxima
-                            int bi = 0x7FFFFFFF;
-#pragma unroll
-                            for (int kb = KB - 1; kb >= 0; --kb)
-                                if (sc[rb][kb][r] == m) bi = kbase + 16 * kb + j;
-                            const int arg = row16_min_i(bi);
-                            if (j == 0) warg[w][16 * rb + 4 * g + r] = arg;
-                        }
-                    }
+                    z += e;
                 }
-            __syncthreads();
-            if (j < 8) {
-                float M = wpart[0][pt_me].x;
-#pragma unroll
-                for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w2][pt_me].x);
-                const float Ms = M == -INFINITY ? 0.0f : M;
-                float Z = 0.0f;
-#pragma unroll
-                for (int w2 = 0; w2 < WV; ++w2) {
-                    const float2 mz = wpart[w2][pt_me];
-                    Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
-                }
-                lse_me = Ms + fast_log2(Z);
-                if (want_arg) {
-                    arg_me = 0x7FFFFFFF;
-#pragma unroll
-                    for (int w2 = WV - 1; w2 >= 0; --w2)
-                        if (wpart[w2][pt_me].x == M) arg_me = warg[w2][pt_me];
-                }
-            }
-            const int64_t p = prow + pt_me;
-            if constexpr (MODE == LK_SWEEP1) {
-                if (w == 0 && j < 8 && p < n) {
-                    a.part_lse[(int64_t)slice * n + p] = lse_me;
+                mcb[cb] = m;
+                zcb[cb] = z + __shfl_xor(z, 32, 64);
+                acb[cb] = 0x7FFFFFFF;
+                if constexpr (!kStats) {
                     if (want_arg) {
-                        float M = wpart[0][pt_me].x;
+                        int bi = 0x7FFFFFFF;
 #pragma unroll
-                        for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w2][pt_me].x);
-                        a.part_arg[(int64_t)slice * n + p] = arg_me;
+                        for (int r = 15; r >= 0; --r)
+                            if (sc[r] == m) bi = kbase + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        acb[cb] = min(bi, __shfl_xor(bi, 32, 64));
+                    }
+                }
+            } else {
+                // sweep 2: gamma = exp2(S - lse) (lse = +inf beyond N) -> LDS [point][component]
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float gv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gv[e] = fast_exp2(fmaf(sc[4 * q + e], F, -lse_cur));
+                    *reinterpret_cast<uint2*>(gw + gch<KW>(pn, 8 * cb + 2 * q + hf)) =
+                        make_uint2(pack_h2(gv[0], gv[1]), pack_h2(gv[2], gv[3]));
+                }
+            }
+        }
+
+        if constexpr (kExchange) {
+            // this wave's (max, sum) per point, base-2 score units
+            float m = mcb[0];
+#pragma unroll
+            for (int cb = 1; cb < CB; ++cb) m = fmaxf(m, mcb[cb]);
+            const float Fm = m == -INFINITY ? -INFINITY : F * m;
+            float z = 0.0f;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int cb = CB - 1; cb >= 0; --cb) {
+                if (mcb[cb] != -INFINITY) z = fmaf(zcb[cb], fast_exp2(F * (mcb[cb] - m)), z);
+                if (mcb[cb] == m) bi = acb[cb];
+            }
+            if (hf == 0) {
+                wpart[w][pn] = make_float2(Fm, z);
+                if (want_arg) warg[w][pn] = bi;
+            }
+            __syncthreads();
+            float M = wpart[0][pn].x;
+#pragma unroll
+            for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w2][pn].x);
+            const float Ms = M == -INFINITY ? 0.0f : M;
+            float Z = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < WV; ++w2) {
+                const float2 mz = wpart[w2][pn];
+                Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
+            }
+            const float lse = Ms + fast_log2(Z);
+            int arg = 0;
+            if (want_arg) {
+                arg = 0x7FFFFFFF;
+#pragma unroll
+                for (int w2 = WV - 1; w2 >= 0; --w2)
+                    if (wpart[w2][pn].x == M) arg = warg[w2][pn];
+            }
+            const int64_t p = prow + pn;
+            if (w == 0 && hf == 0 && pvalid) {
+                if constexpr (MODE == LK_SWEEP1) {
+                    a.part_lse[(int64_t)slice * n + p] = lse;
+                    if (want_arg) {
+                        a.part_arg[(int64_t)slice * n + p] = arg;
                         a.part_max[(int64_t)slice * n + p] = M;
                     }
-                }
-            } else {
-                if (w == 0 && j < 8 && p < n) {
-                    ll2 += (double)lse_me;
+                } else {
+                    ll2 += (double)lse;
                     if constexpr (MODE == LK_FUSED_E) {
-                        if (a.out_lse) a.out_lse[p] = lse_me * kLn2f;
-                        if (want_arg) a.out_arg[p] = arg_me;
+                        if (a.out_lse) a.out_lse[p] = lse * kLn2f;
+                        if (want_arg) a.out_arg[p] = arg;
                     }
                 }
-                lse2[0][0] = dpp_bcast<0>(lse_me); lse2[0][1] = dpp_bcast<1>(lse_me);
-                lse2[0][2] = dpp_bcast<2>(lse_me); lse2[0][3] = dpp_bcast<3>(lse_me);
-                lse2[1][0] = dpp_bcast<4>(lse_me); lse2[1][1] = dpp_bcast<5>(lse_me);
-                lse2[1][2] = dpp_bcast<6>(lse_me); lse2[1][3] = dpp_bcast<7>(lse_me);
             }
-        } else {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const float4 v = *reinterpret_cast<const float4*>(&lse_t[cur][16 * rb + 4 * g]);
-                lse2[rb][0] = v.x; lse2[rb][1] = v.y; lse2[rb][2] = v.z; lse2[rb][3] = v.w;
-            }
-        }
-        (void)arg_me;
-
-        // ---- responsibilities and statistics (registers -> MFMA)
-        if constexpr (kStats) {
             if constexpr (MODE == LK_FUSED_EM) {
-                // gamma = exp(S - m_w) * exp(m_w - lse); zero for rows beyond N
+                // gamma = exp2(F (acc - m_cb)) exp2(F m_cb - lse), zero beyond N -> LDS
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int cb = 0; cb < CB; ++cb) {
+                    const float f = (pvalid && mcb[cb] != -INFINITY) ? fast_exp2(F * mcb[cb] - lse) : 0.0f;
+                    const half2v f2 = {(_Float16)f, (_Float16)f};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool valid = prow + 16 * rb + 4 * g + r < n;
-                        const float f = valid ? fast_exp2(mw[rb][r] - lse2[rb][r]) : 0.0f;
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb) sc[rb][kb][r] *= f;
+                    for (int q = 0; q < 4; ++q) {
+                        const half2v g0 = eh[cb][2 * q] * f2, g1 = eh[cb][2 * q + 1] * f2;
+                        *reinterpret_cast<uint2*>(gw + gch<KW>(pn, 8 * cb + 2 * q + hf)) =
+                            make_uint2(__builtin_bit_cast(uint32_t, g0), __builtin_bit_cast(uint32_t, g1));
                     }
-            } else {
-                // sweep 2: lse is +inf for rows beyond N, so gamma = 0 there
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            sc[rb][kb][r] = fast_exp2(sc[rb][kb][r] - lse2[rb][r]);
-            }
-            half8 ga[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                float s0 = 0.0f, s2 = 0.0f;
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        s0 += sc[rb][kb][r];
-                        if constexpr (kIso) s2 = fmaf(sc[rb][kb][r], yyv[rb][r], s2);
-                    }
-                s0acc[kb] += s0;
-                if constexpr (kIso) s2acc[kb] += s2;
-                // gamma^T operand: component j, points 4g + e (e < 4) and 16 + 4g + e - 4
-                ga[kb] = __builtin_bit_cast(
-                    half8, make_uint4(pack_h2(sc[0][kb][0], sc[0][kb][1]), pack_h2(sc[0][kb][2], sc[0][kb][3]),
-                                      pack_h2(sc[1][kb][0], sc[1][kb][1]), pack_h2(sc[1][kb][2], sc[1][kb][3])));
-            }
-            // B operands (transposed LDS rows) read one step ahead; step i = (f, fc)
-            constexpr int NB = NF * (DP / 16);
-            auto b_read = [&](int i) {
-                const uint16_t* row = trp + (i * 16 + j) * Sh::kRowT;   // feature row f*DP + 16fc + j
-                const uint2 b0 = *reinterpret_cast<const uint2*>(row + 4 * g);
-                const uint2 b1 = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
-                return make_uint4(b0.x, b0.y, b1.x, b1.y);
-            };
-            uint4 bnext = b_read(0);
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const half8 bv = __builtin_bit_cast(half8, bnext);
-                if (i + 1 < NB) bnext = b_read(i + 1);
-                const int f = i / (DP / 16), fc = i % (DP / 16);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    acc[kb][f][fc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga[kb], bv, acc[kb][f][fc], 0, 0, 0);
+                }
             }
         }
 
+        // ---- statistics MFMAs from the responsibility tile (wave-private)
+        if constexpr (kStats) {
+            // A operands: gamma^T (row = component, K = 16 points per step);
+            // B operands: the tile of X (K = points, column = feature), read
+            // two feature blocks ahead of their MFMAs
+            constexpr int kSteps = 2 * NFB;                 // (kp, fb)
+            constexpr int kPFB = kTight ? 1 : 2;
+            half8 bzq[kSteps];
+            half8 ag[2][CB];
+            // transposed reads: lane i of 16-lane group q takes row 16 kp + 8 (q / 2) + i / 4 (+ 4)
+            const int trow = 8 * (gq >> 1) + (gi >> 2);
+            auto bz_read = [&](int i) {
+                const int kp = i / NFB, fb = i % NFB;
+                const int r = 16 * kp + trow, c = 4 * fb + 2 * (gq & 1) + ((gi & 3) >> 1), o = 4 * (gi & 1);
+                const uint2 lo = tr16(yb + Sh::ych(r, c) + o), hi = tr16(yb + Sh::ych(r + 4, c) + o);
+                return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            };
+            auto g_read = [&](int r, int u) {
+                const uint2 lo = tr16(gw + gch<KW>(r, u)), hi = tr16(gw + gch<KW>(r + 4, u));
+                return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            };
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    ag[kp][cb] = g_read(16 * kp + trow, 8 * cb + 4 * (gq & 1) + (gi & 3));
+#pragma unroll
+            for (int i = 0; i < kPFB; ++i) bzq[i] = bz_read(i);
+#pragma unroll
+            for (int i = 0; i < kSteps; ++i) {
+                if (i + kPFB < kSteps) bzq[i + kPFB] = bz_read(i + kPFB);
+                const int kp = i / NFB, fb = i % NFB;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[cb][fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag[kp][cb], bzq[i], acc[cb][fb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (2 * CB + kPFB), 1);
+#pragma unroll
+            for (int i = 0; i < kSteps; ++i) {
+                if (i + kPFB < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, CB, 1);
+            }
+            // s0 (and iso sum gamma |y|^2): 16 components x 32 points against [1, yh]
+            half8 bx;
+            {
+                const uint4 hv = *reinterpret_cast<const uint4*>(&yh_t[cur][8 * gq]);
+                const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+                const uint4 z4 = make_uint4(0, 0, 0, 0);
+                bx = __builtin_bit_cast(half8, gi == 0 ? ones : ((kIso && gi == 1) ? hv : z4));
+            }
+#pragma unroll
+            for (int b = 0; b < KW / 16; ++b) {
+                const half8 ax = g_read(8 * gq + (gi >> 2), 4 * b + (gi & 3));
+                aux[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bx, aux[b], 0, 0, 0);
+            }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);   // staging after the statistics: bounded live ranges
         if (t + 1 < t1) store_tile(cur ^ 1);
         __syncthreads();
     }
 
     // ---- epilogue: per-workgroup partials, one writer per value
-    const int flag = __syncthreads_or(sqmax > kF16Max ? 1 : 0);
+    const int flag = __syncthreads_or(rng > kF16Max ? 1 : 0);
     if (tid == 0) a.part_flag[blockIdx.x] = flag;
     if constexpr (kStats) {
         const int ncol = kIso ? 2 + d : 1 + 2 * d;
         double* dst = a.part + (int64_t)blockIdx.x * kLkSlice * ncol;
-        float* sred = reinterpret_cast<float*>(lds);   // [waves][4][KW][2]; the tiles are done
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            sred[((w * 4 + g) * KW + 16 * kb + j) * 2] = s0acc[kb];
-            sred[((w * 4 + g) * KW + 16 * kb + j) * 2 + 1] = s2acc[kb];
-        }
-        __syncthreads();
-        if (lane < KW) {
-            const int kl = lane;   // one component per lane
-            const float* s = sred + (w * 4 * KW + kl) * 2;
-            const double s0 = ((double)s[0] + (double)s[2 * KW]) + ((double)s[4 * KW] + (double)s[6 * KW]);
-            double* o = dst + (int64_t)(w * KW + kl) * ncol;
-            o[0] = s0;
-            if constexpr (kIso)
-                o[1 + d] = ((double)s[1] + (double)s[2 * KW + 1]) + ((double)s[4 * KW + 1] + (double)s[6 * KW + 1]);
-        }
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int fb = 0; fb < NFB; ++fb) {
+                const int f = 32 * fb + pn;
+                int col = -1;
+                if (kIso) col = f < d ? 1 + f : -1;
+                else if (f < DP) col = f < d ? 1 + d + f : -1;          // y'^2 -> s2'
+                else col = f - DP < d ? 1 + (f - DP) : -1;              // y'   -> s1'
+                if (col >= 0) {
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
-#pragma unroll
-                for (int fc = 0; fc < DP / 16; ++fc) {
-                    const int dd = 16 * fc + j;
-                    if (dd < d) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int kl = w * KW + 16 * kb + 4 * g + r;
-                            dst[(int64_t)kl * ncol + 1 + f * d + dd] = (double)acc[kb][f][fc][r];
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int kl = w * KW + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        dst[(int64_t)kl * ncol + col] = (double)acc[cb][fb][r];
                     }
                 }
+            }
+        if (gi < (kIso ? 2 : 1)) {
+            const double scl = gi == 0 ? 1.0 : (double)a.prm[2];   // iso: undo the 2^-g of yh
+#pragma unroll
+            for (int b = 0; b < KW / 16; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kl = w * KW + 16 * b + 4 * gq + r;
+                    dst[(int64_t)kl * ncol + (gi == 0 ? 0 : 1 + d)] = (double)aux[b][r] * scl;
+                }
+        }
     }
     if constexpr (MODE == LK_FUSED_EM || MODE == LK_FUSED_E) {
         llred[tid] = ll2;

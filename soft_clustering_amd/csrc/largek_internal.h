@@ -1,6 +1,7 @@
 // Internal interface of the large-K family (isotropic or diagonal covariance,
-// X stored in bf16 or fp16, fp16 MFMA operands, fp32 softmax and statistics):
-// workspace pointers, kernel arguments and launch helpers.
+// X stored in bf16 or fp16, fp16 MFMA operands (v_mfma_f32_32x32x16_f16),
+// fp32 softmax and statistics): workspace pointers, kernel arguments and
+// launch helpers.
 #pragma once
 
 #include "common.h"
@@ -40,8 +41,9 @@ struct LkWs {
     float *pi, *mu, *var;        // fp32 parameters theta (var: [K] iso, [K*D] diag)
     float2* dsc;                 // [DP] (c_d, s_d): y' = (x - c_d) * s_d, s_d = 2^-e_d
     float* scan;                 // [scan workgroups][DP][3] sample (sum, min, max)
-    uint4* panel;                // fp16 score panel, MFMA register layout
-    float *cvec, *fsc, *pvec;    // [Kpad] base-2 constant, panel scale 2^f_k, iso ||y||^2 coeff.
+    uint4* panel;                // fp16 score panel, MFMA A-operand register layout
+    float* kmax;                 // [Kpad] largest panel magnitude of each component
+    float* prm;                  // [4] panel scale F = 2^f, |y|^2 scale 2^-g, 2^g, unused
     float* part_lse;             // [S][N] base-2 LSE of each slice; row 0 is then
                                  // overwritten with the merged LSE (two-sweep only)
     int* part_arg;               // [S][N] argmax within each slice (two-sweep only)
@@ -62,9 +64,8 @@ inline LkWs lk_ws(const Plan& p, char* ws) {
     w.dsc = (float2*)(ws + p.off_shift);
     w.scan = (float*)(w.dsc + p.dp);
     w.panel = (uint4*)(ws + p.off_panel);
-    w.cvec = (float*)(ws + p.off_chunk);
-    w.fsc = w.cvec + p.lk_kpad;
-    w.pvec = w.fsc + p.lk_kpad;
+    w.kmax = (float*)(ws + p.off_chunk);
+    w.prm = w.kmax + p.lk_kpad;
     const bool two = p.lk_slices > 1;
     w.part_lse = two ? (float*)(ws + p.off_lse) : nullptr;
     w.part_arg = two ? (int*)(ws + p.off_arg) : nullptr;
@@ -85,10 +86,8 @@ struct LkArgs {
     int64_t n, ldx;
     int d, k_real, S, vec;
     const uint4* panel;
-    int nblk;                    // 16-component blocks in the panel (Kpad / 16)
-    const float* cvec;
-    const float* fsc;
-    const float* pvec;
+    int nblk;                    // 32-component blocks in the panel (Kpad / 32)
+    const float* prm;            // panel scale and |y|^2 scales (LkWs::prm)
     const float2* dsc;
     float* part_lse;             // sweep 1 output [S][N] (base-2 LSE per slice)
     int* part_arg;               // sweep 1 output [S][N] (nullable: no argmax)
@@ -105,12 +104,13 @@ struct LkArgs {
 inline int64_t lk_ncols(int cov, int64_t d) { return cov == GMM_COV_ISO ? 2 + d : 1 + 2 * d; }
 
 // Waves per workgroup of the fused kernel.  The isotropic statistics modes
-// split the slice over 8 waves of 32 components (under 256 registers per
-// lane, so two waves share a SIMD): 4.10 -> 3.71 ms on 1e7 x 128 x 256.  The
-// diagonal statistics modes keep 4 waves of 64 components: at D = 128 the
-// 8-wave variant spills and was slower (sweep 2 of 2e8 x 128 x 1024:
-// 362 -> 474 ms).  The modes without statistics use 4 waves and run two
-// workgroups per CU.
+// run 8 waves of 32 components (one 32-component MFMA block each): at two
+// waves per SIMD each wave's panel, accumulators and operands fit 256
+// registers and the two waves hide each other's latencies (1e7 x 128 x 256:
+// 3.47 -> 2.82 ms).  The diagonal statistics modes keep 4 waves of 64
+// components, one per SIMD (at 8 waves the D = 128 variant spills and reads
+// the tile twice as often: sweep 2 of 2e8 x 128 x 1024 went 253 -> 272 ms).
+// The modes without statistics run 4 waves and two workgroups per CU.
 __host__ __device__ constexpr int lk_waves(int mode, int cov) {
     return ((mode == LK_FUSED_EM || mode == LK_SWEEP2) && cov == GMM_COV_ISO) ? 8 : 4;
 }

@@ -104,76 +104,130 @@ __global__ __launch_bounds__(256) void k_lk_scan(const uint16_t* __restrict__ x,
 }
 
 // Centre and per-dimension scale of X for the fused kernel, from the scan:
-// c_d = sample mean of the finite values rounded to the storage type, s_d = 2^-e_d with 2^e_d the power of two
-// at or below 1/8 of the sample's largest |x_d - c_d|, so the sampled y' lie
-// in [-16, 16] and y'^2 stays below the fp16 maximum for |y'| < 255.  One
-// workgroup.
-__global__ __launch_bounds__(128) void k_lk_centre(int64_t n, int d, int dp, bool bf16,
-                                                   const float* scan, float2* dsc) {
+// c_d = sample mean of the finite values rounded to the storage type, s_d =
+// 2^-e_d with 2^e_d the power of two at or below 1/8 of the sample's largest
+// |x_d - c_d|, so the sampled y' lie in [-16, 16] and y'^2 stays below the
+// fp16 maximum for |y'| < 255.  Isotropic: 2^-g with the sampled bound of
+// |x - c|^2 times 2^-g below 2^14, so |y|^2 2^-g stays in fp16 range for
+// points within twice the sampled spread.  One workgroup of 128 threads.
+__global__ __launch_bounds__(128) void k_lk_centre(int64_t n, int d, int dp, bool bf16, bool iso,
+                                                   const float* scan, float2* dsc, float* prm) {
+    __shared__ double red[128];
     const int dd = threadIdx.x;
-    if (dd >= dp) return;
-    if (dd >= d) {
+    double r2 = 0.0;
+    if (dd < d) {
+        const int64_t ns = n < kLkScanRows ? n : kLkScanRows;
+        double s = 0.0;
+        float lo = INFINITY, hi = -INFINITY;
+        for (int b = 0; b < kLkScanWgs; ++b) {
+            const float* o = scan + ((int64_t)b * dp + dd) * 3;
+            s += (double)o[0];
+            lo = fminf(lo, o[1]);
+            hi = fmaxf(hi, o[2]);
+        }
+        // c is rounded to X's storage type, so x - c is exact in fp32 and, for
+        // data within ~2^11 storage ulps of c, exact in fp16 too: no rounding
+        // bias shared by every point of a coarse storage lattice
+        double c = (ns > 0 && isfinite(s)) ? s / (double)ns : 0.0;
+        if (bf16) c = (double)(float)(__bf16)(float)c;
+        else if (fabs(c) < 65504.0) c = (double)(float)(_Float16)(float)c;
+        const double r = fmax((double)hi - c, c - (double)lo);
+        int e = 0;
+        if (r > 0.0 && isfinite(r)) {
+            e = ilogb(r) - 3;
+            e = e < -60 ? -60 : (e > 60 ? 60 : e);
+            r2 = r * r;
+        }
+        dsc[dd] = make_float2((float)c, (float)ldexp(1.0, -e));
+    } else if (dd < dp) {
         dsc[dd] = make_float2(0.0f, 0.0f);
-        return;
     }
-    const int64_t ns = n < kLkScanRows ? n : kLkScanRows;
-    double s = 0.0;
-    float lo = INFINITY, hi = -INFINITY;
-    for (int b = 0; b < kLkScanWgs; ++b) {
-        const float* o = scan + ((int64_t)b * dp + dd) * 3;
-        s += (double)o[0];
-        lo = fminf(lo, o[1]);
-        hi = fmaxf(hi, o[2]);
+    r2 = block_sum_f64(r2, red);
+    if (dd == 0) {
+        int g = 0;
+        if (iso && r2 > 0.0 && isfinite(r2)) {
+            g = ilogb(r2) - 13;
+            g = g < -100 ? -100 : (g > 100 ? 100 : g);
+        }
+        prm[1] = (float)ldexp(1.0, -g);
+        prm[2] = (float)ldexp(1.0, g);
     }
-    // c is rounded to X's storage type, so x - c is exact in fp32 and, for
-    // data within ~2^11 storage ulps of c, exact in fp16 too: no rounding
-    // bias shared by every point of a coarse storage lattice
-    double c = (ns > 0 && isfinite(s)) ? s / (double)ns : 0.0;
-    if (bf16) c = (double)(float)(__bf16)(float)c;
-    else if (fabs(c) < 65504.0) c = (double)(float)(_Float16)(float)c;
-    const double r = fmax((double)hi - c, c - (double)lo);
-    int e = 0;
-    if (r > 0.0 && isfinite(r)) {
-        e = ilogb(r) - 3;
-        e = e < -60 ? -60 : (e > 60 ? 60 : e);
-    }
-    dsc[dd] = make_float2((float)c, (float)ldexp(1.0, -e));
 }
 
-// Score panel and constants of one component per wave (grid Kpad / 4, 256
-// threads).  Lane l handles dimensions l and l + 64.  Panel entry of
-// (array pa, dim dd, component k) lives at half index
-//   (((pa * KS + dd / 32) * nblk + k / 16) * 64 + 16 * ((dd % 32) / 8) + k % 16) * 8 + dd % 8,
-// the B-operand register layout of v_mfma_f32_16x16x32_f16 (lane 16 g + j
-// holds rows 8g..8g+7 of column j).
-__global__ __launch_bounds__(256) void k_lk_panel(int k_real, int d, int dp, bool iso, int nblk,
-                                                  const float* pi, const float* mu,
-                                                  const float* var, const float2* dsc,
-                                                  uint16_t* panel, float* cvec, float* fsc,
-                                                  float* pvec, int* flags) {
+// Score panel of one component per wave (grid Kpad / 4, 256 threads), lane
+// l handling dimensions l and l + 64.  Contraction index i (inner):
+//   diag: [0, DP) A_k (multiplies y'^2), [DP, 2 DP) B_k (multiplies y'),
+//         2 DP + {0, 1}: C_k high / low parts (against ones);
+//   iso:  [0, DP) W_k (multiplies y'), DP + {0, 1, 2}: P_k 2^g high, high, low
+//         (against |y|^2 2^-g high, low, high), DP + {3, 4}: C_k high / low;
+// all multiplied by 2^-f, one power of two for every component, chosen so the
+// largest magnitude of any component lies in [2^13, 2^14).  Entry (i, k)
+// lives at half index ((i / 16 * nblk + k / 32) * 64 + k % 32 + 32 * (i % 16 / 8)) * 8 + i % 8,
+// the A-operand register layout of v_mfma_f32_32x32x16_f16 (lane l holds row
+// l % 32, K values 8 (l / 32) .. + 7).  Padding components: zero entries and
+// C_k = -inf.  Pass 0 writes each component's largest magnitude, the flags
+// and nothing else; pass 1 derives 2^-f from all of them and writes the panel.
+template <bool WRITE>
+__global__ __launch_bounds__(256) void k_lk_panel(int k_real, int kpad, int d, int dp, bool iso,
+                                                  int nblk, const float* pi, const float* mu,
+                                                  const float* var, const float2* dsc, float* kmax,
+                                                  float* prm, uint16_t* panel, int* flags) {
+    __shared__ float red[256];
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * kKpw + (threadIdx.x >> 6);
-    const int KS = dp / 32;
-    const int npa = iso ? 1 : 2;
-    auto put = [&](int pa, int dd, float v) {
-        const _Float16 h = (_Float16)v;
-        const int64_t idx =
-            (((int64_t)(pa * KS + dd / 32) * nblk + k / 16) * 64 + 16 * ((dd % 32) / 8) + k % 16) * 8 + dd % 8;
+    const int inner = (iso ? dp : 2 * dp) + 16;
+    double sc = 1.0;
+    if constexpr (WRITE) {
+        float mx = 0.0f;
+        for (int i = threadIdx.x; i < kpad; i += 256) mx = fmaxf(mx, kmax[i]);
+        red[threadIdx.x] = mx;
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if ((int)threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+            __syncthreads();
+        }
+        const float M = red[0];
+        int f = 0;
+        if (M > 0.0f && isfinite(M)) f = ilogb(M) - 13;
+        sc = ldexp(1.0, -f);
+        if (blockIdx.x == 0 && threadIdx.x == 0) prm[0] = (float)ldexp(1.0, f);
+    }
+    auto put = [&](int i, double v) {
+        const _Float16 h = (_Float16)(float)v;
+        const int64_t idx = (((int64_t)(i / 16) * nblk + k / 32) * 64 + k % 32 + 32 * ((i % 16) / 8)) * 8 + i % 8;
         panel[idx] = __builtin_bit_cast(uint16_t, h);
     };
-    if (k >= k_real) {   // padding component: zero panel, weight 0
-        for (int dd = lane; dd < dp; dd += 64)
-            for (int pa = 0; pa < npa; ++pa) put(pa, dd, 0.0f);
-        if (lane == 0) {
-            cvec[k] = -INFINITY;
-            fsc[k] = 1.0f;
-            pvec[k] = 0.0f;
+    auto put_bias = [&](double c, double pg) {   // the 16 bias slots (lanes 0..15)
+        if (lane >= 16) return;
+        const int b = iso ? dp : 2 * dp;
+        double v = 0.0;
+        // high part, and the remainder when the high part is finite
+        const double ch = (double)(float)(_Float16)(float)c, ph = (double)(float)(_Float16)(float)pg;
+        const double cl = isfinite(ch) ? c - ch : 0.0, pl = isfinite(ph) ? pg - ph : 0.0;
+        if (iso) {
+            if (lane == 0 || lane == 1) v = ph;
+            else if (lane == 2) v = pl;
+            else if (lane == 3) v = ch;
+            else if (lane == 4) v = cl;
+        } else {
+            if (lane == 0) v = ch;
+            else if (lane == 1) v = cl;
+        }
+        put(b + lane, v);
+    };
+    if (k >= k_real) {   // padding component: zero panel, score -inf
+        if constexpr (WRITE) {
+            for (int i = lane; i < inner - 16; i += 64) put(i, 0.0);
+            put_bias(-INFINITY, 0.0);
+        } else if (lane == 0) {
+            kmax[k] = 0.0f;
         }
         return;
     }
+    const double g2 = (double)prm[2];   // 2^g (isotropic |y|^2 scale)
     // unscaled panel entries (fp64) for dims lane, lane + 64
     double ea[2] = {0.0, 0.0}, eb[2] = {0.0, 0.0};
-    double logv = 0.0, m2p = 0.0, mx = 0.0, bad = 0.0, err2 = 0.0;
+    double logv = 0.0, m2p = 0.0, mx = 0.0, bad = 0.0, err2 = 0.0, yt2 = 0.0;
     const double vi = iso ? (double)var[k] : 0.0;
     for (int h = 0; h < 2; ++h) {
         const int dd = lane + 64 * h;
@@ -185,6 +239,7 @@ __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int d, int dp, boo
         const double pr = 1.0 / v;
         // |y| of a point near this component: |mu - c| + 3 sigma
         const double yt = fabs(mc) + 3.0 * sqrt(fabs(v));
+        yt2 += yt * yt;
         if (iso) {
             ea[h] = kLog2e * mc * pr * esc;                 // W
             mx = fmax(mx, fabs(ea[h]));
@@ -204,28 +259,33 @@ __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int d, int dp, boo
     mx = wave_max_f64(mx);
     bad = wave_max_f64(bad);
     err2 = wave_sum_f64(err2);
+    yt2 = wave_sum_f64(yt2);
     if (iso) logv = (double)d * log(vi);
-    // per-component scale: largest entry in [2^13, 2^14)
-    int f = 0;
-    if (mx > 0.0 && isfinite(mx)) f = ilogb(mx) - 13;
-    const double sc = ldexp(1.0, -f);
-    for (int h = 0; h < 2; ++h) {
-        const int dd = lane + 64 * h;
-        if (dd >= dp) continue;
-        put(0, dd, (float)(ea[h] * sc));
-        if (!iso) put(1, dd, (float)(eb[h] * sc));
-    }
-    if (lane == 0) {
-        const double lp = log((double)pi[k]);
-        const double c = kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logv + m2p));
-        cvec[k] = (float)c;
-        fsc[k] = (float)ldexp(1.0, f);
-        pvec[k] = iso ? (float)(-0.5 * kLog2e / vi * sc) : 0.0f;
-        if (bad > 0.0) flags[k] |= 1;
-        // rounding-error estimate of the fp16 expanded score near the mean
-        // (two roundings of relative size <= 2^-11 per term, random signs)
-        if (sqrt(err2) * ldexp(1.0, -11) * (1.41421356 / 1.7320508) * kLn2 > kLkIllCondNats)
-            flags[k] |= 16;
+    const double lp = log((double)pi[k]);
+    const double cst = kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logv + m2p));   // C_k (base 2)
+    const double pg = iso ? -0.5 * kLog2e / vi * g2 : 0.0;                         // P_k 2^g
+    if constexpr (!WRITE) {
+        if (lane == 0) {
+            double m = mx;
+            if (isfinite(cst)) m = fmax(m, fabs(cst));
+            m = fmax(m, fabs(pg));
+            kmax[k] = isfinite(m) ? (float)m : 0.0f;
+            if (bad > 0.0) flags[k] |= 1;
+            // rounding-error estimate of the fp16 expanded score near the mean,
+            // nats: two roundings of relative size <= 2^-11 per panel term
+            // (random signs), the 2^-22 split of C_k and of P_k |y|^2
+            const double e2 = sqrt(err2) * ldexp(1.0, -11) * (1.41421356 / 1.7320508) +
+                              fabs(cst) * ldexp(1.0, -22) + fabs(pg / g2) * yt2 * ldexp(1.0, -21);
+            if (e2 * kLn2 > kLkIllCondNats) flags[k] |= 16;
+        }
+    } else {
+        for (int h = 0; h < 2; ++h) {
+            const int dd = lane + 64 * h;
+            if (dd >= dp) continue;
+            put(dd, ea[h] * sc);
+            if (!iso) put(dp + dd, eb[h] * sc);
+        }
+        put_bias(cst * sc, pg * sc);
     }
 }
 
@@ -377,12 +437,15 @@ hipError_t refresh_panel(const Plan& p, const LkWs& w, const void* x, hipStream_
         hipLaunchKernelGGL(k_lk_scan<false>, dim3(kLkScanWgs), dim3(256), 0, s, (const uint16_t*)x,
                            p.n, p.ldx, (int)p.d, p.dp, w.scan);
     hipLaunchKernelGGL(k_lk_centre, dim3(1), dim3(128), 0, s, p.n, (int)p.d, p.dp,
-                       p.xdt == GMM_BF16, w.scan, w.dsc);
+                       p.xdt == GMM_BF16, iso, w.scan, w.dsc, w.prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lk_panel, dim3(p.lk_kpad / kKpw), dim3(256), 0, s, (int)p.k, (int)p.d, p.dp,
-                       iso, p.lk_kpad / 16, w.pi, w.mu, w.var, w.dsc, (uint16_t*)w.panel, w.cvec,
-                       w.fsc, w.pvec, w.flags);
+    hipLaunchKernelGGL(k_lk_panel<false>, dim3(p.lk_kpad / kKpw), dim3(256), 0, s, (int)p.k, p.lk_kpad,
+                       (int)p.d, p.dp, iso, p.lk_kpad / 32, w.pi, w.mu, w.var, w.dsc, w.kmax, w.prm,
+                       (uint16_t*)w.panel, w.flags);
+    hipLaunchKernelGGL(k_lk_panel<true>, dim3(p.lk_kpad / kKpw), dim3(256), 0, s, (int)p.k, p.lk_kpad,
+                       (int)p.d, p.dp, iso, p.lk_kpad / 32, w.pi, w.mu, w.var, w.dsc, w.kmax, w.prm,
+                       (uint16_t*)w.panel, w.flags);
     return hipGetLastError();
 }
 
@@ -397,10 +460,8 @@ LkArgs make_args(const Plan& p, const LkWs& w, const void* x) {
     a.S = p.lk_slices;
     a.vec = ((uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0) ? 1 : 0;
     a.panel = w.panel;
-    a.nblk = p.lk_kpad / 16;
-    a.cvec = w.cvec;
-    a.fsc = w.fsc;
-    a.pvec = w.pvec;
+    a.nblk = p.lk_kpad / 32;
+    a.prm = w.prm;
     a.dsc = w.dsc;
     a.part = w.part;
     a.part_ll = w.part_ll;
