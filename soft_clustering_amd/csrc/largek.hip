@@ -38,6 +38,8 @@
 // point chunk are mapped to one XCD so X is read from HBM once and re-read
 // from that L2.
 
+#include <type_traits>
+
 #include "largek_internal.h"
 
 namespace gmm {
@@ -102,9 +104,12 @@ __device__ __forceinline__ float h16_to_f32(uint32_t bits16) {
 }
 
 // Eight consecutive 16-bit elements of one row (zeros beyond column d on the
-// element-wise path; the vector path needs d % 8 == 0 and col < d).
-__device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ row, int col, int d, bool vec) {
-    if (vec) return *reinterpret_cast<const uint4*>(row + col);
+// element-wise path; the vector path needs d % 8 == 0 and col < d).  The
+// path is a template argument: a run-time branch joins the two paths'
+// registers, and the join waits for the prefetch loads to land.
+template <bool VEC>
+__device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ row, int col, int d) {
+    if constexpr (VEC) return *reinterpret_cast<const uint4*>(row + col);
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -124,7 +129,7 @@ __device__ __forceinline__ uint2 tr16(const uint16_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int COV, int DP, int MODE, bool BF16>
+template <int COV, int DP, int MODE, bool BF16, bool VEC>
 __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void k_lk(const LkArgs a) {
     constexpr int WV = lk_waves(MODE, COV);     // waves per workgroup
     constexpr int KW = kLkSlice / WV;           // components per wave
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     __shared__ __attribute__((aligned(16))) uint16_t gbuf[kStats ? WV : 1][kStats ? kT * RG : 8];
     __shared__ __attribute__((aligned(16))) uint16_t yh_t[2][kT];   // iso: |y|^2 2^-g, fp16
     __shared__ uint4 plds[WV][CB][KL + 1][64];   // LDS-resident steps of each wave's panel
-    __shared__ float2 dsc_l[DP];       // [e][8-column block]: (c, s) of column 8 block + e
+    __shared__ float2 dsc_l[DP];       // [e][8-column block], column 8 block + e: iso (c, s), diag (s, -c s)
     __shared__ float2 wpart[WV][kT];   // per-wave (max, sum) of each point, base-2 score units
     __shared__ int warg[WV][kT];
     __shared__ double llred[NT];
@@ -191,7 +196,10 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
             else plds[w][cb][ks < KL ? ks : KL][lane] = v;
         }
     }
-    for (int i = tid; i < DP; i += NT) dsc_l[(i % 8) * Sh::kCB + i / 8] = a.dsc[i];
+    for (int i = tid; i < DP; i += NT) {
+        const float2 cs = a.dsc[i];   // (c, s)
+        dsc_l[(i % 8) * Sh::kCB + i / 8] = kIso ? cs : make_float2(cs.y, -cs.x * cs.y);
+    }
 
     // ---- this chunk's tiles
     const int64_t tiles = (n + kT - 1) / kT;
@@ -215,103 +223,130 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     float rng = 0.0f;   // diag: largest (y')^2 staged; iso: largest |y|^2 2^-g (clamped above fp16 max)
 
     // ---- staging: item (row, 8-column block); the kCB items of a row sit in
-    // consecutive lanes
+    // consecutive lanes and every item of a thread has the same column block.
+    // Rows beyond N repeat the tile's last row (their responsibilities are
+    // zeroed and their LSE is not written); columns beyond D read as zero.
+    // The conversion is straight-line code, so it can be interleaved with the
+    // score MFMAs of the previous tile.
+    static_assert(NT % Sh::kCB == 0, "column block fixed per thread");
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
+    const int cbk = tid % Sh::kCB, col0 = 8 * cbk;
+    const bool col_ok = col0 < d;
     uint4 raw[IPT];
 #pragma unroll
     for (int q = 0; q < IPT; ++q) raw[q] = make_uint4(0, 0, 0, 0);
-    float lse_pf = 0.0f;
-    int rows_in = 0;
+    float lse_nx = 0.0f;
 
     auto load_tile = [&](int64_t t) {
         const int64_t p0 = t * kT;
         const int64_t left = n - p0;
-        rows_in = left >= kT ? kT : (int)left;
+        const int last = (left >= kT ? kT : (int)left) - 1;
 #pragma unroll
         for (int q = 0; q < IPT; ++q) {
             const int it = tid + NT * q;
-            if (it < Sh::kItems) {
-                const int r = it / Sh::kCB, col0 = 8 * (it % Sh::kCB);
-                const int rr = r < rows_in ? r : rows_in - 1;
-                raw[q] = load8(xb + (p0 + rr) * a.ldx, col0 < d ? col0 : 0, d, a.vec);
+            if (Sh::kItems % NT == 0 || it < Sh::kItems) {
+                const int r = it / Sh::kCB;
+                raw[q] = load8<VEC>(xb + (p0 + (r < last ? r : last)) * a.ldx, col_ok ? col0 : 0, d);
             }
         }
-        if constexpr (MODE == LK_SWEEP2) lse_pf = p0 + pn < n ? a.lse_in[p0 + pn] : INFINITY;   // gamma = 0
     };
+    // sweep 2: merged LSE of point pn of tile t (+inf beyond N: gamma = 0)
+    auto load_lse = [&](int64_t t) { const int64_t p = t * kT + pn; return p < n ? a.lse_in[p] : INFINITY; };
 
-    auto store_tile = [&](int buf) {
+    // isotropic bias slots of a row, [yh, yl, yh, 1, 1, 0...]: this lane's 16 / kCB of them
+    constexpr int kSlots = 16 / Sh::kCB;
+    constexpr int kPairs = 4 * IPT;       // staging steps: two columns of one item each
+    uint32_t hy[4], hq[4];                // packed y' and y'^2 of the current item
+    float ss = 0.0f;                      // isotropic: partial |y|^2 of the current item
+    // staging step s: columns 2 (s % 4), +1 of item s / 4; the item's chunks are
+    // written after its fourth step
+    auto stage_pair = [&](int buf, int sp) {
+        const int q = sp / 4, pr = sp % 4;
+        const int it = tid + NT * q;
+        if (Sh::kItems % NT != 0 && it >= Sh::kItems) return;   // whole waves idle
         uint16_t* yb = ybuf[buf];
+        const int r = it / Sh::kCB;
+        const uint32_t wd = col_ok ? (pr == 0 ? raw[q].x : pr == 1 ? raw[q].y : pr == 2 ? raw[q].z : raw[q].w) : 0u;
+        if (pr == 0) ss = 0.0f;
+        float yp[2];
 #pragma unroll
-        for (int q = 0; q < IPT; ++q) {
-            const int it = tid + NT * q;
-            if (Sh::kItems % NT != 0 && it >= Sh::kItems) continue;   // whole waves idle
-            const int r = it / Sh::kCB, cbk = it % Sh::kCB, col0 = 8 * cbk;
-            const bool row_ok = r < rows_in;
-            const uint32_t wv[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-            float yp[8], ss = 0.0f;
-            const bool full = rows_in == kT && d == DP;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
-                const float2 cs = dsc_l[e * Sh::kCB + cbk];
-                float y = h16_to_f32<BF16>(bits) - cs.x;
-                if (!full) y = (row_ok && col0 + e < d) ? y : 0.0f;
-                if constexpr (kIso) ss = fmaf(y, y, ss);
-                yp[e] = y * cs.y;
-            }
-            const int off_y = kIso ? 0 : DP;
-            *reinterpret_cast<uint4*>(yb + Sh::ych(r, (off_y + col0) / 8)) =
-                make_uint4(pack_h2(yp[0], yp[1]), pack_h2(yp[2], yp[3]), pack_h2(yp[4], yp[5]),
-                           pack_h2(yp[6], yp[7]));
-            if constexpr (!kIso) {
-                float y2[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = yp[e] * yp[e];
-                    rng = fmaxf(rng, v);
-                    y2[e] = fminf(v, kF16Max);
-                }
-                *reinterpret_cast<uint4*>(yb + Sh::ych(r, col0 / 8)) =
-                    make_uint4(pack_h2(y2[0], y2[1]), pack_h2(y2[2], y2[3]), pack_h2(y2[4], y2[5]),
-                               pack_h2(y2[6], y2[7]));
+        for (int h = 0; h < 2; ++h) {
+            const int e = 2 * pr + h;
+            const float2 cs = dsc_l[e * Sh::kCB + cbk];
+            const float x = h16_to_f32<BF16>(h ? wd >> 16 : wd & 0xFFFFu);
+            if constexpr (kIso) {
+                const float y = col_ok ? x - cs.x : 0.0f;   // dsc_l: (c, s)
+                ss = fmaf(y, y, ss);
+                yp[h] = y * cs.y;
             } else {
-                // |y|^2 of the row: the kCB lanes of a row are consecutive
-                if constexpr (Sh::kCB >= 2) ss += dpp<kDppXor1>(ss);
-                if constexpr (Sh::kCB >= 4) ss += dpp<kDppXor2>(ss);
-                if constexpr (Sh::kCB >= 8) ss += dpp<kDppHalfMirror>(ss);
-                if constexpr (Sh::kCB >= 16) ss += dpp<kDppMirror>(ss);
+                yp[h] = fmaf(x, cs.x, cs.y);                 // dsc_l: (s, -c s)
             }
-            if (cbk == 0) {
-                // bias slots: diag [1, 1]; iso [yh, yl, yh, 1, 1] with yh + yl = |y|^2 2^-g
-                uint32_t bw[4];
-                if constexpr (kIso) {
-                    const float v = ss * ysc;
-                    rng = fmaxf(rng, v);
-                    const float vc = fminf(v, kF16Max);
-                    const _Float16 yh = (_Float16)vc;
-                    const float yl = vc - (float)yh;
-                    const uint32_t hb = __builtin_bit_cast(uint16_t, yh);
-                    bw[0] = hb | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)yl) << 16);
-                    bw[1] = hb | (0x3C00u << 16);
-                    bw[2] = 0x3C00u;
-                    bw[3] = 0u;
-                    yh_t[buf][r] = (uint16_t)hb;
-                } else {
-                    bw[0] = 0x3C003C00u;
-                    bw[1] = bw[2] = bw[3] = 0u;
+        }
+        hy[pr] = pack_h2(yp[0], yp[1]);
+        if constexpr (!kIso) {
+            const float v0 = yp[0] * yp[0], v1 = yp[1] * yp[1];
+            rng = fmaxf(rng, fmaxf(v0, v1));
+            hq[pr] = pack_h2(fminf(v0, kF16Max), fminf(v1, kF16Max));
+        }
+        if (pr == 3) {
+            const int off_y = kIso ? 0 : DP;
+            *reinterpret_cast<uint4*>(yb + Sh::ych(r, (off_y + col0) / 8)) = make_uint4(hy[0], hy[1], hy[2], hy[3]);
+            if constexpr (!kIso) {
+                *reinterpret_cast<uint4*>(yb + Sh::ych(r, col0 / 8)) = make_uint4(hq[0], hq[1], hq[2], hq[3]);
+            } else {
+                // |y|^2 of the row over its kCB consecutive lanes
+                float t2 = ss;
+                if constexpr (Sh::kCB >= 2) t2 += dpp<kDppXor1>(t2);
+                if constexpr (Sh::kCB >= 4) t2 += dpp<kDppXor2>(t2);
+                if constexpr (Sh::kCB >= 8) t2 += dpp<kDppHalfMirror>(t2);
+                if constexpr (Sh::kCB >= 16) t2 += dpp<kDppMirror>(t2);
+                const float v = t2 * ysc;
+                rng = fmaxf(rng, v);
+                const float vc = fminf(v, kF16Max);
+                const _Float16 yh = (_Float16)vc;
+                const uint16_t hb = __builtin_bit_cast(uint16_t, yh);
+                const uint16_t lb = __builtin_bit_cast(uint16_t, (_Float16)(vc - (float)yh));
+                uint16_t sv[kSlots];
+#pragma unroll
+                for (int m = 0; m < kSlots; ++m) {
+                    const int slot = kSlots * cbk + m;
+                    sv[m] = slot == 0 || slot == 2 ? hb : slot == 1 ? lb : (slot == 3 || slot == 4) ? 0x3C00 : 0;
                 }
-                uint4* bias = reinterpret_cast<uint4*>(yb + Sh::ych(r, Sh::kFCh));
-                bias[0] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-                bias[1] = make_uint4(0, 0, 0, 0);
+                uint16_t* bp = yb + Sh::ych(r, Sh::kFCh) + kSlots * cbk;
+                if constexpr (kSlots == 1) *bp = sv[0];
+                else if constexpr (kSlots == 2) *reinterpret_cast<uint32_t*>(bp) = sv[0] | ((uint32_t)sv[1] << 16);
+                else *reinterpret_cast<uint2*>(bp) = make_uint2(sv[0] | ((uint32_t)sv[1] << 16),
+                                                                 sv[2] | ((uint32_t)sv[3] << 16));
+                yh_t[buf][r] = hb;   // the kCB lanes of the row store the same value
             }
         }
     };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int sp = 0; sp < kPairs; ++sp) stage_pair(buf, sp);
+    };
 
+    // diagonal bias slots: constant [1, 1, 0...] in both tile buffers
+    if constexpr (!kIso) {
+        for (int i = tid; i < 2 * kT; i += NT) {
+            uint4* bias = reinterpret_cast<uint4*>(ybuf[i / kT] + Sh::ych(i % kT, Sh::kFCh));
+            bias[0] = make_uint4(0x3C003C00u, 0u, 0u, 0u);
+            bias[1] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    // pipeline: tile t+1 is staged (from registers loaded during tile t-1)
+    // while tile t's scores run, then tile t+2's loads are issued
     if (t0 < t1) {
         load_tile(t0);
         __syncthreads();   // dsc_l
         store_tile(0);
+        load_tile(t0 + 1 < t1 ? t0 + 1 : t0);
+        if constexpr (MODE == LK_SWEEP2) lse_nx = load_lse(t0);
     }
+    // every prologue load (the panel above all) has landed: no wait inside the
+    // tile loop depends on them
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int64_t t = t0; t < t1; ++t) {
@@ -320,8 +355,10 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
         const int64_t prow = t * kT;
         const bool pvalid = prow + pn < n;
         float lse_cur = 0.0f;
-        if constexpr (MODE == LK_SWEEP2) lse_cur = lse_pf;
-        if (t + 1 < t1) load_tile(t + 1);
+        if constexpr (MODE == LK_SWEEP2) {
+            lse_cur = lse_nx;
+            lse_nx = load_lse(t + 1 < t1 ? t + 1 : t);
+        }
 
         // ---- scores (acc units; S = F acc), one 32-component block at a time:
         // lane (pn, hf), register r of block cb holds point pn and component
@@ -351,6 +388,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
             };
 #pragma unroll
             for (int ks = 0; ks < kPF && ks < KS; ++ks) issue(ks);
+            // step ks: the MFMAs of step ks, then one staging step of the next tile
+            // (the other buffer) while they run; the order is pinned per step
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (ks + kPF < KS) issue(ks + kPF);
@@ -359,17 +398,13 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                     const half8 pa = in_lds(ks) ? pq[cb][ks] : pnl[cb][in_lds(ks) ? 0 : ks - KL];
                     scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
                 }
+                if (ks < kPairs) stage_pair(cur ^ 1, ks);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            constexpr int kFirst = kPF + CB * (kPF < KL ? kPF : KL);   // reads issued up front
-            __builtin_amdgcn_sched_group_barrier(0x100, kFirst, 0);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ks + kPF < KS) {
-                    if (in_lds(ks + kPF)) __builtin_amdgcn_sched_group_barrier(0x100, 1 + CB, 0);
-                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
-            }
+            for (int sp = KS; sp < kPairs; ++sp) stage_pair(cur ^ 1, sp);
+            // the loads of the tile after next
+            load_tile(t + 2 < t1 ? t + 2 : t1 - 1);
         }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -540,8 +575,6 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
             }
         }
 
-        __builtin_amdgcn_sched_barrier(0);   // staging after the statistics: bounded live ranges
-        if (t + 1 < t1) store_tile(cur ^ 1);
         __syncthreads();
     }
 
@@ -590,13 +623,18 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     }
 }
 
+template <int COV, int DP, int MODE, bool VEC>
+hipError_t launch4(const Plan& p, const LkArgs& a, int grid, hipStream_t s) {
+    if (p.xdt == GMM_BF16)
+        hipLaunchKernelGGL((k_lk<COV, DP, MODE, true, VEC>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_lk<COV, DP, MODE, false, VEC>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int COV, int DP, int MODE>
 hipError_t launch3(const Plan& p, const LkArgs& a, int grid, hipStream_t s) {
-    if (p.xdt == GMM_BF16)
-        hipLaunchKernelGGL((k_lk<COV, DP, MODE, true>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_lk<COV, DP, MODE, false>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
-    return hipGetLastError();
+    return a.vec ? launch4<COV, DP, MODE, true>(p, a, grid, s) : launch4<COV, DP, MODE, false>(p, a, grid, s);
 }
 
 template <int COV, int MODE>
