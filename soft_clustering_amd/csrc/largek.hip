@@ -258,6 +258,11 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     constexpr int kPairs = 4 * IPT;       // staging steps: two columns of one item each
     uint32_t hy[4], hq[4];                // packed y' and y'^2 of the current item
     float ss = 0.0f;                      // isotropic: partial |y|^2 of the current item
+    float2 dq[8];                         // this thread's 8 (centre, scale) pairs, read once per tile
+    auto dsc_fetch = [&]() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dq[e] = dsc_l[e * Sh::kCB + cbk];
+    };
     // staging step s: columns 2 (s % 4), +1 of item s / 4; the item's chunks are
     // written after its fourth step
     auto stage_pair = [&](int buf, int sp) {
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int e = 2 * pr + h;
-            const float2 cs = dsc_l[e * Sh::kCB + cbk];
+            const float2 cs = dq[e];
             const float x = h16_to_f32<BF16>(h ? wd >> 16 : wd & 0xFFFFu);
             if constexpr (kIso) {
                 const float y = col_ok ? x - cs.x : 0.0f;   // dsc_l: (c, s)
@@ -322,6 +327,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
         }
     };
     auto store_tile = [&](int buf) {
+        dsc_fetch();
 #pragma unroll
         for (int sp = 0; sp < kPairs; ++sp) stage_pair(buf, sp);
     };
@@ -386,6 +392,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                     for (int cb = 0; cb < CB; ++cb)
                         pq[cb][ks] = __builtin_bit_cast(half8, plds[w][cb][ks < KL ? ks : KL][lane]);
             };
+            dsc_fetch();
 #pragma unroll
             for (int ks = 0; ks < kPF && ks < KS; ++ks) issue(ks);
             // step ks: the MFMAs of step ks, then one staging step of the next tile
