@@ -12,21 +12,34 @@ namespace gmm {
 #define GMM_DIAG_SHAPES(X) \
     X(16, 1) X(16, 2) X(16, 3) X(16, 4) X(32, 1) X(32, 2) X(32, 3) X(32, 4) X(64, 1) X(64, 2) X(128, 1)
 
-// Fused-kernel launch configuration: waves per workgroup (each wave walks its
-// own run of 16-point groups through a 3-slot LDS ring) and one workgroup per
-// CU (grid = CUs, capped by the partial slots and by the number of groups).
-// Eight waves (two per SIMD) when the ring fits in LDS (D <= 64: 104 KB),
-// four for D = 128 (101 KB).  Measured on the 1e6 x 64 x 16 workload:
-// 8 waves x 1 workgroup/CU 108 us, 4 x 2 111 us, 4 x 1 118 us, 2 x 2 182 us.
-constexpr int diag_waves(int dp) { return dp <= 64 ? 8 : 4; }
+// Fused-kernel launch configuration: one workgroup per CU (grid = CUs,
+// capped by the partial slots and by the number of 32-point tiles), each
+// wave walking its own run of tiles.  Each wave holds a 32-point tile pair
+// (fp16 hi / lo, 16 KB for D <= 64, 32 KB for D = 128) in LDS and the split
+// panel plus the statistic accumulators in registers: eight waves (two per
+// SIMD) while that fits 256 registers per lane, else four.
 constexpr int kDiagWgPerCu = 1;
+__host__ __device__ constexpr int diag_split_waves(int dp, int kb) {
+    return (dp <= 64 && dp * kb <= 64) ? 8 : 4;
+}
+
+// |y| bound of the split-fp16 operands: y^2 stays below the fp16 maximum
+// (65504) with margin; a tile with any larger |y| takes the fp32 route.
+constexpr float kSplitLim = 224.0f;
+
+// Halves of the split panel (hi, then lo): 2 x (2 DP / 32) k-steps x KB
+// component blocks x 64 lanes x 8 halves.
+inline size_t diag_panel16_halves(int dp, int kb) { return (size_t)2 * (dp / 16) * kb * 64 * 8; }
 
 // Dimensions per chunk of the M-step / normaliser sums.
 constexpr int kDiagChunkDims = 32;
 inline int diag_chunks(const Plan& p) { return (int)((p.d + kDiagChunkDims - 1) / kDiagChunkDims); }
 
 struct DiagWs {
-    float *pi, *mu, *var, *shift, *panel;
+    float *pi, *mu, *var, *panel;
+    float *shift, *scale;   // [DP] centre c and power-of-two scale s: y = (x - c) s
+    uint4* panel16;         // split fp16 panel (hi, lo) of [a ; b] in y units / F_k
+    float* fk;              // [16 KB] per-component panel scale F_k (power of two)
     double *part, *part_ll, *stats, *ll;
     int *flags, *retries, *nonfinite_ll;
     double* chunk_part;   // [K][chunks][4]: sum log var, sum (mu-c)^2/var, #bad, #non-finite
@@ -38,7 +51,10 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
     w.mu = (float*)(ws + p.off_mu);
     w.var = (float*)(ws + p.off_cov);
     w.shift = (float*)(ws + p.off_shift);
+    w.scale = w.shift + p.dp;
     w.panel = (float*)(ws + p.off_panel);
+    w.panel16 = (uint4*)(ws + p.off_panel + align_up(sizeof(float) * (p.dp / 4) * 2 * p.kb * 64, 256));
+    w.fk = (float*)((char*)w.panel16 + sizeof(uint16_t) * diag_panel16_halves(p.dp, p.kb));
     w.part = (double*)(ws + p.off_part);
     w.part_ll = (double*)(ws + p.off_part_ll);
     w.stats = (double*)(ws + p.off_stats);
@@ -53,9 +69,10 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
 // Number of workgroups (= partial slots) of the fused kernel for this plan.
 int diag_grid(const Plan& p);
 
-// Launch the fused kernel: EM = statistics + LL partials; otherwise E-step
-// only with optional per-point outputs.  Defined in diag_fused.hip.
-hipError_t diag_launch_fused(const Plan& p, const DiagWs& w, const void* x, bool em, int grid,
+// Launch the fused split-fp16 kernel (diag_split.hip): EM = statistics + LL
+// partials (moments of y = (x - c) s, undone by the reduction); otherwise
+// E-step only with optional per-point outputs.
+hipError_t diag_launch_split(const Plan& p, const DiagWs& w, const void* x, bool em, int grid,
                              float* lse, int* arg, hipStream_t s);
 
 }  // namespace gmm

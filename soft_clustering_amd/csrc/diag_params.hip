@@ -46,6 +46,30 @@ __device__ __forceinline__ void put_panel(float* panel, int k, int dd, float a, 
 // gmm_prepare: copy theta into the workspace, choose the centre, build the
 // panel and the per-chunk normaliser sums.  Grid: 16*KB workgroups (one per
 // padded component), 256 threads.
+// Power-of-two scale s of dimension dd for the split-fp16 operands
+// y = (x - c) s: the widest reach of the components that hold weight,
+// max_k |mu_k - c| + 4 sigma_k over pi_k > 0, maps into [4, 8), so data
+// within the model's spread has |y| < 8 and the fp16 range (|y| <
+// kSplitLim) leaves a factor of about 28 for points beyond it.  1 when the
+// reach is zero or not finite.
+template <int KMAX>
+__device__ __forceinline__ float dim_scale(int k_real, int d, int dd, float c, const float* pi,
+                                           const float* mu, const float* var) {
+    float reach = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KMAX; ++kk) {   // unrolled: the loads issue together
+        if (kk < k_real) {
+            const float v = var[(int64_t)kk * d + dd];
+            const float r = fabsf(mu[(int64_t)kk * d + dd] - c) + 4.0f * sqrtf(v > 0.0f ? v : 0.0f);
+            if (pi[kk] > 0.0f && isfinite(r)) reach = fmaxf(reach, r);
+        }
+    }
+    if (!(reach > 0.0f) || !isfinite(reach)) return 1.0f;
+    int e = ilogbf(reach) - 2;
+    e = e < -60 ? -60 : (e > 60 ? 60 : e);
+    return ldexpf(1.0f, -e);
+}
+
 template <int DP, int KB>
 __global__ __launch_bounds__(256) void k_diag_prepare(int k_real, int d, const float* pi,
                                                       const float* mu, const float* var,
@@ -109,6 +133,59 @@ __global__ __launch_bounds__(256) void k_diag_prepare(int k_real, int d, const f
     }
 }
 
+// Split fp16 panel of the split kernel from the prepared fp32 parameters
+// (after gmm_prepare and after every finalize): the per-dimension scale s
+// (every workgroup derives the same one; workgroup 0 stores it for the
+// reduction of the coming step), and the entries
+// a_kd = -1/2 log2(e) / (var s^2) and b_kd = log2(e) (mu - c) / (var s)
+// (y units), divided by the component's power of two F_k that puts its
+// largest entry in [2^14, 2^15), each stored as hi = fp16(v), lo = fp16(v - hi)
+// in the B-operand layout of v_mfma_f32_16x16x32_f16: contraction index kk
+// (a at kk = dd, b at kk = DP + dd) of component k sits in k-step kk / 32,
+// block k / 16, lane 16 ((kk % 32) / 8) + k % 16, half kk % 8.  Padding
+// components and dimensions get zeros (F = 1).  Grid: 16 KB workgroups (one
+// per padded component), DP threads.
+template <int DP, int KB>
+__global__ __launch_bounds__(DP) void k_diag_split_panel(int k_real, int d, const float* th_pi,
+                                                         const float* th_mu, const float* th_var,
+                                                         const float* shift, float* scale,
+                                                         uint16_t* panel16, float* fk) {
+    __shared__ float red[DP];
+    const int k = blockIdx.x, dd = threadIdx.x;
+    const float sd = dd < d ? dim_scale<16 * KB>(k_real, d, dd, shift[dd], th_pi, th_mu, th_var) : 1.0f;
+    if (k == 0) scale[dd] = sd;
+    double a = 0.0, b = 0.0;
+    if (k < k_real && dd < d) {
+        const int64_t i = (int64_t)k * d + dd;
+        const double s = sd;
+        const double pr = 1.0 / (double)th_var[i];
+        a = -0.5 * pr * kLog2e / (s * s);
+        b = ((double)th_mu[i] - (double)shift[dd]) * pr * kLog2e / s;
+    }
+    const float m = (float)fmax(fabs(a), fabs(b));
+    red[dd] = isfinite(m) ? m : 0.0f;
+    __syncthreads();
+    for (int st = DP / 2; st > 0; st >>= 1) {
+        if (dd < st) red[dd] = fmaxf(red[dd], red[dd + st]);
+        __syncthreads();
+    }
+    const float mx = red[0];
+    const int fe = mx > 0.0f ? ilogbf(mx) - 14 : 0;
+    const double inv = ldexp(1.0, -fe);
+    constexpr size_t kLo = (size_t)(DP / 16) * KB * 64 * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kk = h * DP + dd;
+        const float v = (float)((h == 0 ? a : b) * inv);
+        const _Float16 hi = (_Float16)v;
+        const _Float16 lo = (_Float16)(v - (float)hi);
+        const size_t o = ((size_t)((kk / 32) * KB + k / 16) * 64 + 16 * ((kk % 32) / 8) + k % 16) * 8 + kk % 8;
+        panel16[o] = __builtin_bit_cast(uint16_t, hi);
+        panel16[kLo + o] = __builtin_bit_cast(uint16_t, lo);
+    }
+    if (dd == 0) fk[k] = ldexpf(1.0f, fe);
+}
+
 // Reduce the per-workgroup partials, M-step, and prepare the next iteration.
 // Grid (chunks of 32 dimensions, K).  In workgroup (ch, k), lane l of wave w
 // sums column 1 + 64 ch + l over the slots p = w, w + 4, w + 8, ... (fixed
@@ -121,7 +198,8 @@ template <int DP, int KB>
 __global__ __launch_bounds__(256) void k_diag_reduce_finalize(
     const double* __restrict__ part, int P, int64_t n, int d, int k_real, float var_floor,
     double* __restrict__ stats, float* __restrict__ th_pi, float* __restrict__ th_mu,
-    float* __restrict__ th_var, const float* __restrict__ shift, float* __restrict__ out_pi,
+    float* __restrict__ th_var, const float* __restrict__ shift, const float* __restrict__ scale,
+    float* __restrict__ out_pi,
     float* __restrict__ out_mu, float* __restrict__ out_var, float* __restrict__ panel,
     int* __restrict__ flags, double* __restrict__ chunk_part) {
     __shared__ double colw[4][64];
@@ -157,9 +235,11 @@ __global__ __launch_bounds__(256) void k_diag_reduce_finalize(
     if (tid < kDiagChunkDims) {
         const int dd = kDiagChunkDims * ch + tid;
         if (dd < d) {
-            const double t1 = (colw[0][2 * tid] + colw[1][2 * tid]) + (colw[2][2 * tid] + colw[3][2 * tid]);
-            const double t2 = (colw[0][2 * tid + 1] + colw[1][2 * tid + 1]) +
-                              (colw[2][2 * tid + 1] + colw[3][2 * tid + 1]);
+            // moments of y = (x - c) s back to x - c (s is a power of two: exact)
+            const double is = 1.0 / (double)scale[dd];
+            const double t1 = ((colw[0][2 * tid] + colw[1][2 * tid]) + (colw[2][2 * tid] + colw[3][2 * tid])) * is;
+            const double t2 = ((colw[0][2 * tid + 1] + colw[1][2 * tid + 1]) +
+                               (colw[2][2 * tid + 1] + colw[3][2 * tid + 1])) * is * is;
             const double c = shift[dd];
             const int64_t i = (int64_t)k * d + dd;
             // raw moments: sum g x = t1 + c s0, sum g x^2 = t2 + 2 c t1 + c^2 s0
@@ -230,8 +310,8 @@ bool diag_shape_supported(int dp, int kb) {
 }
 
 int diag_grid(const Plan& p) {
-    const int64_t groups = (p.n + 15) / 16;                     // 16-point groups
-    const int64_t per_wg = diag_waves(p.dp);                    // at least one per wave
+    const int64_t groups = (p.n + 31) / 32;                     // 32-point tiles
+    const int64_t per_wg = diag_split_waves(p.dp, p.kb);        // at least one per wave
     int64_t g = (int64_t)kDiagWgPerCu * device_cu_count();
     if (g > p.p_max) g = p.p_max;
     const int64_t need = (groups + per_wg - 1) / per_wg;
@@ -248,6 +328,9 @@ gmm_status diag_prepare(const Plan& p, char* ws, const float* pi, const float* m
         hipLaunchKernelGGL((k_diag_prepare<DP_, KB_>), dim3(16 * KB_), dim3(256), 0, s, (int)p.k, \
                            (int)p.d, pi, mu, var, w.pi, w.mu, w.var, w.shift, w.panel,           \
                            w.chunk_part, w.flags);                                               \
+        hipLaunchKernelGGL((k_diag_split_panel<DP_, KB_>), dim3(16 * KB_), dim3(DP_), 0, s,      \
+                           (int)p.k, (int)p.d, w.pi, w.mu, w.var, w.shift, w.scale,             \
+                           (uint16_t*)w.panel16, w.fk);                                         \
         e = hipGetLastError();                                                                  \
     }
     GMM_DIAG_SHAPES(CASE)
@@ -264,7 +347,7 @@ static gmm_status sum_ll(const Plan& p, const DiagWs& w, int P, double* ll_out, 
 gmm_status diag_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
     DiagWs w = diag_ws(p, ws);
     const int P = diag_grid(p);
-    hipError_t e = diag_launch_fused(p, w, x, true, P, nullptr, nullptr, s);
+    hipError_t e = diag_launch_split(p, w, x, true, P, nullptr, nullptr, s);
     if (e != hipSuccess) return GMM_E_HIP;
     return sum_ll(p, w, P, ll_out, s);
 }
@@ -279,7 +362,10 @@ gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* v
     if (p.dp == DP_ && p.kb == KB_) {                                                             \
         hipLaunchKernelGGL((k_diag_reduce_finalize<DP_, KB_>), dim3(nch, p.k), dim3(256), 0, s,    \
                            w.part, P, p.n, (int)p.d, (int)p.k, p.var_floor, w.stats, w.pi, w.mu,  \
-                           w.var, w.shift, pi, mu, var, w.panel, w.flags, w.chunk_part);          \
+                           w.var, w.shift, w.scale, pi, mu, var, w.panel, w.flags, w.chunk_part); \
+        hipLaunchKernelGGL((k_diag_split_panel<DP_, KB_>), dim3(16 * KB_), dim3(DP_), 0, s,        \
+                           (int)p.k, (int)p.d, w.pi, w.mu, w.var, w.shift, w.scale,               \
+                           (uint16_t*)w.panel16, w.fk);                                           \
         e = hipGetLastError();                                                                    \
     }
     GMM_DIAG_SHAPES(CASE)
@@ -292,7 +378,7 @@ gmm_status diag_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
     DiagWs w = diag_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int P = diag_grid(p);
-    hipError_t e = diag_launch_fused(p, w, x, false, P, lse, argmax, s);
+    hipError_t e = diag_launch_split(p, w, x, false, P, lse, argmax, s);
     if (e != hipSuccess) return GMM_E_HIP;
     return sum_ll(p, w, P, ll_out, s);
 }

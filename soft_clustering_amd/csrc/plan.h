@@ -9,7 +9,7 @@
 namespace gmm {
 
 enum Path : int {
-    PATH_DIAG_F32 = 0,   // diagonal, fp32 MFMA scores and statistics, K <= 64
+    PATH_DIAG_F32 = 0,   // diagonal, K <= 64: fp32-accurate split-fp16 MFMA scores and statistics
     PATH_LARGEK = 1,     // isotropic / diagonal, X in bf16 or fp16, fp16 MFMA, K <= 4096
     PATH_FULL = 2,       // full covariance, X in fp16, fp16 L, fp32 solve, K <= 16, D <= 64
 };
@@ -46,7 +46,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* plan);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Entry points of the diagonal fp32 family (diag_params.hip, diag_fused.hip).
+// Entry points of the diagonal family (diag_params.hip, diag_split.hip).
 gmm_status diag_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
                         const float* var, hipStream_t s);
 gmm_status diag_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s);

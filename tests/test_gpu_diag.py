@@ -172,6 +172,34 @@ def test_degenerate_cases(gmm_lib):
     assert th[0].item() == 1.0
 
 
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_outlier_tiles_take_the_fp32_route(gmm_lib, x_dtype):
+    """Points far outside the components' spread leave the fp16 operand range
+    of the split kernel; their 32-point tiles (first, middle, ragged last)
+    are computed with fp32 operands, and the step still matches the oracle."""
+    n, d, k = 3001, 16, 5
+    xd, xg, ldx, th0 = _make(n, d, k, x_dtype, 0, False, seed=77)
+    far = np.zeros(n, bool)
+    for row, v in ((3, 5000.0), (1500, -3000.0), (2999, 8000.0)):
+        far[row] = True
+        xg[row, 2::3] = v
+    xd = xg.double().cpu().numpy()
+    gm = gmm_lib.Gmm(n, d, k, "diag", x_dtype, ldx=ldx)
+    pi, mu, cov = to_dev(*th0)
+    ll, st, th = gpu_step(gm, xg, pi, mu, cov)
+    ref = oracle.em_step(xd, params64("diag", pi, mu, cov))
+    check_step(ref, ll, st, th, what=f"outliers {x_dtype}")
+    gm.prepare(pi, mu, cov)
+    ll2 = torch.zeros(1, dtype=torch.float64, device="cuda")
+    lse = torch.full((n,), float("nan"), device="cuda")
+    gm.loglik(xg, ll2, lse, None)
+    torch.cuda.synchronize()
+    _, lse_ref, _ = oracle.loglik(xd, params64("diag", pi, mu, cov))
+    got = lse.cpu().numpy()
+    np.testing.assert_allclose(got[~far], lse_ref[~far], rtol=2e-5, atol=2e-3)
+    np.testing.assert_allclose(got[far], lse_ref[far], rtol=2e-5)
+
+
 def test_nonfinite_input_is_flagged(gmm_lib):
     rng = np.random.default_rng(4)
     x = rng.standard_normal((300, 4)).astype(np.float32)
