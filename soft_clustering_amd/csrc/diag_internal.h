@@ -40,6 +40,7 @@ struct DiagWs {
     float *shift, *scale;   // [DP] centre c and power-of-two scale s: y = (x - c) s
     uint4* panel16;         // split fp16 panel (hi, lo) of [a ; b] in y units / F_k
     float* fk;              // [16 KB] per-component panel scale F_k (power of two)
+    float* ck;              // [16 KB] per-component log2 normaliser c_k (-inf: padding)
     double *part, *part_ll, *stats, *ll;
     int *flags, *retries, *nonfinite_ll;
     double* chunk_part;   // [K][chunks][4]: sum log var, sum (mu-c)^2/var, #bad, #non-finite
@@ -55,6 +56,7 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
     w.panel = (float*)(ws + p.off_panel);
     w.panel16 = (uint4*)(ws + p.off_panel + align_up(sizeof(float) * (p.dp / 4) * 2 * p.kb * 64, 256));
     w.fk = (float*)((char*)w.panel16 + sizeof(uint16_t) * diag_panel16_halves(p.dp, p.kb));
+    w.ck = w.fk + 16 * p.kb;
     w.part = (double*)(ws + p.off_part);
     w.part_ll = (double*)(ws + p.off_part_ll);
     w.stats = (double*)(ws + p.off_stats);

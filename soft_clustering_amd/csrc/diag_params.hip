@@ -55,14 +55,20 @@ __device__ __forceinline__ void put_panel(float* panel, int k, int dd, float a, 
 template <int KMAX>
 __device__ __forceinline__ float dim_scale(int k_real, int d, int dd, float c, const float* pi,
                                            const float* mu, const float* var) {
+    // all loads first (clamped, always in bounds) so that they issue together
+    float vv[KMAX], mv[KMAX], pv[KMAX];
+#pragma unroll
+    for (int kk = 0; kk < KMAX; ++kk) {
+        const int kc = kk < k_real ? kk : k_real - 1;
+        vv[kk] = var[(int64_t)kc * d + dd];
+        mv[kk] = mu[(int64_t)kc * d + dd];
+        pv[kk] = kk < k_real ? pi[kc] : 0.0f;
+    }
     float reach = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KMAX; ++kk) {   // unrolled: the loads issue together
-        if (kk < k_real) {
-            const float v = var[(int64_t)kk * d + dd];
-            const float r = fabsf(mu[(int64_t)kk * d + dd] - c) + 4.0f * sqrtf(v > 0.0f ? v : 0.0f);
-            if (pi[kk] > 0.0f && isfinite(r)) reach = fmaxf(reach, r);
-        }
+    for (int kk = 0; kk < KMAX; ++kk) {
+        const float r = fabsf(mv[kk] - c) + 4.0f * sqrtf(vv[kk] > 0.0f ? vv[kk] : 0.0f);
+        reach = (pv[kk] > 0.0f && isfinite(r)) ? fmaxf(reach, r) : reach;
     }
     if (!(reach > 0.0f) || !isfinite(reach)) return 1.0f;
     int e = ilogbf(reach) - 2;
@@ -149,7 +155,8 @@ template <int DP, int KB>
 __global__ __launch_bounds__(DP) void k_diag_split_panel(int k_real, int d, const float* th_pi,
                                                          const float* th_mu, const float* th_var,
                                                          const float* shift, float* scale,
-                                                         uint16_t* panel16, float* fk) {
+                                                         const double* chunk_part, int nch,
+                                                         uint16_t* panel16, float* fk, float* ck) {
     __shared__ float red[DP];
     const int k = blockIdx.x, dd = threadIdx.x;
     const float sd = dd < d ? dim_scale<16 * KB>(k_real, d, dd, shift[dd], th_pi, th_mu, th_var) : 1.0f;
@@ -183,7 +190,21 @@ __global__ __launch_bounds__(DP) void k_diag_split_panel(int k_real, int d, cons
         panel16[o] = __builtin_bit_cast(uint16_t, hi);
         panel16[kLo + o] = __builtin_bit_cast(uint16_t, lo);
     }
-    if (dd == 0) fk[k] = ldexpf(1.0f, fe);
+    if (dd == 0) {
+        fk[k] = ldexpf(1.0f, fe);
+        // c_k = log2(e) (log pi_k - 1/2 (D log 2pi + sum log var + sum (mu-c)^2/var)),
+        // from the per-chunk sums of the prepare / finalize kernel
+        float c = -INFINITY;   // padding component: weight 0
+        if (k < k_real) {
+            double sl = 0.0, sm = 0.0;
+            for (int ch = 0; ch < nch; ++ch) {
+                sl += chunk_part[((int64_t)k * nch + ch) * 4 + 0];
+                sm += chunk_part[((int64_t)k * nch + ch) * 4 + 1];
+            }
+            c = (float)((log((double)th_pi[k]) - 0.5 * (d * kLog2Pi + sl + sm)) * kLog2e);
+        }
+        ck[k] = c;
+    }
 }
 
 // Reduce the per-workgroup partials, M-step, and prepare the next iteration.
@@ -330,7 +351,7 @@ gmm_status diag_prepare(const Plan& p, char* ws, const float* pi, const float* m
                            w.chunk_part, w.flags);                                               \
         hipLaunchKernelGGL((k_diag_split_panel<DP_, KB_>), dim3(16 * KB_), dim3(DP_), 0, s,      \
                            (int)p.k, (int)p.d, w.pi, w.mu, w.var, w.shift, w.scale,             \
-                           (uint16_t*)w.panel16, w.fk);                                         \
+                           w.chunk_part, diag_chunks(p), (uint16_t*)w.panel16, w.fk, w.ck);     \
         e = hipGetLastError();                                                                  \
     }
     GMM_DIAG_SHAPES(CASE)
@@ -365,7 +386,7 @@ gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* v
                            w.var, w.shift, w.scale, pi, mu, var, w.panel, w.flags, w.chunk_part); \
         hipLaunchKernelGGL((k_diag_split_panel<DP_, KB_>), dim3(16 * KB_), dim3(DP_), 0, s,        \
                            (int)p.k, (int)p.d, w.pi, w.mu, w.var, w.shift, w.scale,               \
-                           (uint16_t*)w.panel16, w.fk);                                           \
+                           w.chunk_part, diag_chunks(p), (uint16_t*)w.panel16, w.fk, w.ck);       \
         e = hipGetLastError();                                                                    \
     }
     GMM_DIAG_SHAPES(CASE)

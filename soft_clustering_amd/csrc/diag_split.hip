@@ -107,10 +107,6 @@ __device__ __forceinline__ f32x4 mfma_f16(const half8& a, const half8& b, f32x4 
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // Order this wave's LDS writes before its later LDS reads and the reads
 // before later writes (one wave: a compiler / memory fence at wavefront
 // scope, no s_barrier).
@@ -182,12 +178,27 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
 // hi = fp16(v) (round to nearest even, both lanes in one conversion) and
-// lo = fp16(v - hi) (one mixed-precision fma per value).
+// lo = fp16(v - hi): v - hi is exact in fp32 and rounded once, by one
+// mixed-precision fma per value that reads hi as fp16 and writes its fp16
+// result into one half of the packed register.
 __device__ __forceinline__ void split2(float v0, float v1, uint32_t& hi, uint32_t& lo) {
     const half2v h = __builtin_convertvector((float2v){v0, v1}, half2v);
-    const half2v l = {(_Float16)(v0 - (float)h[0]), (_Float16)(v1 - (float)h[1])};
     hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, l);
+    uint32_t l;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(l) : "v"(v0), "v"(hi));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(l) : "v"(v1), "v"(hi));
+    lo = l;
+}
+
+// y^2 from the split of y (h + l, packed pairs): h2 = fp16(h h), the
+// remainder h h - h2 (exact in fp16) plus 2 h l rounded once as the low
+// part; the dropped l^2 and that rounding are below 2^-21 of y^2.
+__device__ __forceinline__ void square2(uint32_t hi, uint32_t lo, uint32_t& hi2, uint32_t& lo2) {
+    const half2v h = __builtin_bit_cast(half2v, hi), l = __builtin_bit_cast(half2v, lo);
+    const half2v h2 = h * h;
+    const half2v ex = __builtin_elementwise_fma(h, h, -h2);
+    hi2 = __builtin_bit_cast(uint32_t, h2);
+    lo2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h + h, l, ex));
 }
 
 // Split a tile into H / L (columns [y^2 | y]); returns this lane's max |y|.
@@ -214,7 +225,7 @@ __device__ __forceinline__ float stage_tile(const uint4 (&raw)[SplitShape<DP, KB
             const float y1 = fmaf(xv[e + 1], sv[e + 1], -csv[e + 1]);
             mx = fmaxf(mx, fmaxf(fabsf(y0), fabsf(y1)));
             split2(y0, y1, h1[e / 2], l1[e / 2]);
-            split2(y0 * y0, y1 * y1, h2[e / 2], l2[e / 2]);
+            square2(h1[e / 2], l1[e / 2], h2[e / 2], l2[e / 2]);
         }
         // y^2 at columns [0, DP), y at [DP, 2 DP)
         const int o2 = uoff<S::kPitch>(r, col0 / 8) + (col0 & 7);
@@ -244,9 +255,8 @@ __device__ __forceinline__ float y_at(const XT* __restrict__ x, int64_t p, int d
 template <int DP, int KB, typename XT, bool VEC, bool EM>
 __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split(
     const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
-    const uint4* __restrict__ panel16, const float* __restrict__ fk,
-    const float* __restrict__ panel32, const float* __restrict__ th_pi,
-    const double* __restrict__ chunk_part, int nch, const float* __restrict__ shift,
+    const uint4* __restrict__ panel16, const float* __restrict__ fk, const float* __restrict__ ck,
+    const float* __restrict__ panel32, const float* __restrict__ shift,
     const float* __restrict__ scale, double* __restrict__ part, double* __restrict__ part_ll,
     float* __restrict__ out_lse, int* __restrict__ out_arg) {
     using S = SplitShape<DP, KB, XT>;
@@ -273,23 +283,12 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
             ph[ks][b] = __builtin_bit_cast(half8, panel16[(ks * KB + b) * 64 + lane]);
             pl[ks][b] = __builtin_bit_cast(half8, panel16[((KS + ks) * KB + b) * 64 + lane]);
         }
-    // c_k = log2(e) (log pi_k - 1/2 (D log 2pi + sum log var + sum (mu-c)^2/var)),
-    // from the prepared per-chunk sums; F_k the panel's power-of-two scale
+    // per-component log2 normaliser c_k and panel scale F_k (prepared)
     float cv[KB], fv[KB];
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
-        const int k = 16 * b + j;
-        fv[b] = fk[k];
-        if (k < k_real) {
-            double sl = 0.0, sm = 0.0;
-            for (int ch = 0; ch < nch; ++ch) {
-                sl += chunk_part[((int64_t)k * nch + ch) * 4 + 0];
-                sm += chunk_part[((int64_t)k * nch + ch) * 4 + 1];
-            }
-            cv[b] = (float)((log((double)th_pi[k]) - 0.5 * (d * kLog2Pi + sl + sm)) * kLog2e);
-        } else {
-            cv[b] = -INFINITY;   // padding component: weight 0
-        }
+        fv[b] = fk[16 * b + j];
+        cv[b] = ck[16 * b + j];
     }
     // y = x s - c s per column (s, c s; zero scale beyond D)
     for (int dd = tid; dd < DP; dd += THREADS) {
@@ -495,11 +494,7 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
 #pragma unroll
                     for (int q2 = 0; q2 < 4; ++q2) {
                         const int g2 = q2 >> 1, r = 2 * (q2 & 1);
-                        const _Float16 h0 = (_Float16)s[g2][b][r], h1 = (_Float16)s[g2][b][r + 1];
-                        const _Float16 l0 = (_Float16)(s[g2][b][r] - (float)h0);
-                        const _Float16 l1 = (_Float16)(s[g2][b][r + 1] - (float)h1);
-                        hw[q2] = pack2(h0, h1);
-                        lw[q2] = pack2(l0, l1);
+                        split2(s[g2][b][r], s[g2][b][r + 1], hw[q2], lw[q2]);
                     }
                     gh[b] = __builtin_bit_cast(half8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
                     gl[b] = __builtin_bit_cast(half8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
@@ -507,6 +502,7 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
                 // B operand (32 points x 16 columns) by transposed reads: lane
                 // (g, i) addresses row 4g + i / 4 (and 16 + ...), column 16 cb + 4 (i % 4)
                 const int rr = 4 * g + (j >> 2), cq = 4 * (j & 3);
+                half8 bh[NCB], bl[NCB];
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     const int c0 = 16 * cb + cq;
@@ -514,14 +510,24 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
                     const int ob = uoff<P>(rr + 16, c0 >> 3) + (c0 & 7);
                     const uint2 ha = tr16(H + oa), hb = tr16(H + ob);
                     const uint2 la = tr16(L + oa), lb = tr16(L + ob);
-                    const half8 bh = __builtin_bit_cast(half8, make_uint4(ha.x, ha.y, hb.x, hb.y));
-                    const half8 bl = __builtin_bit_cast(half8, make_uint4(la.x, la.y, lb.x, lb.y));
+                    bh[cb] = __builtin_bit_cast(half8, make_uint4(ha.x, ha.y, hb.x, hb.y));
+                    bl[cb] = __builtin_bit_cast(half8, make_uint4(la.x, la.y, lb.x, lb.y));
+                }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                     for (int b = 0; b < KB; ++b) {
-                        acc[b][cb] = mfma_f16(gh[b], bh, acc[b][cb]);
-                        acc[b][cb] = mfma_f16(gh[b], bl, acc[b][cb]);
-                        acc[b][cb] = mfma_f16(gl[b], bh, acc[b][cb]);
+                        acc[b][cb] = mfma_f16(gh[b], bh[cb], acc[b][cb]);
+                        acc[b][cb] = mfma_f16(gh[b], bl[cb], acc[b][cb]);
+                        acc[b][cb] = mfma_f16(gl[b], bh[cb], acc[b][cb]);
                     }
+                // reads run two column blocks ahead of the MFMAs, so the LDS
+                // latency is paid about once per tile, not once per block
+                __builtin_amdgcn_sched_group_barrier(0x100, NCB > 1 ? 8 : 4, 0);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 3 * KB, 0);
+                    if (cb + 2 < NCB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
                 }
             } else {
                 // fp32 fallback: [S2 | S1] += gamma^T [y^2 | y], y read back from
@@ -555,8 +561,8 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     }
 
     // ---- one fp64 partial per workgroup, waves summed in a fixed order
-    __syncthreads();   // every wave is done with its tiles before the LDS is reused
-    llred[tid] = (j == 0) ? ll2 : 0.0;
+    // LL: fixed-order tree over the workgroup (the lanes j == 0 hold the sums)
+    const double ll_wg = block_sum_f64((j == 0) ? ll2 : 0.0, llred);   // synchronises
     float* red = reinterpret_cast<float*>(smem);
     if constexpr (EM) {
         // acc[b][cb] lane (g, j): components 16 b + 4 g + r, column 16 cb + j of [y^2 | y]
@@ -592,11 +598,7 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
             part[(wg * k_real + k) * ncol + c] = v;
         }
     }
-    if (tid == 0) {
-        double sum = 0.0;
-        for (int i = 0; i < THREADS; ++i) sum += llred[i];
-        part_ll[wg] = sum * kLn2;
-    }
+    if (tid == 0) part_ll[wg] = ll_wg * kLn2;
 }
 
 template <int DP, int KB, typename XT, bool VEC, bool EM>
@@ -604,9 +606,8 @@ hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, flo
                     int* arg, hipStream_t s) {
     constexpr int W = diag_split_waves(DP, KB);
     hipLaunchKernelGGL((k_diag_split<DP, KB, XT, VEC, EM>), dim3(grid), dim3(64 * W), 0, s,
-                       (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.panel16, w.fk, w.panel,
-                       w.pi, w.chunk_part, diag_chunks(p), w.shift, w.scale, w.part, w.part_ll,
-                       lse, arg);
+                       (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.panel16, w.fk, w.ck, w.panel,
+                       w.shift, w.scale, w.part, w.part_ll, lse, arg);
     return hipGetLastError();
 }
 
