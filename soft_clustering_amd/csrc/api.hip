@@ -78,8 +78,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_mu = take(sizeof(float) * p->k * p->d);
         p->off_cov = take(sizeof(float) * p->k * p->d);
         p->off_shift = take(sizeof(float) * 2 * dp);
-        p->off_panel = take(align_up(sizeof(float) * (dp / 4) * 2 * kb * 64, A) +
-                            sizeof(uint16_t) * diag_panel16_halves(dp, kb) + sizeof(float) * 2 * 16 * kb);
+        p->off_panel = take(sizeof(float) * (dp / 4) * 2 * kb * 64);
         p->off_part = take(sizeof(double) * p->p_max * p->k * p->ncols);
         p->off_part_ll = take(sizeof(double) * p->p_max);
         p->off_stats = take(sizeof(double) * p->k * p->ncols);

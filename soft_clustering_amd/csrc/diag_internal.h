@@ -27,9 +27,11 @@ __host__ __device__ constexpr int diag_split_waves(int dp, int kb) {
 // (65504) with margin; a tile with any larger |y| takes the fp32 route.
 constexpr float kSplitLim = 224.0f;
 
-// Halves of the split panel (hi, then lo): 2 x (2 DP / 32) k-steps x KB
-// component blocks x 64 lanes x 8 halves.
-inline size_t diag_panel16_halves(int dp, int kb) { return (size_t)2 * (dp / 16) * kb * 64 * 8; }
+
+// Threads of the reduction / M-step kernel (one workgroup per component and
+// 32-dimension chunk): sixteen waves, so that each wave's strided walk over
+// the partial slots is short.
+constexpr int kDiagReduceThreads = 1024;
 
 // Dimensions per chunk of the M-step / normaliser sums.
 constexpr int kDiagChunkDims = 32;
@@ -38,11 +40,10 @@ inline int diag_chunks(const Plan& p) { return (int)((p.d + kDiagChunkDims - 1) 
 struct DiagWs {
     float *pi, *mu, *var, *panel;
     float *shift, *scale;   // [DP] centre c and power-of-two scale s: y = (x - c) s
-    uint4* panel16;         // split fp16 panel (hi, lo) of [a ; b] in y units / F_k
-    float* fk;              // [16 KB] per-component panel scale F_k (power of two)
-    float* ck;              // [16 KB] per-component log2 normaliser c_k (-inf: padding)
+                            // (s: written by the fused kernel for its reduction)
     double *part, *part_ll, *stats, *ll;
     int *flags, *retries, *nonfinite_ll;
+    int* done;              // workgroups of the running fused kernel that have finished
     double* chunk_part;   // [K][chunks][4]: sum log var, sum (mu-c)^2/var, #bad, #non-finite
 };
 
@@ -54,9 +55,6 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
     w.shift = (float*)(ws + p.off_shift);
     w.scale = w.shift + p.dp;
     w.panel = (float*)(ws + p.off_panel);
-    w.panel16 = (uint4*)(ws + p.off_panel + align_up(sizeof(float) * (p.dp / 4) * 2 * p.kb * 64, 256));
-    w.fk = (float*)((char*)w.panel16 + sizeof(uint16_t) * diag_panel16_halves(p.dp, p.kb));
-    w.ck = w.fk + 16 * p.kb;
     w.part = (double*)(ws + p.off_part);
     w.part_ll = (double*)(ws + p.off_part_ll);
     w.stats = (double*)(ws + p.off_stats);
@@ -64,6 +62,7 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
     w.flags = (int*)(ws + p.off_diag);
     w.retries = w.flags + p.k;
     w.nonfinite_ll = w.flags + 2 * p.k;
+    w.done = w.flags + 2 * p.k + 1;
     w.chunk_part = (double*)(ws + p.off_chunk);
     return w;
 }
@@ -71,10 +70,11 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
 // Number of workgroups (= partial slots) of the fused kernel for this plan.
 int diag_grid(const Plan& p);
 
-// Launch the fused split-fp16 kernel (diag_split.hip): EM = statistics + LL
+// Launch the fused split-fp16 kernel (diag_split.hip): EM = statistics
 // partials (moments of y = (x - c) s, undone by the reduction); otherwise
-// E-step only with optional per-point outputs.
+// E-step only with optional per-point outputs.  Either way the kernel
+// leaves the LL in the workspace and in ll_out (nullable).
 hipError_t diag_launch_split(const Plan& p, const DiagWs& w, const void* x, bool em, int grid,
-                             float* lse, int* arg, hipStream_t s);
+                             double* ll_out, float* lse, int* arg, hipStream_t s);
 
 }  // namespace gmm

@@ -46,36 +46,6 @@ __device__ __forceinline__ void put_panel(float* panel, int k, int dd, float a, 
 // gmm_prepare: copy theta into the workspace, choose the centre, build the
 // panel and the per-chunk normaliser sums.  Grid: 16*KB workgroups (one per
 // padded component), 256 threads.
-// Power-of-two scale s of dimension dd for the split-fp16 operands
-// y = (x - c) s: the widest reach of the components that hold weight,
-// max_k |mu_k - c| + 4 sigma_k over pi_k > 0, maps into [4, 8), so data
-// within the model's spread has |y| < 8 and the fp16 range (|y| <
-// kSplitLim) leaves a factor of about 28 for points beyond it.  1 when the
-// reach is zero or not finite.
-template <int KMAX>
-__device__ __forceinline__ float dim_scale(int k_real, int d, int dd, float c, const float* pi,
-                                           const float* mu, const float* var) {
-    // all loads first (clamped, always in bounds) so that they issue together
-    float vv[KMAX], mv[KMAX], pv[KMAX];
-#pragma unroll
-    for (int kk = 0; kk < KMAX; ++kk) {
-        const int kc = kk < k_real ? kk : k_real - 1;
-        vv[kk] = var[(int64_t)kc * d + dd];
-        mv[kk] = mu[(int64_t)kc * d + dd];
-        pv[kk] = kk < k_real ? pi[kc] : 0.0f;
-    }
-    float reach = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < KMAX; ++kk) {
-        const float r = fabsf(mv[kk] - c) + 4.0f * sqrtf(vv[kk] > 0.0f ? vv[kk] : 0.0f);
-        reach = (pv[kk] > 0.0f && isfinite(r)) ? fmaxf(reach, r) : reach;
-    }
-    if (!(reach > 0.0f) || !isfinite(reach)) return 1.0f;
-    int e = ilogbf(reach) - 2;
-    e = e < -60 ? -60 : (e > 60 ? 60 : e);
-    return ldexpf(1.0f, -e);
-}
-
 template <int DP, int KB>
 __global__ __launch_bounds__(256) void k_diag_prepare(int k_real, int d, const float* pi,
                                                       const float* mu, const float* var,
@@ -135,75 +105,10 @@ __global__ __launch_bounds__(256) void k_diag_prepare(int k_real, int d, const f
         th_pi[k] = pk;
         flags[k] = (!(pk >= 0.0f) || !isfinite(pk)) ? 1 : 0;   // bit 0: bad weight
         flags[k_real + k] = 0;                                 // ridge retries (full only)
-        if (k == 0) flags[2 * k_real] = 0;                     // non-finite LL
-    }
-}
-
-// Split fp16 panel of the split kernel from the prepared fp32 parameters
-// (after gmm_prepare and after every finalize): the per-dimension scale s
-// (every workgroup derives the same one; workgroup 0 stores it for the
-// reduction of the coming step), and the entries
-// a_kd = -1/2 log2(e) / (var s^2) and b_kd = log2(e) (mu - c) / (var s)
-// (y units), divided by the component's power of two F_k that puts its
-// largest entry in [2^14, 2^15), each stored as hi = fp16(v), lo = fp16(v - hi)
-// in the B-operand layout of v_mfma_f32_16x16x32_f16: contraction index kk
-// (a at kk = dd, b at kk = DP + dd) of component k sits in k-step kk / 32,
-// block k / 16, lane 16 ((kk % 32) / 8) + k % 16, half kk % 8.  Padding
-// components and dimensions get zeros (F = 1).  Grid: 16 KB workgroups (one
-// per padded component), DP threads.
-template <int DP, int KB>
-__global__ __launch_bounds__(DP) void k_diag_split_panel(int k_real, int d, const float* th_pi,
-                                                         const float* th_mu, const float* th_var,
-                                                         const float* shift, float* scale,
-                                                         const double* chunk_part, int nch,
-                                                         uint16_t* panel16, float* fk, float* ck) {
-    __shared__ float red[DP];
-    const int k = blockIdx.x, dd = threadIdx.x;
-    const float sd = dd < d ? dim_scale<16 * KB>(k_real, d, dd, shift[dd], th_pi, th_mu, th_var) : 1.0f;
-    if (k == 0) scale[dd] = sd;
-    double a = 0.0, b = 0.0;
-    if (k < k_real && dd < d) {
-        const int64_t i = (int64_t)k * d + dd;
-        const double s = sd;
-        const double pr = 1.0 / (double)th_var[i];
-        a = -0.5 * pr * kLog2e / (s * s);
-        b = ((double)th_mu[i] - (double)shift[dd]) * pr * kLog2e / s;
-    }
-    const float m = (float)fmax(fabs(a), fabs(b));
-    red[dd] = isfinite(m) ? m : 0.0f;
-    __syncthreads();
-    for (int st = DP / 2; st > 0; st >>= 1) {
-        if (dd < st) red[dd] = fmaxf(red[dd], red[dd + st]);
-        __syncthreads();
-    }
-    const float mx = red[0];
-    const int fe = mx > 0.0f ? ilogbf(mx) - 14 : 0;
-    const double inv = ldexp(1.0, -fe);
-    constexpr size_t kLo = (size_t)(DP / 16) * KB * 64 * 8;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int kk = h * DP + dd;
-        const float v = (float)((h == 0 ? a : b) * inv);
-        const _Float16 hi = (_Float16)v;
-        const _Float16 lo = (_Float16)(v - (float)hi);
-        const size_t o = ((size_t)((kk / 32) * KB + k / 16) * 64 + 16 * ((kk % 32) / 8) + k % 16) * 8 + kk % 8;
-        panel16[o] = __builtin_bit_cast(uint16_t, hi);
-        panel16[kLo + o] = __builtin_bit_cast(uint16_t, lo);
-    }
-    if (dd == 0) {
-        fk[k] = ldexpf(1.0f, fe);
-        // c_k = log2(e) (log pi_k - 1/2 (D log 2pi + sum log var + sum (mu-c)^2/var)),
-        // from the per-chunk sums of the prepare / finalize kernel
-        float c = -INFINITY;   // padding component: weight 0
-        if (k < k_real) {
-            double sl = 0.0, sm = 0.0;
-            for (int ch = 0; ch < nch; ++ch) {
-                sl += chunk_part[((int64_t)k * nch + ch) * 4 + 0];
-                sm += chunk_part[((int64_t)k * nch + ch) * 4 + 1];
-            }
-            c = (float)((log((double)th_pi[k]) - 0.5 * (d * kLog2Pi + sl + sm)) * kLog2e);
+        if (k == 0) {
+            flags[2 * k_real] = 0;       // non-finite LL
+            flags[2 * k_real + 1] = 0;   // finished-workgroup count of the fused kernel
         }
-        ck[k] = c;
     }
 }
 
@@ -216,40 +121,49 @@ __global__ __launch_bounds__(DP) void k_diag_split_panel(int k_real, int d, cons
 // bad / non-finite values) go to chunk_part[k][ch]; the next fused kernel
 // forms c_k from them.
 template <int DP, int KB>
-__global__ __launch_bounds__(256) void k_diag_reduce_finalize(
+__global__ __launch_bounds__(kDiagReduceThreads) void k_diag_reduce_finalize(
     const double* __restrict__ part, int P, int64_t n, int d, int k_real, float var_floor,
     double* __restrict__ stats, float* __restrict__ th_pi, float* __restrict__ th_mu,
     float* __restrict__ th_var, const float* __restrict__ shift, const float* __restrict__ scale,
     float* __restrict__ out_pi,
     float* __restrict__ out_mu, float* __restrict__ out_var, float* __restrict__ panel,
     int* __restrict__ flags, double* __restrict__ chunk_part) {
-    __shared__ double colw[4][64];
-    __shared__ double s0w[256];
+    constexpr int RW = kDiagReduceThreads / 64;   // waves
+    __shared__ double colw[RW][64];
+    __shared__ double s0w[kDiagReduceThreads];
     __shared__ double cs[4][kDiagChunkDims];
     const int ch = blockIdx.x, k = blockIdx.y, nch = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ncol = 1 + 2 * d;
     const int col = 1 + 64 * ch + lane;
 
-    // column sums over the partial slots (4 interleaved accumulators for MLP)
+    // column sums over the partial slots: wave w takes slots w, w + RW, ...
+    // (4 interleaved accumulators, so that several loads are in flight)
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     if (col < ncol) {
         const double* src = part + (int64_t)k * ncol + col;
         const int64_t stride = (int64_t)k_real * ncol;
         int p = w;
-        for (; p + 12 < P; p += 16) {
+        for (; p + 3 * RW < P; p += 4 * RW) {
             a0 += src[(int64_t)p * stride];
-            a1 += src[(int64_t)(p + 4) * stride];
-            a2 += src[(int64_t)(p + 8) * stride];
-            a3 += src[(int64_t)(p + 12) * stride];
+            a1 += src[(int64_t)(p + RW) * stride];
+            a2 += src[(int64_t)(p + 2 * RW) * stride];
+            a3 += src[(int64_t)(p + 3 * RW) * stride];
         }
-        for (; p < P; p += 4) a0 += src[(int64_t)p * stride];
+        for (; p < P; p += RW) a0 += src[(int64_t)p * stride];
     }
     colw[w][lane] = (a0 + a1) + (a2 + a3);
     // s0: every workgroup of component k sums column 0 the same way
     double z = 0.0;
-    for (int p = tid; p < P; p += 256) z += part[((int64_t)p * k_real + k) * ncol];
+    for (int p = tid; p < P; p += kDiagReduceThreads) z += part[((int64_t)p * k_real + k) * ncol];
     const double s0 = block_sum_f64(z, s0w);   // contains __syncthreads
+    // the waves' column sums, in a fixed order
+    auto colsum = [&](int c2) {
+        double v = 0.0;
+#pragma unroll
+        for (int ww = 0; ww < RW; ++ww) v += colw[ww][c2];
+        return v;
+    };
     const bool empty = s0 < kEmptyNk;
 
     double slogv = 0.0, sm2p = 0.0, bad = 0.0, nonfin = 0.0;
@@ -258,9 +172,8 @@ __global__ __launch_bounds__(256) void k_diag_reduce_finalize(
         if (dd < d) {
             // moments of y = (x - c) s back to x - c (s is a power of two: exact)
             const double is = 1.0 / (double)scale[dd];
-            const double t1 = ((colw[0][2 * tid] + colw[1][2 * tid]) + (colw[2][2 * tid] + colw[3][2 * tid])) * is;
-            const double t2 = ((colw[0][2 * tid + 1] + colw[1][2 * tid + 1]) +
-                               (colw[2][2 * tid + 1] + colw[3][2 * tid + 1])) * is * is;
+            const double t1 = colsum(2 * tid) * is;
+            const double t2 = colsum(2 * tid + 1) * is * is;
             const double c = shift[dd];
             const int64_t i = (int64_t)k * d + dd;
             // raw moments: sum g x = t1 + c s0, sum g x^2 = t2 + 2 c t1 + c^2 s0
@@ -349,9 +262,6 @@ gmm_status diag_prepare(const Plan& p, char* ws, const float* pi, const float* m
         hipLaunchKernelGGL((k_diag_prepare<DP_, KB_>), dim3(16 * KB_), dim3(256), 0, s, (int)p.k, \
                            (int)p.d, pi, mu, var, w.pi, w.mu, w.var, w.shift, w.panel,           \
                            w.chunk_part, w.flags);                                               \
-        hipLaunchKernelGGL((k_diag_split_panel<DP_, KB_>), dim3(16 * KB_), dim3(DP_), 0, s,      \
-                           (int)p.k, (int)p.d, w.pi, w.mu, w.var, w.shift, w.scale,             \
-                           w.chunk_part, diag_chunks(p), (uint16_t*)w.panel16, w.fk, w.ck);     \
         e = hipGetLastError();                                                                  \
     }
     GMM_DIAG_SHAPES(CASE)
@@ -368,9 +278,8 @@ static gmm_status sum_ll(const Plan& p, const DiagWs& w, int P, double* ll_out, 
 gmm_status diag_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
     DiagWs w = diag_ws(p, ws);
     const int P = diag_grid(p);
-    hipError_t e = diag_launch_split(p, w, x, true, P, nullptr, nullptr, s);
-    if (e != hipSuccess) return GMM_E_HIP;
-    return sum_ll(p, w, P, ll_out, s);
+    hipError_t e = diag_launch_split(p, w, x, true, P, ll_out, nullptr, nullptr, s);
+    return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
 gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var,
@@ -381,12 +290,9 @@ gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* v
     hipError_t e = hipErrorInvalidValue;
 #define CASE(DP_, KB_)                                                                            \
     if (p.dp == DP_ && p.kb == KB_) {                                                             \
-        hipLaunchKernelGGL((k_diag_reduce_finalize<DP_, KB_>), dim3(nch, p.k), dim3(256), 0, s,    \
+        hipLaunchKernelGGL((k_diag_reduce_finalize<DP_, KB_>), dim3(nch, p.k), dim3(kDiagReduceThreads), 0, s, \
                            w.part, P, p.n, (int)p.d, (int)p.k, p.var_floor, w.stats, w.pi, w.mu,  \
                            w.var, w.shift, w.scale, pi, mu, var, w.panel, w.flags, w.chunk_part); \
-        hipLaunchKernelGGL((k_diag_split_panel<DP_, KB_>), dim3(16 * KB_), dim3(DP_), 0, s,        \
-                           (int)p.k, (int)p.d, w.pi, w.mu, w.var, w.shift, w.scale,               \
-                           w.chunk_part, diag_chunks(p), (uint16_t*)w.panel16, w.fk, w.ck);       \
         e = hipGetLastError();                                                                    \
     }
     GMM_DIAG_SHAPES(CASE)
@@ -399,9 +305,8 @@ gmm_status diag_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
     DiagWs w = diag_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int P = diag_grid(p);
-    hipError_t e = diag_launch_split(p, w, x, false, P, lse, argmax, s);
-    if (e != hipSuccess) return GMM_E_HIP;
-    return sum_ll(p, w, P, ll_out, s);
+    hipError_t e = diag_launch_split(p, w, x, false, P, ll_out, lse, argmax, s);
+    return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
 }  // namespace gmm

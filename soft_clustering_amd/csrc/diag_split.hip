@@ -255,10 +255,12 @@ __device__ __forceinline__ float y_at(const XT* __restrict__ x, int64_t p, int d
 template <int DP, int KB, typename XT, bool VEC, bool EM>
 __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split(
     const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
-    const uint4* __restrict__ panel16, const float* __restrict__ fk, const float* __restrict__ ck,
+    const float* __restrict__ th_pi, const float* __restrict__ th_mu,
+    const float* __restrict__ th_var, const double* __restrict__ chunk_part, int nch,
     const float* __restrict__ panel32, const float* __restrict__ shift,
-    const float* __restrict__ scale, double* __restrict__ part, double* __restrict__ part_ll,
-    float* __restrict__ out_lse, int* __restrict__ out_arg) {
+    float* __restrict__ scale, double* __restrict__ part, double* __restrict__ part_ll,
+    unsigned* __restrict__ done, double* __restrict__ ll_ws, double* __restrict__ ll_out,
+    int* __restrict__ nonfinite_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
     using S = SplitShape<DP, KB, XT>;
     constexpr int WAVES = S::kWaves, THREADS = S::kThreads;
     constexpr int KS = S::kKS, NCB = S::kNCB, EV = S::kEV, P = S::kPitch;
@@ -274,28 +276,15 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     const int lane = tid & 63, g = lane >> 4, j = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
 
-    // fp16 split panel (B operand: lane holds component 16b + j, K 8g..8g+7)
-    half8 ph[KS][KB], pl[KS][KB];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            ph[ks][b] = __builtin_bit_cast(half8, panel16[(ks * KB + b) * 64 + lane]);
-            pl[ks][b] = __builtin_bit_cast(half8, panel16[((KS + ks) * KB + b) * 64 + lane]);
-        }
-    // per-component log2 normaliser c_k and panel scale F_k (prepared)
-    float cv[KB], fv[KB];
-#pragma unroll
-    for (int b = 0; b < KB; ++b) {
-        fv[b] = fk[16 * b + j];
-        cv[b] = ck[16 * b + j];
-    }
-    // y = x s - c s per column (s, c s; zero scale beyond D)
-    for (int dd = tid; dd < DP; dd += THREADS) {
-        const float s = dd < d ? scale[dd] : 0.0f;
-        sc_l[dd] = s;
-        cs_l[dd] = dd < d ? shift[dd] * s : 0.0f;
-    }
+    // this wave's run of tiles (wave-uniform; the 64-bit division expands to
+    // vector code, so its results are moved back to scalar registers)
+    const int64_t tiles = (n + kST - 1) / kST;
+    const int64_t nw = (int64_t)gridDim.x * WAVES, gw = (int64_t)blockIdx.x * WAVES + w;
+    const int64_t tb = tiles / nw, tr = tiles % nw;
+    const int64_t t0 = uniform64(gw * tb + (gw < tr ? gw : tr));
+    const int nt = __builtin_amdgcn_readfirstlane((int)(tb + (gw < tr ? 1 : 0)));
+    const int64_t tlast = t0 + nt - 1;
+
     const int col0 = (lane % S::kVPR) * EV;
     const bool colok = col0 < d;
     // offsets of this lane's vector slots from a tile's first row (bytes on
@@ -309,24 +298,137 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
         loff[i] = VEC ? (uint32_t)(((int64_t)r * ldx + (colok ? col0 : 0)) * sizeof(XT))
                       : (uint32_t)((int64_t)r * ldx);
     }
+    // First row of the 32 that tile t reads: the last, ragged tile is moved
+    // back to end at row N (rows before its own start were counted by the
+    // previous tile and are masked); problems under 32 points start at 0.
+    auto tile_row = [&](int64_t t) {
+        const int64_t p = t * kST;
+        const int64_t pmax = n > kST ? n - kST : 0;
+        return p < pmax ? p : pmax;
+    };
+    // the first tile's loads fly while the panel is built
+    TileRegs<XT, DP, KB, VEC> ld;
+    if (nt > 0) ld.load(x + tile_row(t0) * ldx, loff, d, lane);
+
+    // ---- this step's split fp16 panel, built by every workgroup from the
+    // prepared fp32 parameters (same inputs and code in all of them)
+    constexpr int NC = 16 * KB;                     // padded components
+    // threads per component: the largest power of two with NC * TPC <= THREADS
+    constexpr int TPC = THREADS / NC >= 32 ? 32 : THREADS / NC >= 16 ? 16 : THREADS / NC >= 8 ? 8 : 4;
+    constexpr int VPT = 2 * DP / TPC;               // panel values per thread
+    float* const pab = reinterpret_cast<float*>(smem);   // [NC][2 DP]: a | b, y units / F_k
+    float* const tmu = pab + NC * 2 * DP;                // [NC][DP] staged means
+    float* const tvar = tmu + NC * DP;                   // [NC][DP] staged variances
+    __shared__ float pf[NC], pc[NC], tpi[NC];
+    // (0) the parameters into LDS in one round trip (padding: mu 0, var 1,
+    // pi 0), and each component's log2 normaliser
+    // c_k = log2(e) (log pi_k - 1/2 (D log 2pi + sum log var + sum (mu-c)^2/var))
+    // from the per-chunk sums of the prepare / finalize kernel
+    for (int e2 = tid; e2 < NC * DP; e2 += THREADS) {
+        const int kb = e2 / DP, dd = e2 % DP;
+        const bool ok = kb < k_real && dd < d;
+        tmu[e2] = ok ? th_mu[(int64_t)kb * d + dd] : 0.0f;
+        tvar[e2] = ok ? th_var[(int64_t)kb * d + dd] : 1.0f;
+    }
+    for (int kb = tid; kb < NC; kb += THREADS) {
+        float cval = -INFINITY;   // padding component: weight 0
+        float pk = 0.0f;
+        if (kb < k_real) {
+            pk = th_pi[kb];
+            double sl = 0.0, sm = 0.0;
+            for (int ch = 0; ch < nch; ++ch) {
+                sl += chunk_part[((int64_t)kb * nch + ch) * 4 + 0];
+                sm += chunk_part[((int64_t)kb * nch + ch) * 4 + 1];
+            }
+            cval = (float)((log((double)pk) - 0.5 * (d * kLog2Pi + sl + sm)) * kLog2e);
+        }
+        tpi[kb] = pk;
+        pc[kb] = cval;
+    }
+    __syncthreads();
+    // (1) per-dimension scale s (a power of two): the widest reach of the
+    // components that hold weight, max_k |mu_k - c| + 4 sigma_k over
+    // pi_k > 0, maps into [4, 8), so data within the model's spread has
+    // |y| < 8 and the fp16 range (|y| < kSplitLim) leaves a factor of about
+    // 28 for points beyond it; 1 when the reach is zero or not finite
+    for (int dd = tid; dd < DP; dd += THREADS) {
+        const float c = dd < d ? shift[dd] : 0.0f;
+        float reach = 0.0f;
+        for (int kb = 0; kb < k_real; ++kb) {
+            const float v = tvar[kb * DP + dd];
+            const float r = fabsf(tmu[kb * DP + dd] - c) + 4.0f * sqrtf(v > 0.0f ? v : 0.0f);
+            if (tpi[kb] > 0.0f && isfinite(r)) reach = fmaxf(reach, r);
+        }
+        float sd = 1.0f;
+        if (reach > 0.0f && isfinite(reach)) {
+            int e = ilogbf(reach) - 2;
+            e = e < -60 ? -60 : (e > 60 ? 60 : e);
+            sd = ldexpf(1.0f, -e);
+        }
+        if (dd >= d) sd = 0.0f;
+        sc_l[dd] = sd;
+        cs_l[dd] = c * sd;
+        if (blockIdx.x == 0) scale[dd] = dd < d ? sd : 1.0f;   // read by the reduction
+    }
+    __syncthreads();
+    // (2) entries a = -1/2 log2(e) / (var s^2), b = log2(e) (mu - c) / (var s)
+    // (fp32, a few roundings; s is a power of two, so dividing by it is
+    // exact) and the component's power-of-two scale F_k (largest entry in
+    // [2^14, 2^15))
+    for (int kb = tid / TPC; kb < NC; kb += THREADS / TPC) {
+        const int t = tid % TPC;
+        float v[VPT];
+        float mxa = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int kk = t + TPC * i;
+            const int dd = kk < DP ? kk : kk - DP;
+            float val = 0.0f;
+            if (kb < k_real && dd < d) {
+                const float is = 1.0f / sc_l[dd];
+                const float pr = (float)kLog2e / tvar[kb * DP + dd];
+                val = kk < DP ? -0.5f * pr * is * is : (tmu[kb * DP + dd] - shift[dd]) * pr * is;
+            }
+            v[i] = val;
+            if (isfinite(v[i])) mxa = fmaxf(mxa, fabsf(v[i]));
+        }
+#pragma unroll
+        for (int o = TPC / 2; o > 0; o >>= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, o));
+        const int fe = mxa > 0.0f ? ilogbf(mxa) - 14 : 0;
+        const float inv = ldexpf(1.0f, -fe);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) pab[kb * (2 * DP) + t + TPC * i] = v[i] * inv;
+        if (t == 0) pf[kb] = ldexpf(1.0f, fe);
+    }
+    __syncthreads();
+    // (3) this lane's B operands: component 16 b + j, K index 32 ks + 8 g + e
+    half8 ph[KS][KB], pl[KS][KB];
+    float cv[KB], fv[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+        const float* row = pab + (16 * b + j) * (2 * DP);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float4 v0 = *reinterpret_cast<const float4*>(row + 32 * ks + 8 * g);
+            const float4 v1 = *reinterpret_cast<const float4*>(row + 32 * ks + 8 * g + 4);
+            uint32_t hw[4], lw[4];
+            split2(v0.x, v0.y, hw[0], lw[0]);
+            split2(v0.z, v0.w, hw[1], lw[1]);
+            split2(v1.x, v1.y, hw[2], lw[2]);
+            split2(v1.z, v1.w, hw[3], lw[3]);
+            ph[ks][b] = __builtin_bit_cast(half8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            pl[ks][b] = __builtin_bit_cast(half8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+        fv[b] = pf[16 * b + j];
+        cv[b] = pc[16 * b + j];
+    }
     float sv[EV], csv[EV];
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
-        const int cc = col0 + e;
-        const float s = cc < d ? scale[cc] : 0.0f;
-        sv[e] = s;
-        csv[e] = cc < d ? shift[cc] * s : 0.0f;
+        sv[e] = sc_l[col0 + e];
+        csv[e] = cs_l[col0 + e];
     }
-    __syncthreads();
-
-    // this wave's run of tiles (wave-uniform; the 64-bit division expands to
-    // vector code, so its results are moved back to scalar registers)
-    const int64_t tiles = (n + kST - 1) / kST;
-    const int64_t nw = (int64_t)gridDim.x * WAVES, gw = (int64_t)blockIdx.x * WAVES + w;
-    const int64_t tb = tiles / nw, tr = tiles % nw;
-    const int64_t t0 = uniform64(gw * tb + (gw < tr ? gw : tr));
-    const int nt = __builtin_amdgcn_readfirstlane((int)(tb + (gw < tr ? 1 : 0)));
-    const int64_t tlast = t0 + nt - 1;
+    __syncthreads();   // the panel area is reused by the tiles
 
     f32x4 acc[EM ? KB : 1][EM ? NCB : 1];
     float s0acc[KB];
@@ -342,15 +444,6 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
 
     uint16_t* H = reinterpret_cast<uint16_t*>(smem) + w * 2 * S::kTile;
     uint16_t* L = H + S::kTile;
-
-    // First row of the 32 that tile t reads: the last, ragged tile is moved
-    // back to end at row N (rows before its own start were counted by the
-    // previous tile and are masked); problems under 32 points start at 0.
-    auto tile_row = [&](int64_t t) {
-        const int64_t p = t * kST;
-        const int64_t pmax = n > kST ? n - kST : 0;
-        return p < pmax ? p : pmax;
-    };
 
     // One tile: split-stage `ld`, issue the loads of tile q + 1 into it (they
     // land while this tile is computed), scores, softmax, statistics.
@@ -554,11 +647,7 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
         wave_lds_fence();   // this tile's LDS reads before the next staging writes
     };
 
-    if (nt > 0) {
-        TileRegs<XT, DP, KB, VEC> ld;
-        ld.load(x + tile_row(t0) * ldx, loff, d, lane);
-        for (int q = 0; q < nt; ++q) step(q, ld);
-    }
+    for (int q = 0; q < nt; ++q) step(q, ld);
 
     // ---- one fp64 partial per workgroup, waves summed in a fixed order
     // LL: fixed-order tree over the workgroup (the lanes j == 0 hold the sums)
@@ -598,32 +687,56 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
             part[(wg * k_real + k) * ncol + c] = v;
         }
     }
-    if (tid == 0) part_ll[wg] = ll_wg * kLn2;
+    // LL of the whole pass: the last workgroup to finish sums the
+    // per-workgroup values in a fixed order (release before the count,
+    // acquire after it, both at device scope; the count returns to zero for
+    // the next launch)
+    __shared__ int last_wg;
+    if (tid == 0) {
+        part_ll[wg] = ll_wg * kLn2;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const unsigned prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_wg = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (last_wg) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        double v = 0.0;
+        for (int p = tid; p < (int)gridDim.x; p += THREADS) v += part_ll[p];
+        v = block_sum_f64(v, llred);
+        if (tid == 0) {
+            *ll_ws = v;
+            if (ll_out != nullptr) *ll_out = v;
+            *nonfinite_ll = isfinite(v) ? 0 : 1;
+            *done = 0u;
+        }
+    }
 }
 
 template <int DP, int KB, typename XT, bool VEC, bool EM>
-hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, float* lse,
-                    int* arg, hipStream_t s) {
+hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, double* ll_out,
+                    float* lse, int* arg, hipStream_t s) {
     constexpr int W = diag_split_waves(DP, KB);
     hipLaunchKernelGGL((k_diag_split<DP, KB, XT, VEC, EM>), dim3(grid), dim3(64 * W), 0, s,
-                       (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.panel16, w.fk, w.ck, w.panel,
-                       w.shift, w.scale, w.part, w.part_ll, lse, arg);
+                       (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.pi, w.mu, w.var,
+                       w.chunk_part, diag_chunks(p), w.panel, w.shift, w.scale, w.part, w.part_ll,
+                       (unsigned*)w.done, w.ll, ll_out, w.nonfinite_ll, lse, arg);
     return hipGetLastError();
 }
 
 template <int DP, int KB, bool EM>
 hipError_t launch_x(const Plan& p, const DiagWs& w, const void* x, bool vec, int grid,
-                    float* lse, int* arg, hipStream_t s) {
+                    double* ll_out, float* lse, int* arg, hipStream_t s) {
     switch (p.xdt) {
         case GMM_F32:
-            return vec ? launch_t<DP, KB, float, true, EM>(p, w, x, grid, lse, arg, s)
-                       : launch_t<DP, KB, float, false, EM>(p, w, x, grid, lse, arg, s);
+            return vec ? launch_t<DP, KB, float, true, EM>(p, w, x, grid, ll_out, lse, arg, s)
+                       : launch_t<DP, KB, float, false, EM>(p, w, x, grid, ll_out, lse, arg, s);
         case GMM_BF16:
-            return vec ? launch_t<DP, KB, bf16_t, true, EM>(p, w, x, grid, lse, arg, s)
-                       : launch_t<DP, KB, bf16_t, false, EM>(p, w, x, grid, lse, arg, s);
+            return vec ? launch_t<DP, KB, bf16_t, true, EM>(p, w, x, grid, ll_out, lse, arg, s)
+                       : launch_t<DP, KB, bf16_t, false, EM>(p, w, x, grid, ll_out, lse, arg, s);
         default:
-            return vec ? launch_t<DP, KB, _Float16, true, EM>(p, w, x, grid, lse, arg, s)
-                       : launch_t<DP, KB, _Float16, false, EM>(p, w, x, grid, lse, arg, s);
+            return vec ? launch_t<DP, KB, _Float16, true, EM>(p, w, x, grid, ll_out, lse, arg, s)
+                       : launch_t<DP, KB, _Float16, false, EM>(p, w, x, grid, ll_out, lse, arg, s);
     }
 }
 
@@ -636,12 +749,12 @@ bool x_vec_ok(const Plan& p, const void* x) {
 }  // namespace
 
 hipError_t diag_launch_split(const Plan& p, const DiagWs& w, const void* x, bool em, int grid,
-                             float* lse, int* arg, hipStream_t s) {
+                             double* ll_out, float* lse, int* arg, hipStream_t s) {
     const bool vec = x_vec_ok(p, x);
 #define CASE(DP_, KB_)                                                                          \
     if (p.dp == DP_ && p.kb == KB_)                                                             \
-        return em ? launch_x<DP_, KB_, true>(p, w, x, vec, grid, lse, arg, s)                  \
-                  : launch_x<DP_, KB_, false>(p, w, x, vec, grid, lse, arg, s);
+        return em ? launch_x<DP_, KB_, true>(p, w, x, vec, grid, ll_out, lse, arg, s)          \
+                  : launch_x<DP_, KB_, false>(p, w, x, vec, grid, ll_out, lse, arg, s);
     GMM_DIAG_SHAPES(CASE)
 #undef CASE
     return hipErrorInvalidValue;
