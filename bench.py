@@ -52,17 +52,17 @@ METRIC = "GMM EM iterations/sec & points·components/s at N,D,K; % of HBM or MFM
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="f234b5304709cc43", fetch_kib=125146.0, write_kib=4136.1,
+        sources="e51900e7e1386a6b", fetch_kib=125183.9, write_kib=4144.3,
         copy_bytes=256e6, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="332fc60c6829d587", fetch_kib=1251255.6, write_kib=66790.1,
-        copy_bytes=2.56e9, copy_fetch_kib=1250035.5625, copy_write_kib=2500000.0),
+        sources="0a4813fb83900d74", fetch_kib=1251255.1, write_kib=66738.9,
+        copy_bytes=2.56e9, copy_fetch_kib=1250035.6875, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="332fc60c6829d587", fetch_kib=113095256.6, write_kib=4044192.8,
-        copy_bytes=51.2e9, copy_fetch_kib=25000264.6875, copy_write_kib=50000000.0),
+        sources="0a4813fb83900d74", fetch_kib=114549383.6, write_kib=4044132.1,
+        copy_bytes=51.2e9, copy_fetch_kib=25000258.5625, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="87339fa36c2a0976", fetch_kib=63185.8, write_kib=68707.8,
-        copy_bytes=128e6, copy_fetch_kib=62516.375, copy_write_kib=125000.0),
+        sources="91ec44f146de072c", fetch_kib=63184.9, write_kib=68703.9,
+        copy_bytes=128e6, copy_fetch_kib=62514.375, copy_write_kib=125000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
 FAMILY_SOURCES = {
