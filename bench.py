@@ -98,8 +98,8 @@ def measured_traffic(w, family):
 def algorithmic_work(w):
     """(flops, bytes) of one fused E+M pass: X read once; flops per point:
     diag 8DK (scores 4DK + statistics 4DK), iso 4DK, full (2 D(D+1) + 4D) K
-    (forward solve D(D+1)/2 FMA + symmetric outer product D(D+1)/2 FMA +
-    4D per point and component)."""
+    (whitening by the triangular inverse factor D(D+1)/2 FMA + symmetric outer
+    product D(D+1)/2 FMA + 4D per point and component)."""
     es = 4 if w.x_dtype == "f32" else 2
     d = w.d
     per_pt = {"diag": 8 * d * w.k, "iso": 4 * d * w.k, "full": (2 * d * (d + 1) + 4 * d) * w.k}[w.cov]
@@ -198,10 +198,11 @@ def main(argv=None):
 
     flops, nbytes = algorithmic_work(w)
     fp32_path = w.cov == "diag" and w.k <= 64          # fp32-accurate split-fp16 MFMA family
-    full_path = w.cov == "full"                        # fp32 vector forward solve
-    # the diagonal family runs its contractions on the fp16 matrix cores (each
-    # fp32 operand as an fp16 hi + lo pair): its compute roof is the fp16 one
-    peak_key = "f32_vector" if full_path else "f16"
+    full_path = w.cov == "full"                        # fp16 MFMA whitening + moments
+    # every family runs its contractions on the fp16 matrix cores (the diagonal
+    # family and the full family's whitening factor as fp16 hi + lo pairs):
+    # the compute roof is the fp16 one
+    peak_key = "f16"
     achieved_tflops = flops / (fused_avg * 1e-3) / 1e12
     hbm = nbytes / (fused_avg * 1e-3) / 1e9
     t_mfma = flops / (PEAK_TFLOPS[peak_key] * 1e12)
@@ -209,13 +210,10 @@ def main(argv=None):
     family = "diag_f32" if fp32_path else ("full" if full_path else "largek")
     traffic = measured_traffic(w, family)
     if t_mfma >= t_hbm:
-        roof = {"bound": "alu" if full_path else "mfma", "achieved": achieved_tflops,
+        roof = {"bound": "mfma", "achieved": achieved_tflops,
                 "peak": PEAK_TFLOPS[peak_key], "unit": "TFLOP/s",
                 "frac": achieved_tflops / PEAK_TFLOPS[peak_key],
                 "traffic": None if traffic is None else traffic["bytes"]}
-        if full_path:   # packed fp32 instructions are not used: half the published rate
-            roof["peak_unpacked_fma"] = PEAK_TFLOPS[peak_key] / 2
-            roof["frac_unpacked_fma"] = achieved_tflops / (PEAK_TFLOPS[peak_key] / 2)
     else:
         roof = {"bound": "hbm", "achieved": hbm, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": hbm / PEAK_HBM_GBPS, "traffic": None if traffic is None else traffic["bytes"]}
@@ -249,10 +247,11 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "split-f16/f32" if fp32_path else ("f32" if full_path else "f16"),
+        "dtype": "split-f16/f32" if fp32_path else "f16",
         "math": ("products of fp16 hi/lo operand pairs on fp16 MFMA, fp32 accumulation, "
                  "fp32 exp/log/statistics" if fp32_path else
-                 "fp32 vector forward solve, fp16 MFMA second moments" if full_path else
+                 "fp16 MFMA whitening (inverse factor as fp16 hi + lo pairs) and second "
+                 "moments, fp32 accumulation and softmax" if full_path else
                  "fp16 MFMA scores and statistics, fp32 accumulation and softmax"),
         "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "d": w.d, "k": w.k, "cov": w.cov,

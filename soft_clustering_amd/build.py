@@ -12,7 +12,6 @@ import argparse
 import concurrent.futures as cf
 import glob
 import os
-import shutil
 import subprocess
 import sys
 
@@ -35,25 +34,26 @@ FLAGS = [
 
 # Translation units whose kernels never test floats for NaN: IEEE mode off
 # lets max/min fold into DPP forms (one v_max_f32_dpp per reduction step).
-NO_IEEE = {f: ["-mno-amdgpu-ieee", "-fno-honor-nans"] for f in ("diag_split.hip", "largek.hip")}
+NO_IEEE = {f: ["-fno-honor-nans", "-mno-amdgpu-ieee"] for f in ("diag_split.hip", "largek.hip")}
 
-# The full-covariance forward solve must unroll completely (its z vector lives
-# in registers); the default size cap for requested unrolling stops at D = 64.
+# The full-covariance kernel's second-moment loops must unroll completely (its
+# accumulator blocks live in registers); the default size cap for requested
+# unrolling stops short of D = 64.
 EXTRA = {"full_fused.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
 
 
 def _compile(src: str, asm_dir: str | None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     base = os.path.basename(src)
-    cmd = [HIPCC, *FLAGS, *NO_IEEE.get(base, []), *EXTRA.get(base, []), "-c", src, "-o", obj]
-    if asm_dir:
-        cmd += ["-save-temps=obj"]
-    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")
-    if asm_dir:
-        for s in glob.glob(os.path.join(BUILD, "*gfx950*.s")):
-            shutil.copy(s, asm_dir)
+    flags = [*FLAGS, *NO_IEEE.get(base, []), *EXTRA.get(base, [])]
+    cmds = [[HIPCC, *flags, "-c", src, "-o", obj]]
+    if asm_dir:   # the device code's ISA, compiled on its own
+        asm = os.path.join(os.path.abspath(asm_dir), base.replace(".hip", f"-{ARCH}.s"))
+        cmds.append([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", asm])
+    for cmd in cmds:
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")
     return obj
 
 

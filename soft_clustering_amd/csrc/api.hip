@@ -126,7 +126,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         return GMM_OK;
     }
     if (p->cov == GMM_COV_FULL && p->xdt == GMM_F16) {
-        // full covariance: fp16 X / mu / L, fp32 forward solve, fp16 MFMA second moments
+        // full covariance: fp16 X, split fp16 whitening panel, fp16 MFMA whitening and moments
         if (p->d > 64 || p->k > kFullKP) return GMM_E_UNSUPPORTED;
         int dp = pad_dim(p->d);
         const int64_t tiles = (p->n + kFullT - 1) / kFullT;
@@ -139,8 +139,8 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_pi = take(sizeof(float) * p->k);
         p->off_mu = take(sizeof(float) * p->k * p->d);
         p->off_cov = take(sizeof(float) * p->k * p->d * p->d);
-        p->off_panel = take(sizeof(uint16_t) * kFullKP * full_l_halves(dp));
-        p->off_shift = take(sizeof(float) * (2 * kFullKP * dp + 2 * kFullKP));
+        p->off_panel = take(sizeof(uint4) * full_w_vecs(dp));
+        p->off_shift = take(sizeof(float) * (kFullKP * full_dpo(dp) + kFullKP * dp + 2 * kFullKP));
         p->off_part = take(sizeof(double) * (size_t)p->p_max * kFullKP * ncolp);
         p->off_part_ll = take(sizeof(double) * kFullLLSlots);
         p->off_chunk = take(sizeof(double) * p->k * ncolp);

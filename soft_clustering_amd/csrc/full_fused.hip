@@ -1,24 +1,27 @@
 // Full-covariance Gaussian mixture, X stored in fp16: fused E-step + M-step
 // statistics, one pass over X, no N x K matrix in memory.
 //
-// Density ([LP-GMM] 1.2, route 2): d^2 = |z|^2 with L z = x - mu solved by
-// forward substitution (no inverse), L the ridged Cholesky factor stored in
-// fp16 ([LP-GMM] 2.1 storage plan, 4.1 ridge); log|C| = 2 sum log L_ii.  The
-// solve and every exp / log / normaliser run in fp32 ([LP-GMM] 1.3 first
-// boundary): the fp16 entries of L feed v_fma_mix_f32 directly.
+// Density ([LP-GMM] 1.2, route 2): d^2 = |z|^2 with L z = x - mu.  The
+// triangular solve is taken as a product with the inverse factor: z 2^e =
+// W x - W mu, W = (L 2^-e)^{-1} formed in fp64 by the preparation kernel and
+// stored as fp16 hi + lo parts, so each 32 x 32 block of W x is two
+// v_mfma_f32_32x32x16_f16 per K step against the exact fp16 X, accumulated in
+// fp32; the bias, |z|^2, exp, log and every normaliser stay fp32 ([LP-GMM]
+// 1.3 first boundary); log|C| = 2 sum log L_ii.
 // Statistics ([Flash-GMM] Method, s0 / s1 / sum gamma x x^T on chip): s1 =
 // gamma^T X and the centred second moment sum_n gamma_nk (x_n - mu_k)
 // (x_n - mu_k)^T (lower-triangle 16 x 16 blocks) on fp16 MFMA
 // (v_mfma_f32_16x16x32_f16) with fp32 accumulation; the M-step turns them into
 // raw moments and the new covariance in fp64.
 //
-// Work split: a workgroup of 256 threads takes 256-point tiles.  Phase 1: each
-// thread solves its own point against every component (L of all components
-// staged once in LDS, broadcast reads), forms the base-2 log-sum-exp and the
-// responsibilities in registers, and writes gamma^T and x^T for the tile to
-// LDS.  Phase 2 (E+M only): wave w accumulates the second moments of
-// components 4w..4w+3 and the first moments of dimension block w over the
-// tile.  Two barriers per tile.
+// Work split: a workgroup of 256 threads takes 256-point tiles.  Each thread
+// loads one point into a row-major and a transposed LDS copy of the tile.
+// Phase 1: wave w whitens the tile against components 4w..4w+3 (the
+// component's panel in registers, the next component's panel loading behind
+// it), writing the base-2 scores to LDS.  Then each thread forms the
+// log-sum-exp and the responsibilities of its point.  Phase 2 (E+M only):
+// wave w accumulates the second moments of components 4w..4w+3 and the first
+// moments of dimension block w over the tile.
 
 #include "full_internal.h"
 
@@ -34,51 +37,49 @@ constexpr int T = kFullT;
 constexpr float kLn2f = 0.69314718055994530942f;
 constexpr float kHalfLog2e = 0.72134752044448170368f;   // log2(e) / 2
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 template <int DP>
 struct FullShape {
-    static constexpr int kLH = full_l_halves(DP);       // halves of packed L per component
     static constexpr int kNB = DP / 16;                  // 16-dim blocks
     static constexpr int kNBlk = kNB * (kNB + 1) / 2;    // lower-triangle 16 x 16 blocks
     static constexpr int kXT = T + 8;                    // halves per x^T row
+    static constexpr int kXR = DP + 8;                   // halves per row of the row-major tile
+    static constexpr int kNOB = full_nob(DP), kNKS = full_nks(DP), kDPO = full_dpo(DP);
+    static constexpr int kNV = 2 * kNOB * kNKS;          // panel vectors per lane and component
 };
 
 __device__ __forceinline__ int blk_index(int ab, int bb) { return ab * (ab + 1) / 2 + bb; }
 
+static_assert(KP == 16, "four components per wave, four waves");
+
 template <int DP, bool EM>
 __global__ __launch_bounds__(256, 1) void k_full_fused(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real, int vec,
-    const uint16_t* __restrict__ lpk, const float* __restrict__ pdiag, const float* __restrict__ muh,
+    const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, double* __restrict__ part,
     double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
     using Sh = FullShape<DP>;
     constexpr int NB = Sh::kNB, NBLK = Sh::kNBlk;
-    __shared__ __attribute__((aligned(16))) uint16_t l_s[KP * Sh::kLH];
-    __shared__ __attribute__((aligned(16))) float pd_s[KP][DP];
-    __shared__ __attribute__((aligned(16))) float ms_s[KP][DP];      // mu * 2^-e_k
+    constexpr int NOB = Sh::kNOB, NKS = Sh::kNKS, DPO = Sh::kDPO, NV = Sh::kNV;
     __shared__ __attribute__((aligned(16))) uint16_t mh_s[KP][DP];   // fp16 mu
-    __shared__ float cv_s[KP], rs_s[KP];
+    __shared__ __attribute__((aligned(16))) float wb_s[KP][DPO];     // W mu
+    __shared__ float cv_s[KP], hq_s[KP];
     __shared__ __attribute__((aligned(16))) float g_s[KP][T];        // scores, then gamma
+    __shared__ __attribute__((aligned(16))) uint16_t xr_s[T][Sh::kXR];   // the tile, row-major
     __shared__ __attribute__((aligned(16))) uint16_t xt_s[EM ? DP : 1][Sh::kXT];
     __shared__ double red[256];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
 
     // ---- stage the prepared parameters of all components
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(lpk);
-        uint4* dst = reinterpret_cast<uint4*>(l_s);
-        for (int i = tid; i < KP * Sh::kLH / 8; i += 256) dst[i] = src[i];
-        for (int i = tid; i < KP * DP; i += 256) {
-            const int k = i / DP, dd = i % DP;
-            pd_s[k][dd] = pdiag[i];
-            const float m = muh[i];
-            ms_s[k][dd] = m * rscale[k];
-            mh_s[k][dd] = __builtin_bit_cast(uint16_t, (_Float16)m);
-        }
-        if (tid < KP) {
-            cv_s[tid] = cvec[tid];
-            rs_s[tid] = rscale[tid];
-        }
+    for (int i = tid; i < KP * DP; i += 256)
+        mh_s[i / DP][i % DP] = __builtin_bit_cast(uint16_t, (_Float16)muh[i]);
+    for (int i = tid; i < KP * DPO; i += 256) wb_s[i / DPO][i % DPO] = wbias[i];
+    if (tid < KP) {
+        const float rs = rscale[tid];
+        cv_s[tid] = cvec[tid];
+        hq_s[tid] = kHalfLog2e * rs * rs;   // |z|^2 = 2^-2e |W x - W mu|^2
     }
 
     const int G = gridDim.x;
@@ -101,64 +102,119 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     }
     double ll = 0.0;
 
+    // One point of tile t (fp16), zero outside [0, N) x [0, D).  Every load is
+    // issued unconditionally from an in-bounds address and masked afterwards,
+    // so the loads of a tile are all in flight together.
+    auto load_point = [&](int64_t t, uint4 (&xv)[DP / 8]) __attribute__((always_inline)) {
+        const int64_t p = t * T + tid;
+        const bool valid = p < n;
+        const _Float16* row = x + (valid ? p : 0) * ldx;
+        if (vec) {   // d % 8 == 0, rows 16-byte aligned
+            const int cmax = d / 8;
+#pragma unroll
+            for (int c = 0; c < DP / 8; ++c) {
+                const uint4 v = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
+                const uint32_t m = (valid && c < cmax) ? ~0u : 0u;
+                xv[c] = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+            }
+        } else {
+            const uint16_t* rb = reinterpret_cast<const uint16_t*>(row);
+#pragma unroll
+            for (int c = 0; c < DP / 8; ++c) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i0 = 8 * c + 2 * q;
+                    const uint32_t lo = rb[i0 < d ? i0 : 0], hi = rb[i0 + 1 < d ? i0 + 1 : 0];
+                    wv[q] = (valid && i0 < d ? lo : 0u) | ((valid && i0 + 1 < d ? hi : 0u) << 16);
+                }
+                xv[c] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+        }
+    };
+    // The panel of component k (this lane's NV vectors).
+    auto load_panel = [&](int k, half8 (&wp)[NV]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            wp[v] = __builtin_bit_cast(half8, wpk[((int64_t)k * NV + v) * 64 + lane]);
+    };
+
+    uint4 xv[DP / 8];
+    half8 wp[NV];
+    if (t0 < t1) {
+        load_point(t0, xv);
+        load_panel(4 * w, wp);
+    }
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t p = t * T + tid;
         const bool valid = p < n;
-        // ---- load this thread's point (fp16 -> fp32), zero outside [0, N) x [0, D)
-        float xf[DP];
-        {
-            const _Float16* row = x + (valid ? p : 0) * ldx;
-            if (vec) {
+        __syncthreads();   // the previous tile is done with xr_s / xt_s / g_s
 #pragma unroll
-                for (int c = 0; c < DP / 8; ++c) {
-                    uint4 v = make_uint4(0, 0, 0, 0);
-                    if (8 * c < d) v = *reinterpret_cast<const uint4*>(row + 8 * c);
-                    const half8 h = __builtin_bit_cast(half8, v);
+        for (int c = 0; c < DP / 8; ++c) {
+            *reinterpret_cast<uint4*>(&xr_s[tid][8 * c]) = xv[c];
+            if constexpr (EM) {
+                const uint32_t wv[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) xf[8 * c + e] = valid ? (float)h[e] : 0.0f;
+                for (int q = 0; q < 4; ++q) {
+                    xt_s[8 * c + 2 * q][tid] = (uint16_t)(wv[q] & 0xFFFFu);
+                    xt_s[8 * c + 2 * q + 1][tid] = (uint16_t)(wv[q] >> 16);
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < DP; ++i) xf[i] = (valid && i < d) ? (float)row[i] : 0.0f;
             }
         }
-        __syncthreads();   // the previous tile's phase 2 is done with g_s / xt_s
+        __syncthreads();
+        if (t + 1 < t1) load_point(t + 1, xv);   // the next tile, behind this one's work
 
-        // ---- phase 1: forward solve against every component (fp32)
-        for (int k = 0; k < KP; ++k) {
-            const uint16_t* Lk = l_s + k * Sh::kLH;
-            const float s = rs_s[k];
-            float z[DP];
-            float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;   // |z|^2 partial sums
+        // ---- phase 1: W x for the components of this wave, 32 points at a time:
+        // A = panel (out dimensions x inputs), B = tile rows (inputs x points);
+        // lane l holds point l % 32, out dimensions 32 ob + 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll 1
+        for (int kk = 0; kk < KP / 4; ++kk) {
+            const int k = 4 * w + kk;
+            half8 wc[NV];
 #pragma unroll
-            for (int i = 0; i < DP; ++i) {
-                const float r = fmaf(xf[i], s, -ms_s[k][i]);
-                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            for (int v = 0; v < NV; ++v) wc[v] = wp[v];
+            if (kk + 1 < KP / 4) load_panel(k + 1, wp);   // the next component's panel
+            else if (t + 1 < t1) load_panel(4 * w, wp);  // the first one of the next tile
+            float bias[NOB][16];
 #pragma unroll
-                for (int jb = 0; jb < DP / 8; ++jb) {   // constant trip count: unrolls fully
-                    if (8 * jb >= i) continue;
-                    const half8 lh = __builtin_bit_cast(
-                        half8, *reinterpret_cast<const uint4*>(Lk + full_row_off(i) + 8 * jb));
+            for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int jj = 8 * jb + e;
-                        if (jj < i) {
-                            const float lv = (float)lh[e];   // v_fma_mix_f32
-                            if ((e & 3) == 0) a0 = fmaf(lv, z[jj], a0);
-                            else if ((e & 3) == 1) a1 = fmaf(lv, z[jj], a1);
-                            else if ((e & 3) == 2) a2 = fmaf(lv, z[jj], a2);
-                            else a3 = fmaf(lv, z[jj], a3);
-                        }
+                for (int r = 0; r < 16; ++r)
+                    bias[ob][r] = wb_s[k][32 * ob + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
+            const float cvk = cv_s[k], hqk = hq_s[k];
+#pragma unroll 2
+            for (int st = 0; st < T / 32; ++st) {
+                f32x16 acc[NOB];
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[ob][r] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const half8 xb = __builtin_bit_cast(
+                        half8, *reinterpret_cast<const uint4*>(&xr_s[32 * st + (lane & 31)][16 * ks + 8 * (lane >> 5)]));
+#pragma unroll
+                    for (int ob = 0; ob < NOB; ++ob) {
+                        if (ks > 2 * ob + 1) continue;   // above the diagonal: W is lower triangular
+                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wc[ob * NKS + ks], xb, acc[ob], 0, 0, 0);
+                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wc[(NOB + ob) * NKS + ks], xb, acc[ob], 0, 0, 0);
                     }
                 }
-                z[i] = (r - ((a0 + a1) + (a2 + a3))) * pd_s[k][i];
-                if ((i & 3) == 0) q0 = fmaf(z[i], z[i], q0);
-                else if ((i & 3) == 1) q1 = fmaf(z[i], z[i], q1);
-                else if ((i & 3) == 2) q2 = fmaf(z[i], z[i], q2);
-                else q3 = fmaf(z[i], z[i], q3);
+                float q0 = 0.0f, q1 = 0.0f;
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const float z0 = acc[ob][r] - bias[ob][r], z1 = acc[ob][r + 1] - bias[ob][r + 1];
+                        q0 = fmaf(z0, z0, q0);
+                        q1 = fmaf(z1, z1, q1);
+                    }
+                float q = q0 + q1;
+                q += __shfl_xor(q, 32);
+                if (lane < 32) g_s[k][32 * st + lane] = cvk - hqk * q;
             }
-            g_s[k][tid] = cv_s[k] - kHalfLog2e * ((q0 + q1) + (q2 + q3));
         }
+        __syncthreads();
 
         // ---- base-2 log-sum-exp, responsibilities (thread-local)
         {
@@ -183,8 +239,6 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                     s0acc[k] += gk;
                     g_s[k][tid] = gk;
                 }
-#pragma unroll
-                for (int i = 0; i < DP; ++i) xt_s[i][tid] = __builtin_bit_cast(uint16_t, (_Float16)xf[i]);
             } else if (valid) {
                 if (out_lse) out_lse[p] = lse2 * kLn2f;
                 if (out_arg) {
@@ -291,11 +345,11 @@ hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int
     const int vec = ((uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0) ? 1 : 0;
     if (em)
         hipLaunchKernelGGL((k_full_fused<DP, true>), dim3(grid), dim3(256), 0, s, (const _Float16*)x,
-                           p.n, (int)p.d, p.ldx, (int)p.k, vec, w.lpk, w.pdiag, w.muh, w.cvec,
+                           p.n, (int)p.d, p.ldx, (int)p.k, vec, w.wpk, w.wbias, w.muh, w.cvec,
                            w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr);
     else
         hipLaunchKernelGGL((k_full_fused<DP, false>), dim3(grid), dim3(256), 0, s, (const _Float16*)x,
-                           p.n, (int)p.d, p.ldx, (int)p.k, vec, w.lpk, w.pdiag, w.muh, w.cvec,
+                           p.n, (int)p.d, p.ldx, (int)p.k, vec, w.wpk, w.wbias, w.muh, w.cvec,
                            w.rscale, w.part, w.part_ll, lse, arg);
     return hipGetLastError();
 }

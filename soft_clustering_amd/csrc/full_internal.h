@@ -1,6 +1,6 @@
-// Internal interface of the full-covariance family: X stored in fp16 (or
-// bf16 / fp32), per-component Cholesky factors L stored in fp16, fp32 forward
-// solve on the vector unit, fp16 MFMA for the second-moment statistics.
+// Internal interface of the full-covariance family: X stored in fp16, the
+// inverse Cholesky factor of every component as a split fp16 panel,
+// whitening and second moments on fp16 MFMA, fp32 softmax and accumulation.
 #pragma once
 
 #include "common.h"
@@ -12,27 +12,26 @@ constexpr int kFullKP = 16;        // components per launch (K <= 16, padded to 
 constexpr int kFullT = 256;        // points per tile: one per thread
 constexpr int kFullLLSlots = 512;  // per-workgroup LL partial slots
 
-// Halves per packed row of the strictly-lower part of L: row i holds
-// L[i][0..i-1], padded to a multiple of 8 so that every row starts on a
-// 16-byte boundary.
-__host__ __device__ constexpr int full_row_halves(int i) { return (i + 7) / 8 * 8; }
-__host__ __device__ constexpr int full_row_off(int i) {
-    int o = 0;
-    for (int r = 0; r < i; ++r) o += full_row_halves(r);
-    return o;
-}
-__host__ __device__ constexpr int full_l_halves(int dp) { return full_row_off(dp); }
+// Whitening panel W = (L s)^{-1} (s = 2^-e the component's power-of-two
+// scale) as the A operand of v_mfma_f32_32x32x16_f16: output dimensions in
+// blocks of 32 (rows), input dimensions in steps of 16 (K); every entry split
+// into fp16 hi and lo parts.  Per component: [hi / lo][out block][K step][64
+// lanes] 16-byte vectors, lane l holding row l % 32 and K 8 (l / 32) + e.
+__host__ __device__ constexpr int full_nob(int dp) { return dp >= 32 ? dp / 32 : 1; }
+__host__ __device__ constexpr int full_nks(int dp) { return dp / 16; }
+__host__ __device__ constexpr int full_dpo(int dp) { return 32 * full_nob(dp); }
+inline size_t full_w_vecs(int dp) { return (size_t)kFullKP * 2 * full_nob(dp) * full_nks(dp) * 64; }
 
 // Packed lower triangle of a D x D symmetric matrix, row-major: (i, j <= i).
 __host__ __device__ inline int64_t tri_idx(int64_t i, int64_t j) { return i * (i + 1) / 2 + j; }
 
 struct FullWs {
     float *pi, *mu, *cov;      // fp32 parameters theta (cov [K][D][D])
-    uint16_t* lpk;             // [KP][full_l_halves(DP)] fp16 strictly-lower L (scaled)
-    float* pdiag;              // [KP][DP] 1 / L_ii (of the fp16-rounded, scaled L)
-    float* muh;                // [KP][DP] fp16-rounded mean, as fp32 (the solve's centre)
+    uint4* wpk;                // whitening panel (see full_nob), hi / lo fp16
+    float* wbias;              // [KP][dpo] W mu (fp32): z 2^e = W x - W mu
+    float* muh;                // [KP][DP] fp16-rounded mean, as fp32 (centre of the moments)
     float* cvec;               // [KP] base-2 constant log2 pi - 1/2 log2 e (D log 2pi + log|C|)
-    float* rscale;             // [KP] 2^-e_k: the solve runs on (x - mu) 2^-e_k against L 2^-e_k
+    float* rscale;             // [KP] 2^-e_k: |z|^2 = 2^-2e_k |W x - W mu|^2
     double *part, *part_ll;    // per-workgroup partials [P][KP][ncolp], [P]
     double *colsum;            // [K][ncolp] reduced partials
     double *stats, *ll;        // [K][1 + D + D*D] raw statistics (full matrices), LL
@@ -46,10 +45,10 @@ inline FullWs full_ws(const Plan& p, char* ws) {
     w.pi = (float*)(ws + p.off_pi);
     w.mu = (float*)(ws + p.off_mu);
     w.cov = (float*)(ws + p.off_cov);
-    w.lpk = (uint16_t*)(ws + p.off_panel);
+    w.wpk = (uint4*)(ws + p.off_panel);
     char* after = ws + p.off_shift;
-    w.pdiag = (float*)after;
-    w.muh = w.pdiag + kFullKP * p.dp;
+    w.wbias = (float*)after;
+    w.muh = w.wbias + kFullKP * full_dpo(p.dp);
     w.cvec = w.muh + kFullKP * p.dp;
     w.rscale = w.cvec + kFullKP;
     w.part = (double*)(ws + p.off_part);

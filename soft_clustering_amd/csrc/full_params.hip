@@ -6,10 +6,12 @@
 // in fp64; on a pivot that is not positive (or not finite) eps becomes
 // max(10 eps, 1e-3 |tr C| / D) and the factorisation is repeated, at most 3
 // times, after which the component is flagged not positive definite and its
-// weight is treated as 0.  L is scaled by 2^-e_k (2^e_k near sqrt(|tr C|/D))
-// and stored in fp16; log|C~| = 2 sum log L_ii is taken from the rounded
-// factor, so the density matches the L the solve uses.  The mean is stored
-// in fp16 as the solve's centre.
+// weight is treated as 0.  The forward solve L z = x - mu is carried out by
+// the fused kernel as a product with W = (L 2^-e_k)^{-1} (2^e_k near
+// sqrt(|tr C|/D)), which this kernel forms in fp64 (a triangular inverse,
+// one column per thread) and stores as a split fp16 panel (hi + lo, 22
+// bits) with the bias W mu; log|C~| = 2 sum log L_ii from the fp64 factor.
+// The mean is also stored in fp16 as the centre of the second moments.
 // M-step ([Flash-GMM] Method): pi' = s0/N, mu' = s1/s0,
 // C' = sum gamma (x - mu')(x - mu')^T / s0, here from the second moment
 // about the stored centre: C' = M2/s0 - delta delta^T, delta = mu' - centre.
@@ -47,18 +49,20 @@ __global__ __launch_bounds__(256) void k_full_load(int k_real, int d, const floa
 template <int DP>
 __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridge_rel,
                                                    const float* pi, const float* mu,
-                                                   const float* cov, uint16_t* lpk, float* pdiag,
+                                                   const float* cov, uint4* wpk, float* wbias,
                                                    float* muh, float* cvec, float* rscale,
                                                    int* flags) {
+    constexpr int NOB = full_nob(DP), NKS = full_nks(DP), DPO = full_dpo(DP);
+    constexpr int NV = 2 * NOB * NKS * 64;   // panel vectors per component
     __shared__ double A[DP][DP + 1];
+    __shared__ double W[DP][DP + 1];
     __shared__ double red[256];
     __shared__ int fail;
     const int k = blockIdx.x, tid = threadIdx.x;
-    constexpr int LH = full_l_halves(DP);
-    uint16_t* Lk = lpk + (int64_t)k * LH;
-    auto put_identity = [&]() {
-        for (int i = tid; i < LH; i += 256) Lk[i] = 0;
-        for (int i = tid; i < DP; i += 256) pdiag[k * DP + i] = 1.0f;
+    uint4* Wk = wpk + (int64_t)k * NV;
+    auto put_identity = [&]() {   // a zero panel: the component is never scored (c_k = -inf)
+        for (int i = tid; i < NV; i += 256) Wk[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < DPO; i += 256) wbias[k * DPO + i] = 0.0f;
     };
     if (k >= k_real) {   // padding component
         put_identity();
@@ -132,29 +136,61 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         }
         return;
     }
-    // scale 2^-e with 2^e near sqrt(|tr| / D); fp16 factor, its reciprocal diagonal, log-det
+    // scale s = 2^-e with 2^e near sqrt(|tr| / D); W = (L s)^{-1} in fp64, one
+    // column per thread: W_jj = 1 / (L s)_jj, W_ij = -(sum_{m=j}^{i-1} (L s)_im W_mj) / (L s)_ii
     int e = 0;
     if (scale > 0.0 && isfinite(scale)) {
         e = ilogb(sqrt(scale));
         e = e < -60 ? -60 : (e > 60 ? 60 : e);
     }
     const double sc = ldexp(1.0, -e);
+    for (int jc = tid; jc < DP; jc += 256) {
+        for (int i = 0; i < jc; ++i) W[i][jc] = 0.0;
+        W[jc][jc] = 1.0 / (A[jc][jc] * sc);
+        for (int i = jc + 1; i < DP; ++i) {
+            double acc = 0.0;
+            for (int m = jc; m < i; ++m) acc += A[i][m] * W[m][jc];
+            W[i][jc] = -(acc * sc) / (A[i][i] * sc);
+        }
+    }
+    __syncthreads();
+    // panel: out dimension o = 32 ob + l % 32 (rows), input i = 16 ks + 8 (l / 32) + q;
+    // zero outside the D x D lower triangle; hi = fp16(w), lo = fp16(w - hi)
+    for (int v = tid; v < NV / 2; v += 256) {
+        const int l = v % 64, ks = (v / 64) % NKS, ob = v / (64 * NKS);
+        const int o = 32 * ob + (l & 31);
+        uint32_t hw[4], lw[4];
+        for (int q2 = 0; q2 < 4; ++q2) {
+            _Float16 h[2], lo[2];
+            for (int t = 0; t < 2; ++t) {
+                const int i = 16 * ks + 8 * (l >> 5) + 2 * q2 + t;
+                const double wv = (o < d && i < d && i <= o) ? W[o][i] : 0.0;
+                const float f = (float)wv;
+                h[t] = (_Float16)f;
+                lo[t] = (_Float16)(f - (float)h[t]);
+            }
+            hw[q2] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+            lw[q2] = (uint32_t)__builtin_bit_cast(uint16_t, lo[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, lo[1]) << 16);
+        }
+        Wk[v] = make_uint4(hw[0], hw[1], hw[2], hw[3]);              // hi half of the panel
+        Wk[NV / 2 + v] = make_uint4(lw[0], lw[1], lw[2], lw[3]);     // lo half
+    }
+    // bias W mu (fp64), the fp16 centre of the moments, log|C~| from the fp64 factor
     double ld = 0.0;
+    for (int o = tid; o < DPO; o += 256) {
+        double b = 0.0;
+        if (o < d)
+            for (int i = 0; i <= o; ++i) b += W[o][i] * (double)mu[(int64_t)k * d + i];
+        wbias[k * DPO + o] = (float)b;
+    }
     for (int i = tid; i < DP; i += 256) {
-        const _Float16 h = (_Float16)(float)(A[i][i] * sc);
-        const float lf = (float)h;
-        pdiag[k * DP + i] = 1.0f / lf;
-        if (i < d) ld += log((double)lf);
+        if (i < d) ld += log(A[i][i]);
         const float m = i < d ? mu[(int64_t)k * d + i] : 0.0f;
         muh[k * DP + i] = (float)(_Float16)m;
-        for (int c = 0; c < full_row_halves(i); ++c) {
-            const float v = c < i ? (float)(A[i][c] * sc) : 0.0f;
-            Lk[full_row_off(i) + c] = __builtin_bit_cast(uint16_t, (_Float16)v);
-        }
     }
     ld = block_sum_f64(ld, red);
     if (tid == 0) {
-        const double logdet = 2.0 * ld + 2.0 * (double)d * (double)e * kLn2;
+        const double logdet = 2.0 * ld;
         const double lp = log((double)pi[k]);
         cvec[k] = (float)(kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logdet)));
         rscale[k] = (float)sc;
@@ -256,7 +292,7 @@ __global__ __launch_bounds__(256) void k_full_sum_ll(const double* part_ll, int 
 hipError_t chol(const Plan& p, const FullWs& w, hipStream_t s) {
 #define FULL_CHOL(DP_)                                                                            \
     hipLaunchKernelGGL((k_full_chol<DP_>), dim3(kFullKP), dim3(256), 0, s, (int)p.k, (int)p.d,     \
-                       p.ridge_rel, w.pi, w.mu, w.cov, w.lpk, w.pdiag, w.muh, w.cvec, w.rscale,    \
+                       p.ridge_rel, w.pi, w.mu, w.cov, w.wpk, w.wbias, w.muh, w.cvec, w.rscale,    \
                        w.flags)
     switch (p.dp) {
         case 16: FULL_CHOL(16); break;
