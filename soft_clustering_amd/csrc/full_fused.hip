@@ -38,12 +38,23 @@ constexpr float kLn2f = 0.69314718055994530942f;
 constexpr float kHalfLog2e = 0.72134752044448170368f;   // log2(e) / 2
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i' reads 4 halves of
+// row (i' / 4) at column 4 (i' % 4) (addresses as given); lane i receives
+// column i of the 4 rows.
+__device__ __forceinline__ uint2 tr16(const uint16_t* p) {
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_u16*)p));
+    return __builtin_bit_cast(uint2, v);
+}
 
 template <int DP>
 struct FullShape {
     static constexpr int kNB = DP / 16;                  // 16-dim blocks
     static constexpr int kNBlk = kNB * (kNB + 1) / 2;    // lower-triangle 16 x 16 blocks
-    static constexpr int kXT = T + 8;                    // halves per x^T row
+    static constexpr int kGS = T + 4;                    // floats per row of the score tile
     static constexpr int kXR = DP + 8;                   // halves per row of the row-major tile
     static constexpr int kNOB = full_nob(DP), kNKS = full_nks(DP), kDPO = full_dpo(DP);
     static constexpr int kNV = 2 * kNOB * kNKS;          // panel vectors per lane and component
@@ -53,29 +64,32 @@ __device__ __forceinline__ int blk_index(int ab, int bb) { return ab * (ab + 1) 
 
 static_assert(KP == 16, "four components per wave, four waves");
 
-template <int DP, bool EM>
+// VEC: d % 8 == 0 and 16-byte aligned rows (whole-vector loads); otherwise
+// per-element loads.  A template parameter, so that each kernel holds one path.
+template <int DP, bool EM, bool VEC>
 __global__ __launch_bounds__(256, 1) void k_full_fused(
-    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real, int vec,
+    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, double* __restrict__ part,
     double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
     using Sh = FullShape<DP>;
     constexpr int NB = Sh::kNB, NBLK = Sh::kNBlk;
     constexpr int NOB = Sh::kNOB, NKS = Sh::kNKS, DPO = Sh::kDPO, NV = Sh::kNV;
-    __shared__ __attribute__((aligned(16))) uint16_t mh_s[KP][DP];   // fp16 mu
-    __shared__ __attribute__((aligned(16))) float wb_s[KP][DPO];     // W mu
+    __shared__ __attribute__((aligned(16))) uint32_t nm_s[KP][DP];   // (-mu, -mu) as fp16 pairs
+    __shared__ __attribute__((aligned(16))) float wb_s[KP][DPO];     // -W mu
     __shared__ float cv_s[KP], hq_s[KP];
-    __shared__ __attribute__((aligned(16))) float g_s[KP][T];        // scores, then gamma
+    __shared__ __attribute__((aligned(16))) float g_s[KP][Sh::kGS];  // scores, then gamma
     __shared__ __attribute__((aligned(16))) uint16_t xr_s[T][Sh::kXR];   // the tile, row-major
-    __shared__ __attribute__((aligned(16))) uint16_t xt_s[EM ? DP : 1][Sh::kXT];
     __shared__ double red[256];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
 
     // ---- stage the prepared parameters of all components
-    for (int i = tid; i < KP * DP; i += 256)
-        mh_s[i / DP][i % DP] = __builtin_bit_cast(uint16_t, (_Float16)muh[i]);
-    for (int i = tid; i < KP * DPO; i += 256) wb_s[i / DPO][i % DPO] = wbias[i];
+    for (int i = tid; i < KP * DP; i += 256) {
+        const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-muh[i]));
+        nm_s[i / DP][i % DP] = h | (h << 16);
+    }
+    for (int i = tid; i < KP * DPO; i += 256) wb_s[i / DPO][i % DPO] = -wbias[i];
     if (tid < KP) {
         const float rs = rscale[tid];
         cv_s[tid] = cvec[tid];
@@ -109,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
         const int64_t p = t * T + tid;
         const bool valid = p < n;
         const _Float16* row = x + (valid ? p : 0) * ldx;
-        if (vec) {   // d % 8 == 0, rows 16-byte aligned
+        if constexpr (VEC) {
             const int cmax = d / 8;
 #pragma unroll
             for (int c = 0; c < DP / 8; ++c) {
@@ -148,19 +162,9 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t p = t * T + tid;
         const bool valid = p < n;
-        __syncthreads();   // the previous tile is done with xr_s / xt_s / g_s
+        __syncthreads();   // the previous tile is done with xr_s / g_s
 #pragma unroll
-        for (int c = 0; c < DP / 8; ++c) {
-            *reinterpret_cast<uint4*>(&xr_s[tid][8 * c]) = xv[c];
-            if constexpr (EM) {
-                const uint32_t wv[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    xt_s[8 * c + 2 * q][tid] = (uint16_t)(wv[q] & 0xFFFFu);
-                    xt_s[8 * c + 2 * q + 1][tid] = (uint16_t)(wv[q] >> 16);
-                }
-            }
-        }
+        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[tid][8 * c]) = xv[c];
         __syncthreads();
         if (t + 1 < t1) load_point(t + 1, xv);   // the next tile, behind this one's work
 
@@ -175,20 +179,18 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
             for (int v = 0; v < NV; ++v) wc[v] = wp[v];
             if (kk + 1 < KP / 4) load_panel(k + 1, wp);   // the next component's panel
             else if (t + 1 < t1) load_panel(4 * w, wp);  // the first one of the next tile
-            float bias[NOB][16];
+            f32x16 nb[NOB];   // -W mu: the accumulators start from it, so they end at W (x - mu)
 #pragma unroll
             for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    bias[ob][r] = wb_s[k][32 * ob + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
+                    nb[ob][r] = wb_s[k][32 * ob + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
             const float cvk = cv_s[k], hqk = hq_s[k];
 #pragma unroll 2
             for (int st = 0; st < T / 32; ++st) {
                 f32x16 acc[NOB];
 #pragma unroll
-                for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[ob][r] = 0.0f;
+                for (int ob = 0; ob < NOB; ++ob) acc[ob] = nb[ob];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const half8 xb = __builtin_bit_cast(
@@ -205,9 +207,8 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                 for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
                     for (int r = 0; r < 16; r += 2) {
-                        const float z0 = acc[ob][r] - bias[ob][r], z1 = acc[ob][r + 1] - bias[ob][r + 1];
-                        q0 = fmaf(z0, z0, q0);
-                        q1 = fmaf(z1, z1, q1);
+                        q0 = fmaf(acc[ob][r], acc[ob][r], q0);
+                        q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
                     }
                 float q = q0 + q1;
                 q += __shfl_xor(q, 32);
@@ -257,10 +258,14 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
 #pragma unroll 1
             for (int ks = 0; ks < T / 32; ++ks) {
                 const int pc = 32 * ks + 8 * g;   // this lane's 8 points of the K-step
+                // x of points pc..pc+7, dimension 16 bb + j: two transposed reads of the tile
                 uint4 xb[NB];
 #pragma unroll
-                for (int bb = 0; bb < NB; ++bb)
-                    xb[bb] = *reinterpret_cast<const uint4*>(&xt_s[16 * bb + j][pc]);
+                for (int bb = 0; bb < NB; ++bb) {
+                    const uint16_t* src = &xr_s[32 * ks + 8 * g + (j >> 2)][16 * bb + 4 * (j & 3)];
+                    const uint2 lo = tr16(src), hi = tr16(src + 4 * Sh::kXR);
+                    xb[bb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
                 if (w < NB) {   // s1 += gamma^T x over all components, dims 16w..16w+15
                     const float4 g0 = *reinterpret_cast<const float4*>(&g_s[j][pc]);
                     const float4 g1 = *reinterpret_cast<const float4*>(&g_s[j][pc + 4]);
@@ -278,10 +283,11 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                     half8 yc[NB], ya[NB];
 #pragma unroll
                     for (int bb = 0; bb < NB; ++bb) {
-                        const _Float16 m = __builtin_bit_cast(_Float16, mh_s[k][16 * bb + j]);
-                        const half8 xv = __builtin_bit_cast(half8, xb[bb]);
-                        yc[bb] = xv - m;      // (x - mu_k) in fp16, packed
-                        ya[bb] = yc[bb] * gh; // gamma (x - mu_k)
+                        const half2v nm = __builtin_bit_cast(half2v, nm_s[k][16 * bb + j]);
+                        const half8 x8 = __builtin_bit_cast(half8, xb[bb]);
+                        // x + (-mu): an add of the splatted pair stays on v_pk_add_f16
+                        yc[bb] = x8 + __builtin_shufflevector(nm, nm, 0, 1, 0, 1, 0, 1, 0, 1);
+                        ya[bb] = yc[bb] * gh;   // gamma (x - mu_k)
                     }
 #pragma unroll
                     for (int ab = 0; ab < NB; ++ab)
@@ -339,19 +345,26 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     if (tid == 0) part_ll[b] = red[0] * kLn2;
 }
 
+template <int DP, bool VEC>
+hipError_t launch_dv(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
+                     int* arg, hipStream_t s) {
+    if (em)
+        hipLaunchKernelGGL((k_full_fused<DP, true, VEC>), dim3(grid), dim3(256), 0, s,
+                           (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
+                           w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr);
+    else
+        hipLaunchKernelGGL((k_full_fused<DP, false, VEC>), dim3(grid), dim3(256), 0, s,
+                           (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
+                           w.cvec, w.rscale, w.part, w.part_ll, lse, arg);
+    return hipGetLastError();
+}
+
 template <int DP>
 hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
                      int* arg, hipStream_t s) {
-    const int vec = ((uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0) ? 1 : 0;
-    if (em)
-        hipLaunchKernelGGL((k_full_fused<DP, true>), dim3(grid), dim3(256), 0, s, (const _Float16*)x,
-                           p.n, (int)p.d, p.ldx, (int)p.k, vec, w.wpk, w.wbias, w.muh, w.cvec,
-                           w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr);
-    else
-        hipLaunchKernelGGL((k_full_fused<DP, false>), dim3(grid), dim3(256), 0, s, (const _Float16*)x,
-                           p.n, (int)p.d, p.ldx, (int)p.k, vec, w.wpk, w.wbias, w.muh, w.cvec,
-                           w.rscale, w.part, w.part_ll, lse, arg);
-    return hipGetLastError();
+    const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
+    return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, s)
+               : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, s);
 }
 
 }  // namespace

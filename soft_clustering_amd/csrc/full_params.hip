@@ -9,7 +9,7 @@
 // weight is treated as 0.  The forward solve L z = x - mu is carried out by
 // the fused kernel as a product with W = (L 2^-e_k)^{-1} (2^e_k near
 // sqrt(|tr C|/D)), which this kernel forms in fp64 (a triangular inverse,
-// one column per thread) and stores as a split fp16 panel (hi + lo, 22
+// one row per step) and stores as a split fp16 panel (hi + lo, 22
 // bits) with the bias W mu; log|C~| = 2 sum log L_ii from the fp64 factor.
 // The mean is also stored in fp16 as the centre of the second moments.
 // M-step ([Flash-GMM] Method): pi' = s0/N, mu' = s1/s0,
@@ -45,7 +45,9 @@ __global__ __launch_bounds__(256) void k_full_load(int k_real, int d, const floa
 }
 
 // One workgroup per padded component (256 threads).  The factorisation is
-// right-looking on the lower triangle of C~ (fp64, LDS), one column per step.
+// right-looking on the lower triangle of C~ (fp64), one column per step: each
+// thread holds its elements (ti + 16 a, tc + 16 b) in registers and the column
+// of each step is broadcast through LDS.
 template <int DP>
 __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridge_rel,
                                                    const float* pi, const float* mu,
@@ -54,23 +56,26 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                                                    int* flags) {
     constexpr int NOB = full_nob(DP), NKS = full_nks(DP), DPO = full_dpo(DP);
     constexpr int NV = 2 * NOB * NKS * 64;   // panel vectors per component
+    constexpr int RT = DP / 16;   // rows (and columns) of the matrix per thread
     __shared__ double A[DP][DP + 1];
     __shared__ double W[DP][DP + 1];
+    __shared__ double pinv[DP], mus[DP];
+    __shared__ double colv[2][DP], rowv[2][DP];   // broadcast column / row, double-buffered
     __shared__ double red[256];
-    __shared__ int fail;
     const int k = blockIdx.x, tid = threadIdx.x;
+    const int ti = tid / 16, tc = tid % 16;   // this thread's elements: (ti + 16 a, tc + 16 b)
     uint4* Wk = wpk + (int64_t)k * NV;
     auto put_identity = [&]() {   // a zero panel: the component is never scored (c_k = -inf)
         for (int i = tid; i < NV; i += 256) Wk[i] = make_uint4(0, 0, 0, 0);
         for (int i = tid; i < DPO; i += 256) wbias[k * DPO + i] = 0.0f;
-    };
-    if (k >= k_real) {   // padding component
-        put_identity();
         for (int i = tid; i < DP; i += 256) muh[k * DP + i] = 0.0f;
         if (tid == 0) {
             cvec[k] = -INFINITY;
             rscale[k] = 1.0f;
         }
+    };
+    if (k >= k_real) {   // padding component
+        put_identity();
         return;
     }
     const float* C = cov + (int64_t)k * d * d;
@@ -87,71 +92,136 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     double eps = (double)ridge_rel * scale;
     int attempt = 0;
     bool ok = false;
+    double Ar[RT][RT];
     for (; attempt <= kRidgeRetries; ++attempt) {
-        for (int i = tid; i < DP * DP; i += 256) {
-            const int r = i / DP, c = i % DP;
-            double v = 0.0;
-            if (c <= r) {
-                if (r < d) v = (double)C[(int64_t)r * d + c] + (r == c ? eps : 0.0);
-                else v = (r == c) ? 1.0 : 0.0;   // padded dimensions: identity
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int b2 = 0; b2 < RT; ++b2) {
+                const int r = ti + 16 * a, c = tc + 16 * b2;
+                double v = 0.0;
+                if (c <= r) {
+                    if (r < d) v = (double)C[(int64_t)r * d + c] + (r == c ? eps : 0.0);
+                    else v = (r == c) ? 1.0 : 0.0;   // padded dimensions: identity
+                }
+                Ar[a][b2] = v;
             }
-            A[r][c] = v;
+        if (tc == 0) {
+#pragma unroll
+            for (int a = 0; a < RT; ++a) colv[0][ti + 16 * a] = Ar[a][0];
         }
-        if (tid == 0) fail = 0;
-        __syncthreads();
+        // column jc is final after step jc - 1, so step jc reads it and updates only
+        // columns c > jc.  The columns are kept unscaled: L_ij = A_ij / sqrt(A_jj).
+        // The owners of column jc + 1 publish it (final after step jc) into the
+        // other half of the double buffer.
+        bool failed = false;
         for (int jc = 0; jc < DP; ++jc) {
-            if (tid == 0) {
-                const double piv = A[jc][jc];
-                if (!(piv > 0.0) || !isfinite(piv)) fail = 1;
-                else A[jc][jc] = sqrt(piv);
+            __syncthreads();
+            const double* cv = colv[jc & 1];
+            const double piv = cv[jc];   // read by every thread: the test is uniform
+            if (!(piv > 0.0) || !isfinite(piv)) {
+                failed = true;
+                break;
             }
-            __syncthreads();
-            if (fail) break;
-            const double ljj = A[jc][jc];
-            for (int i = jc + 1 + tid; i < DP; i += 256) A[i][jc] /= ljj;
-            __syncthreads();
-            // trailing update of the lower triangle: A[i][c] -= L[i][jc] L[c][jc], jc < c <= i
-            const int m = DP - jc - 1;
-            for (int q = tid; q < m * m; q += 256) {
-                const int i = jc + 1 + q / m, c = jc + 1 + q % m;
-                if (c <= i) A[i][c] -= A[i][jc] * A[c][jc];
+            const double rinv = 1.0 / piv;
+            double cc[RT];
+#pragma unroll
+            for (int b2 = 0; b2 < RT; ++b2) cc[b2] = cv[tc + 16 * b2];
+#pragma unroll
+            for (int a = 0; a < RT; ++a) {
+                const int i = ti + 16 * a;
+                if (i <= jc) continue;
+                const double f = cv[i] * rinv;
+#pragma unroll
+                for (int b2 = 0; b2 < RT; ++b2) {
+                    const int c = tc + 16 * b2;
+                    if (c > jc && c <= i) Ar[a][b2] -= f * cc[b2];
+                }
             }
-            __syncthreads();
+            const int jn = jc + 1;
+            if (jn < DP && tc == jn % 16) {
+#pragma unroll
+                for (int b2 = 0; b2 < RT; ++b2)
+                    if (b2 == jn / 16) {
+#pragma unroll
+                        for (int a = 0; a < RT; ++a) colv[jn & 1][ti + 16 * a] = Ar[a][b2];
+                    }
+            }
         }
-        if (!fail) {
+        __syncthreads();
+        if (!failed) {
             ok = true;
             break;
         }
         eps = fmax(10.0 * eps, kRidgeEscalate * scale);
-        __syncthreads();
     }
     if (!ok || bad > 0.0) {
         put_identity();
-        for (int i = tid; i < DP; i += 256) muh[k * DP + i] = 0.0f;
         if (tid == 0) {
-            cvec[k] = -INFINITY;
-            rscale[k] = 1.0f;
             flags[k] |= (bad > 0.0 ? 1 : 0) | (ok ? 0 : 2);
             flags[k_real + k] = attempt > kRidgeRetries ? kRidgeRetries : attempt;
         }
         return;
     }
-    // scale s = 2^-e with 2^e near sqrt(|tr| / D); W = (L s)^{-1} in fp64, one
-    // column per thread: W_jj = 1 / (L s)_jj, W_ij = -(sum_{m=j}^{i-1} (L s)_im W_mj) / (L s)_ii
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) A[ti + 16 * a][tc + 16 * b2] = Ar[a][b2];
+    // scale s = 2^-e with 2^e near sqrt(|tr| / D)
     int e = 0;
     if (scale > 0.0 && isfinite(scale)) {
         e = ilogb(sqrt(scale));
         e = e < -60 ? -60 : (e > 60 ? 60 : e);
     }
     const double sc = ldexp(1.0, -e);
-    for (int jc = tid; jc < DP; jc += 256) {
-        for (int i = 0; i < jc; ++i) W[i][jc] = 0.0;
-        W[jc][jc] = 1.0 / (A[jc][jc] * sc);
-        for (int i = jc + 1; i < DP; ++i) {
-            double acc = 0.0;
-            for (int m = jc; m < i; ++m) acc += A[i][m] * W[m][jc];
-            W[i][jc] = -(acc * sc) / (A[i][i] * sc);
+    // W = (L s)^{-1}, L = U D^{1/2} with U unit lower triangular (U_ij = A_ij / A_jj):
+    // W = s^-1 D^{-1/2} U^{-1}.  U^{-1} right-looking: R = I; at step i, row i of R
+    // is final and the rows below take R_r -= U_ri R_i (row i read, rows r > i written)
+    __syncthreads();
+    for (int i = tid; i < DP; i += 256) {
+        pinv[i] = 1.0 / A[i][i];
+        mus[i] = i < d ? (double)mu[(int64_t)k * d + i] : 0.0;
+    }
+    double Rr[RT][RT];
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) Rr[a][b2] = (ti + 16 * a == tc + 16 * b2) ? 1.0 : 0.0;
+    if (ti == 0) {
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) rowv[0][tc + 16 * b2] = Rr[0][b2];
+    }
+    for (int i = 0; i < DP - 1; ++i) {
+        __syncthreads();
+        const double* rv = rowv[i & 1];
+        double rr[RT];
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) rr[b2] = rv[tc + 16 * b2];
+#pragma unroll
+        for (int a = 0; a < RT; ++a) {
+            const int r = ti + 16 * a;
+            if (r <= i) continue;
+            const double u = A[r][i] * pinv[i];
+#pragma unroll
+            for (int b2 = 0; b2 < RT; ++b2)
+                if (tc + 16 * b2 <= i) Rr[a][b2] -= u * rr[b2];
         }
+        const int in = i + 1;   // row in is final after this step: publish it
+        if (ti == in % 16) {
+#pragma unroll
+            for (int a = 0; a < RT; ++a)
+                if (a == in / 16) {
+#pragma unroll
+                    for (int b2 = 0; b2 < RT; ++b2) rowv[in & 1][tc + 16 * b2] = Rr[a][b2];
+                }
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < RT; ++a) {
+        const int r = ti + 16 * a;
+        const double f = sqrt(pinv[r]) / sc;   // 1 / (sqrt(A_rr) s)
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) W[r][tc + 16 * b2] = Rr[a][b2] * f;
     }
     __syncthreads();
     // panel: out dimension o = 32 ob + l % 32 (rows), input i = 16 ks + 8 (l / 32) + q;
@@ -163,11 +233,11 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         for (int q2 = 0; q2 < 4; ++q2) {
             _Float16 h[2], lo[2];
             for (int t = 0; t < 2; ++t) {
-                const int i = 16 * ks + 8 * (l >> 5) + 2 * q2 + t;
-                const double wv = (o < d && i < d && i <= o) ? W[o][i] : 0.0;
-                const float f = (float)wv;
-                h[t] = (_Float16)f;
-                lo[t] = (_Float16)(f - (float)h[t]);
+                const int ic = 16 * ks + 8 * (l >> 5) + 2 * q2 + t;
+                const double wv = (o < d && ic < d && ic <= o) ? W[o][ic] : 0.0;
+                const float fv = (float)wv;
+                h[t] = (_Float16)fv;
+                lo[t] = (_Float16)(fv - (float)h[t]);
             }
             hw[q2] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
             lw[q2] = (uint32_t)__builtin_bit_cast(uint16_t, lo[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, lo[1]) << 16);
@@ -176,17 +246,16 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         Wk[NV / 2 + v] = make_uint4(lw[0], lw[1], lw[2], lw[3]);     // lo half
     }
     // bias W mu (fp64), the fp16 centre of the moments, log|C~| from the fp64 factor
-    double ld = 0.0;
     for (int o = tid; o < DPO; o += 256) {
-        double b = 0.0;
+        double bsum = 0.0;
         if (o < d)
-            for (int i = 0; i <= o; ++i) b += W[o][i] * (double)mu[(int64_t)k * d + i];
-        wbias[k * DPO + o] = (float)b;
+            for (int ic = 0; ic <= o; ++ic) bsum += W[o][ic] * mus[ic];
+        wbias[k * DPO + o] = (float)bsum;
     }
+    double ld = 0.0;
     for (int i = tid; i < DP; i += 256) {
-        if (i < d) ld += log(A[i][i]);
-        const float m = i < d ? mu[(int64_t)k * d + i] : 0.0f;
-        muh[k * DP + i] = (float)(_Float16)m;
+        if (i < d) ld += 0.5 * log(A[i][i]);   // log L_ii
+        muh[k * DP + i] = (float)(_Float16)(float)mus[i];
     }
     ld = block_sum_f64(ld, red);
     if (tid == 0) {
