@@ -25,6 +25,17 @@ namespace gmm {
 
 namespace {
 
+// 1 / x from the hardware estimate and two Newton steps (each doubles the
+// number of correct bits: about 2^-26 -> 2^-52 -> the last bit).  Used on the
+// factorisation's pivots; what it yields for a pivot that is not positive or
+// not finite is discarded, as the factorisation stops on such a pivot.
+__device__ __forceinline__ double recip_f64(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    r = fma(r, fma(-x, r, 1.0), r);
+    r = fma(r, fma(-x, r, 1.0), r);
+    return r;
+}
+
 constexpr int kRidgeRetries = 3;
 constexpr double kRidgeEscalate = 1e-3;   // escalation floor, relative to |tr C| / D
 
@@ -60,7 +71,8 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     __shared__ double A[DP][DP + 1];
     __shared__ double W[DP][DP + 1];
     __shared__ double pinv[DP], mus[DP];
-    __shared__ double colv[2][DP], rowv[2][DP];   // broadcast column / row, double-buffered
+    __shared__ double pan[2][4][DP];   // four broadcast columns (factorisation), double-buffered
+    __shared__ double rpan[2][4][DP];  // four broadcast rows (inverse), double-buffered
     __shared__ double red[256];
     const int k = blockIdx.x, tid = threadIdx.x;
     const int ti = tid / 16, tc = tid % 16;   // this thread's elements: (ti + 16 a, tc + 16 b)
@@ -79,13 +91,20 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         return;
     }
     const float* C = cov + (int64_t)k * d * d;
-    // |trace| / D and the bad-parameter check (non-finite entries of the lower triangle)
+    // this thread's elements of the lower triangle, |trace| / D and the
+    // bad-parameter check (non-finite entries of the lower triangle)
+    float Cr[RT][RT];
     double tr = 0.0, bad = 0.0;
-    for (int i = tid; i < d; i += 256) tr += (double)C[(int64_t)i * d + i];
-    for (int i = tid; i < d * d; i += 256) {
-        const int r = i / d, c = i % d;
-        if (c <= r && !isfinite(C[i])) bad = 1.0;
-    }
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) {
+            const int r = ti + 16 * a, c = tc + 16 * b2;
+            const bool in = c <= r && r < d;
+            Cr[a][b2] = in ? C[(int64_t)r * d + c] : 0.0f;
+            if (in && !isfinite(Cr[a][b2])) bad = 1.0;
+            if (in && r == c) tr += (double)Cr[a][b2];
+        }
     tr = block_sum_f64(tr, red);
     bad = block_sum_f64(bad, red);
     const double scale = fabs(tr) / (double)d;
@@ -101,50 +120,98 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                 const int r = ti + 16 * a, c = tc + 16 * b2;
                 double v = 0.0;
                 if (c <= r) {
-                    if (r < d) v = (double)C[(int64_t)r * d + c] + (r == c ? eps : 0.0);
+                    if (r < d) v = (double)Cr[a][b2] + (r == c ? eps : 0.0);
                     else v = (r == c) ? 1.0 : 0.0;   // padded dimensions: identity
                 }
                 Ar[a][b2] = v;
             }
-        if (tc == 0) {
+        // Blocked by 4 columns: step st takes columns J = 4 st .. 4 st + 3.  Every
+        // thread factors the 4 x 4 diagonal block itself (pivots p_t, multipliers
+        // l_tu = x'_u(j0 + t) / p_u), maps the panel values x_u(r) = A_r,j0+u of
+        // its rows and columns to x'(r) (x'_t = x_t - sum_{u<t} l_tu x'_u: what the
+        // four single-column steps would leave), and updates
+        // A_ic -= sum_t x'_t(i) x'_t(c) / p_t for c > j0 + 3, c <= i.  The owners
+        // of J keep x' (the unscaled factor: L_ij = x'_j(i) / sqrt(p_j)); the owners
+        // of the next four columns publish them (final at the start of the next
+        // step) into the other half of the double-buffered panel.
+        if (tc < 4) {
 #pragma unroll
-            for (int a = 0; a < RT; ++a) colv[0][ti + 16 * a] = Ar[a][0];
+            for (int a = 0; a < RT; ++a) pan[0][tc][ti + 16 * a] = Ar[a][0];
         }
-        // column jc is final after step jc - 1, so step jc reads it and updates only
-        // columns c > jc.  The columns are kept unscaled: L_ij = A_ij / sqrt(A_jj).
-        // The owners of column jc + 1 publish it (final after step jc) into the
-        // other half of the double buffer.
         bool failed = false;
-        for (int jc = 0; jc < DP; ++jc) {
+        for (int st = 0; st < DP / 4; ++st) {
+            const int j0 = 4 * st;
             __syncthreads();
-            const double* cv = colv[jc & 1];
-            const double piv = cv[jc];   // read by every thread: the test is uniform
-            if (!(piv > 0.0) || !isfinite(piv)) {
+            const double(*pv)[DP] = pan[st & 1];
+            double p[4], rp[4], l[4][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                double xs[4];
+#pragma unroll
+                for (int u = 0; u <= t; ++u) {
+                    double v = pv[u][j0 + t];
+#pragma unroll
+                    for (int w2 = 0; w2 < u; ++w2) v -= l[u][w2] * xs[w2];
+                    xs[u] = v;
+                    if (u < t) l[t][u] = v * rp[u];
+                }
+                p[t] = xs[t];
+                rp[t] = recip_f64(p[t]);
+            }
+            bool bad_piv = false;   // the same in every thread: the test is uniform
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bad_piv = bad_piv || !(p[t] > 0.0) || !isfinite(p[t]);
+            if (bad_piv) {
                 failed = true;
                 break;
             }
-            const double rinv = 1.0 / piv;
-            double cc[RT];
+            auto transform = [&](int r, double (&xo)[4]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int b2 = 0; b2 < RT; ++b2) cc[b2] = cv[tc + 16 * b2];
+                for (int u = 0; u < 4; ++u) {
+                    double v = pv[u][r];
+#pragma unroll
+                    for (int w2 = 0; w2 < u; ++w2) v -= l[u][w2] * xo[w2];
+                    xo[u] = v;
+                }
+            };
+            double xc[RT][4];
+#pragma unroll
+            for (int b2 = 0; b2 < RT; ++b2) transform(tc + 16 * b2, xc[b2]);
+            const int own_t = tc - (j0 & 15);   // column j0 + own_t is this thread's (0..3)
 #pragma unroll
             for (int a = 0; a < RT; ++a) {
                 const int i = ti + 16 * a;
-                if (i <= jc) continue;
-                const double f = cv[i] * rinv;
+                double xr[4];
+                transform(i, xr);
+                if (i > j0 + 3) {
+                    double g[4];
 #pragma unroll
-                for (int b2 = 0; b2 < RT; ++b2) {
-                    const int c = tc + 16 * b2;
-                    if (c > jc && c <= i) Ar[a][b2] -= f * cc[b2];
+                    for (int t = 0; t < 4; ++t) g[t] = xr[t] * rp[t];
+#pragma unroll
+                    for (int b2 = 0; b2 < RT; ++b2) {
+                        const int c = tc + 16 * b2;
+                        if (c > j0 + 3 && c <= i)
+                            Ar[a][b2] -= g[0] * xc[b2][0] + g[1] * xc[b2][1] + g[2] * xc[b2][2] +
+                                         g[3] * xc[b2][3];
+                    }
+                }
+                if (own_t >= 0 && own_t < 4 && i >= j0 + own_t) {
+                    double v = xr[0];
+#pragma unroll
+                    for (int t = 1; t < 4; ++t)
+                        if (own_t == t) v = xr[t];
+#pragma unroll
+                    for (int b2 = 0; b2 < RT; ++b2)
+                        if (b2 == j0 / 16) Ar[a][b2] = v;
                 }
             }
-            const int jn = jc + 1;
-            if (jn < DP && tc == jn % 16) {
+            const int jn = j0 + 4, nt = tc - (jn & 15);
+            if (jn < DP && nt >= 0 && nt < 4) {
 #pragma unroll
                 for (int b2 = 0; b2 < RT; ++b2)
                     if (b2 == jn / 16) {
 #pragma unroll
-                        for (int a = 0; a < RT; ++a) colv[jn & 1][ti + 16 * a] = Ar[a][b2];
+                        for (int a = 0; a < RT; ++a) pan[(st + 1) & 1][nt][ti + 16 * a] = Ar[a][b2];
                     }
             }
         }
@@ -175,8 +242,8 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     }
     const double sc = ldexp(1.0, -e);
     // W = (L s)^{-1}, L = U D^{1/2} with U unit lower triangular (U_ij = A_ij / A_jj):
-    // W = s^-1 D^{-1/2} U^{-1}.  U^{-1} right-looking: R = I; at step i, row i of R
-    // is final and the rows below take R_r -= U_ri R_i (row i read, rows r > i written)
+    // W = s^-1 D^{-1/2} U^{-1}.  U^{-1} right-looking from R = I: once row i of R is
+    // final, the rows below take R_r -= U_ri R_i.
     __syncthreads();
     for (int i = tid; i < DP; i += 256) {
         pinv[i] = 1.0 / A[i][i];
@@ -187,35 +254,69 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     for (int a = 0; a < RT; ++a)
 #pragma unroll
         for (int b2 = 0; b2 < RT; ++b2) Rr[a][b2] = (ti + 16 * a == tc + 16 * b2) ? 1.0 : 0.0;
-    if (ti == 0) {
+    // blocked by 4 rows: step st takes rows I = 4 st .. 4 st + 3 (their values y at
+    // the start of the step broadcast through rpan).  Every thread finishes the
+    // block rows for its columns (y'_t = y_t - sum_{w<t} U_{i0+t, i0+w} y'_w), the
+    // owners of I keep y', and the rows below take R_r -= sum_t U_{r, i0+t} y'_t.
+    if (ti < 4) {
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) rowv[0][tc + 16 * b2] = Rr[0][b2];
+        for (int b2 = 0; b2 < RT; ++b2) rpan[0][ti][tc + 16 * b2] = Rr[0][b2];
     }
-    for (int i = 0; i < DP - 1; ++i) {
+    for (int st = 0; st < DP / 4; ++st) {
+        const int i0 = 4 * st;
         __syncthreads();
-        const double* rv = rowv[i & 1];
-        double rr[RT];
+        const double(*rv)[DP] = rpan[st & 1];
+        double ub[4][4];   // U within the block
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) rr[b2] = rv[tc + 16 * b2];
+        for (int t = 1; t < 4; ++t)
+#pragma unroll
+            for (int w2 = 0; w2 < t; ++w2) ub[t][w2] = A[i0 + t][i0 + w2] * pinv[i0 + w2];
+        double yc[RT][4];
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) {
+            const int c = tc + 16 * b2;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                double v = rv[t][c];
+#pragma unroll
+                for (int w2 = 0; w2 < t; ++w2) v -= ub[t][w2] * yc[b2][w2];
+                yc[b2][t] = v;
+            }
+        }
+        const int own_t = ti - (i0 & 15);   // row i0 + own_t is this thread's (0..3)
 #pragma unroll
         for (int a = 0; a < RT; ++a) {
             const int r = ti + 16 * a;
-            if (r <= i) continue;
-            const double u = A[r][i] * pinv[i];
+            if (r > i0 + 3) {
+                double ur[4];
 #pragma unroll
-            for (int b2 = 0; b2 < RT; ++b2)
-                if (tc + 16 * b2 <= i) Rr[a][b2] -= u * rr[b2];
+                for (int t = 0; t < 4; ++t) ur[t] = A[r][i0 + t] * pinv[i0 + t];
+#pragma unroll
+                for (int b2 = 0; b2 < RT; ++b2)
+                    Rr[a][b2] -= ur[0] * yc[b2][0] + ur[1] * yc[b2][1] + ur[2] * yc[b2][2] +
+                                 ur[3] * yc[b2][3];
+            } else if (own_t >= 0 && own_t < 4 && a == i0 / 16) {
+#pragma unroll
+                for (int b2 = 0; b2 < RT; ++b2) {
+                    double v = yc[b2][0];
+#pragma unroll
+                    for (int t = 1; t < 4; ++t)
+                        if (own_t == t) v = yc[b2][t];
+                    Rr[a][b2] = v;
+                }
+            }
         }
-        const int in = i + 1;   // row in is final after this step: publish it
-        if (ti == in % 16) {
+        const int in = i0 + 4, nt = ti - (in & 15);
+        if (in < DP && nt >= 0 && nt < 4) {
 #pragma unroll
             for (int a = 0; a < RT; ++a)
                 if (a == in / 16) {
 #pragma unroll
-                    for (int b2 = 0; b2 < RT; ++b2) rowv[in & 1][tc + 16 * b2] = Rr[a][b2];
+                    for (int b2 = 0; b2 < RT; ++b2) rpan[(st + 1) & 1][nt][tc + 16 * b2] = Rr[a][b2];
                 }
         }
     }
+    __syncthreads();
 #pragma unroll
     for (int a = 0; a < RT; ++a) {
         const int r = ti + 16 * a;
