@@ -141,7 +141,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_cov = take(sizeof(float) * p->k * p->d * p->d);
         p->off_panel = take(sizeof(uint4) * full_w_vecs(dp));
         p->off_shift = take(sizeof(float) * (kFullKP * full_dpo(dp) + kFullKP * dp + 2 * kFullKP));
-        p->off_part = take(sizeof(double) * (size_t)p->p_max * kFullKP * ncolp);
+        p->off_part = take(sizeof(float) * (size_t)p->p_max * kFullKP * ncolp);
         p->off_part_ll = take(sizeof(double) * kFullLLSlots);
         p->off_chunk = take(sizeof(double) * p->k * ncolp);
         p->off_stats = take(sizeof(double) * p->k * p->ncols);

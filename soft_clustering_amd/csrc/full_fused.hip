@@ -70,7 +70,7 @@ template <int DP, bool EM, bool VEC>
 __global__ __launch_bounds__(256, 1) void k_full_fused(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
-    const float* __restrict__ cvec, const float* __restrict__ rscale, double* __restrict__ part,
+    const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
     double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
     using Sh = FullShape<DP>;
     constexpr int NB = Sh::kNB, NBLK = Sh::kNBlk;
@@ -304,20 +304,20 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     __syncthreads();
     if constexpr (EM) {
         const int ncolp = 1 + d + d * (d + 1) / 2;
-        double* dst = part + (int64_t)b * KP * ncolp;
+        float* dst = part + (int64_t)b * KP * ncolp;   // fp32: the accumulators' own precision
 #pragma unroll
         for (int k = 0; k < KP; ++k) g_s[k][tid] = s0acc[k];
         __syncthreads();
         if (tid < KP) {
             double s = 0.0;
             for (int i = 0; i < T; ++i) s += (double)g_s[tid][i];
-            dst[(int64_t)tid * ncolp] = s;
+            dst[(int64_t)tid * ncolp] = (float)s;
         }
         if (w < NB) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int k = 4 * g + r, dd = 16 * w + j;
-                if (dd < d) dst[(int64_t)k * ncolp + 1 + dd] = (double)acc1[r];
+                if (dd < d) dst[(int64_t)k * ncolp + 1 + dd] = acc1[r];
             }
         }
 #pragma unroll
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                         const int row = 16 * ab + 4 * g + r, col = 16 * bb + j;
                         if (row >= col && row < d)
                             dst[(int64_t)k * ncolp + 1 + d + tri_idx(row, col)] =
-                                (double)acc2[kk][blk_index(ab, bb)][r];
+                                acc2[kk][blk_index(ab, bb)][r];
                     }
         }
     }

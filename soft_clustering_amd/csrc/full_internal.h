@@ -32,7 +32,8 @@ struct FullWs {
     float* muh;                // [KP][DP] fp16-rounded mean, as fp32 (centre of the moments)
     float* cvec;               // [KP] base-2 constant log2 pi - 1/2 log2 e (D log 2pi + log|C|)
     float* rscale;             // [KP] 2^-e_k: |z|^2 = 2^-2e_k |W x - W mu|^2
-    double *part, *part_ll;    // per-workgroup partials [P][KP][ncolp], [P]
+    float* part;               // per-workgroup partials [P][KP][ncolp] (fp32 accumulators)
+    double* part_ll;           // [P]
     double *colsum;            // [K][ncolp] reduced partials
     double *stats, *ll;        // [K][1 + D + D*D] raw statistics (full matrices), LL
     int* flags;                // [K] flags, [K] ridge retries, misc[0] non-finite LL
@@ -51,7 +52,7 @@ inline FullWs full_ws(const Plan& p, char* ws) {
     w.muh = w.wbias + kFullKP * full_dpo(p.dp);
     w.cvec = w.muh + kFullKP * p.dp;
     w.rscale = w.cvec + kFullKP;
-    w.part = (double*)(ws + p.off_part);
+    w.part = (float*)(ws + p.off_part);
     w.part_ll = (double*)(ws + p.off_part_ll);
     w.colsum = (double*)(ws + p.off_chunk);
     w.stats = (double*)(ws + p.off_stats);

@@ -369,24 +369,33 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     }
 }
 
-// Column sums of the partials over the workgroups, fixed order.  Grid
-// (ceil(ncolp / 256), K).
-__global__ __launch_bounds__(256) void k_full_reduce(const double* __restrict__ part, int P,
+// Column sums (fp64) of the fp32 partials over the workgroups, fixed order.
+// Grid (ceil(ncolp / 64), K); thread (c, q) of a workgroup sums the quarter q of
+// the workgroups for column c in four interleaved chains, and the quarters are
+// added in a fixed order.
+__global__ __launch_bounds__(256) void k_full_reduce(const float* __restrict__ part, int P,
                                                      int ncolp, double* __restrict__ colsum) {
-    const int k = blockIdx.y, col = blockIdx.x * 256 + threadIdx.x;
-    if (col >= ncolp) return;
-    const double* src = part + (int64_t)k * ncolp + col;
+    __shared__ double qs[4][64];
+    const int k = blockIdx.y, c = threadIdx.x % 64, q = threadIdx.x / 64;
+    const int col = blockIdx.x * 64 + c;
     const int64_t stride = (int64_t)kFullKP * ncolp;
+    const int pq = (P + 3) / 4, p0 = q * pq, p1 = p0 + pq < P ? p0 + pq : P;
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int q = 0;
-    for (; q + 3 < P; q += 4) {
-        a0 += src[(int64_t)q * stride];
-        a1 += src[(int64_t)(q + 1) * stride];
-        a2 += src[(int64_t)(q + 2) * stride];
-        a3 += src[(int64_t)(q + 3) * stride];
+    if (col < ncolp) {
+        const float* src = part + (int64_t)k * ncolp + col;
+        int i = p0;
+        for (; i + 3 < p1; i += 4) {
+            a0 += (double)src[(int64_t)i * stride];
+            a1 += (double)src[(int64_t)(i + 1) * stride];
+            a2 += (double)src[(int64_t)(i + 2) * stride];
+            a3 += (double)src[(int64_t)(i + 3) * stride];
+        }
+        for (; i < p1; ++i) a0 += (double)src[(int64_t)i * stride];
     }
-    for (; q < P; ++q) a0 += src[(int64_t)q * stride];
-    colsum[(int64_t)k * ncolp + col] = (a0 + a1) + (a2 + a3);
+    qs[q][c] = (a0 + a1) + (a2 + a3);
+    __syncthreads();
+    if (q == 0 && col < ncolp)
+        colsum[(int64_t)k * ncolp + col] = (qs[0][c] + qs[1][c]) + (qs[2][c] + qs[3][c]);
 }
 
 // M-step per component (grid K, 256 threads) and the raw statistics
@@ -503,7 +512,7 @@ gmm_status full_finalize(const Plan& p, char* ws, float* pi, float* mu, float* c
     FullWs w = full_ws(p, ws);
     const int G = full_grid(p);
     const int ncolp = (int)full_ncolp(p.d);
-    hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 255) / 256, p.k), dim3(256), 0, s, w.part, G,
+    hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 63) / 64, p.k), dim3(256), 0, s, w.part, G,
                        ncolp, w.colsum);
     hipLaunchKernelGGL(k_full_mstep, dim3(p.k), dim3(256), 0, s, w.colsum, p.n, (int)p.d, p.dp,
                        w.muh, w.stats, w.pi, w.mu, w.cov, pi, mu, cov, w.flags);
