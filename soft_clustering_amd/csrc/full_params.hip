@@ -317,13 +317,34 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         }
     }
     __syncthreads();
+    // W = (L s)^{-1}; where its largest entry would leave the range the fp16
+    // panel holds comfortably (above 2^14: a covariance far wider in one
+    // direction than its mean variance suggests), s grows by the power of two
+    // that brings the largest entry into [2^13, 2^14)
+    double wmax = 0.0;
 #pragma unroll
     for (int a = 0; a < RT; ++a) {
         const int r = ti + 16 * a;
         const double f = sqrt(pinv[r]) / sc;   // 1 / (sqrt(A_rr) s)
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) W[r][tc + 16 * b2] = Rr[a][b2] * f;
+        for (int b2 = 0; b2 < RT; ++b2) {
+            Rr[a][b2] *= f;
+            wmax = fmax(wmax, fabs(Rr[a][b2]));
+        }
     }
+    red[tid] = wmax;
+    __syncthreads();
+    for (int s2 = 128; s2 > 0; s2 >>= 1) {
+        if (tid < s2) red[tid] = fmax(red[tid], red[tid + s2]);
+        __syncthreads();
+    }
+    wmax = red[0];
+    const int e2 = (wmax > 16384.0 && isfinite(wmax)) ? ilogb(wmax) - 13 : 0;
+    const double sc2 = ldexp(sc, e2), wf = ldexp(1.0, -e2);
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) W[ti + 16 * a][tc + 16 * b2] = Rr[a][b2] * wf;
     __syncthreads();
     // panel: out dimension o = 32 ob + l % 32 (rows), input i = 16 ks + 8 (l / 32) + q;
     // zero outside the D x D lower triangle; hi = fp16(w), lo = fp16(w - hi)
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         const double logdet = 2.0 * ld;
         const double lp = log((double)pi[k]);
         cvec[k] = (float)(kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logdet)));
-        rscale[k] = (float)sc;
+        rscale[k] = (float)sc2;
         if (bad > 0.0) flags[k] |= 1;
         flags[k_real + k] = attempt;
     }

@@ -219,6 +219,28 @@ def test_ridge_retry_and_not_pd(gmm_lib):
     assert metrics.rel(ll_b, ll_ref) <= LL_TOL
 
 
+def test_thin_component_whitening_range(gmm_lib):
+    """A component whose variance in one direction is 1e-12 of the others
+    (ridge_rel = 0, so nothing widens it): its inverse factor relative to the
+    mean scale reaches about 1e6, beyond fp16, and the preparation rescales
+    the whitening panel into range.  LL (E-step and E+M) against the oracle
+    with the same ridge."""
+    n, d, k = 3000, 16, 3
+    xd, xg, ldx, (pi0, mu0, cov0) = _make(n, d, k, 0, False, seed=23)
+    dv = np.ones(d)
+    dv[6] = 1e-12
+    cov0[1] = np.diag(dv).astype(np.float32)
+    th = to_dev(pi0, mu0, cov0)
+    gm = gmm_lib.Gmm(n, d, k, "full", "f16", ridge_rel=0.0)
+    ll_e, _, _ = gpu_loglik(gm, xg, th)
+    ll_ref, _, _ = oracle.loglik(xd, params64("full", *th), ridge_rel=0.0)
+    print("thin component LL gpu", ll_e, "oracle", ll_ref, flush=True)
+    assert np.isfinite(ll_e) and metrics.rel(ll_e, ll_ref) <= LL_TOL
+    ll, st, th1 = gpu_step(gm, xg, *th)
+    ref = oracle.em_step(xd, params64("full", *th), ridge_rel=0.0)
+    assert metrics.rel(ll, ref.ll) <= LL_TOL
+
+
 def test_single_component_closed_form(gmm_lib):
     """K = 1: mu' is the sample mean and C' the population covariance."""
     rng = np.random.default_rng(22)
