@@ -345,6 +345,315 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     if (tid == 0) part_ll[b] = red[0] * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// D = 64: a two-stage pipeline over 256-point tiles in one workgroup of 12
+// waves (three per SIMD).  Waves 0..3 whiten tile i (components 4w..4w+3, as
+// above) and stage tile i + 1 into LDS; waves 4..11 take tile i - 1: every one
+// forms the base-2 log-sum-exp of all 256 points from the 16 scores, keeps the
+// responsibilities of its two components (2v, 2v + 1) in a private LDS row, and
+// accumulates their first and second moments.  One barrier per tile; three tile
+// buffers (the whitened tile, the tile of the moments, the tile being staged)
+// and two score buffers.  A SIMD thus holds one whitening wave and two moment
+// waves, whose vector and matrix work overlap.
+namespace pipe {
+constexpr int kWaves = 12;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kP1 = 256;                 // threads of the whitening stage
+constexpr int DP = 64, NB = 4, NBLK = 10, NOB = 2, NKS = 4, DPO = 64, NV = 16;
+constexpr int kGS = T + 4;
+// 16-byte unit u of tile row r sits at unit u ^ ((r >> 1) & 7): 16 consecutive
+// rows read at one logical unit fall on 16 distinct (bank half, unit) pairs
+__device__ __forceinline__ int xoff(int r, int u) { return r * DP + 8 * (u ^ ((r >> 1) & 7)); }
+}  // namespace pipe
+
+template <bool EM>
+__global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
+    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
+    const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
+    const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
+    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
+    using namespace pipe;
+    __shared__ __attribute__((aligned(16))) uint32_t nm_s[KP][DP];     // (-mu, -mu) fp16 pairs
+    __shared__ __attribute__((aligned(16))) float wb_s[KP][NOB][2][16];  // -W mu, accumulator layout
+    __shared__ float cv_s[KP], hq_s[KP];
+    __shared__ __attribute__((aligned(16))) float g_s[2][KP][kGS];     // scores of two tiles
+    __shared__ __attribute__((aligned(16))) uint16_t xr_s[3][T * DP];  // three tiles, swizzled
+    __shared__ __attribute__((aligned(16))) float gp_s[EM ? 8 : 1][2][kGS];   // gamma, per moment wave
+    __shared__ double red[T];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+    const bool p1 = w < 4;
+    const int v = w - 4;   // moment wave index (0..7)
+
+    for (int i = tid; i < KP * DP; i += kThreads) {
+        const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-muh[i]));
+        nm_s[i / DP][i % DP] = h | (h << 16);
+    }
+    for (int i = tid; i < KP * NOB * 32; i += kThreads) {
+        const int k = i / (NOB * 32), ob = (i / 32) % NOB, hh = (i / 16) % 2, r = i % 16;
+        wb_s[k][ob][hh][r] = -wbias[k * DPO + 32 * ob + 8 * (r >> 2) + 4 * hh + (r & 3)];
+    }
+    if (tid < KP) {
+        const float rs = rscale[tid];
+        cv_s[tid] = cvec[tid];
+        hq_s[tid] = kHalfLog2e * rs * rs;
+    }
+
+    const int G = gridDim.x;
+    const int64_t tiles = (n + T - 1) / T;
+    const int64_t tb = tiles / G, tr = tiles % G;
+    const int b = blockIdx.x;
+    const int64_t t0 = b * tb + (b < tr ? b : tr);
+    const int nt = (int)(tb + (b < tr ? 1 : 0));
+
+    // the whitening stage's point loads: thread tid < 256 holds point tid of a tile
+    uint4 xv[8];
+    auto load_point = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t p = t * T + tid;
+        const bool valid = p < n;
+        const _Float16* row = x + (valid ? p : 0) * ldx;
+        const int cmax = d / 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint4 vv = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
+            const uint32_t m = (valid && c < cmax) ? ~0u : 0u;
+            xv[c] = make_uint4(vv.x & m, vv.y & m, vv.z & m, vv.w & m);
+        }
+    };
+    auto store_point = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(&xr_s[buf][xoff(tid, c)]) = xv[c];
+    };
+
+    if (p1) {
+        // ---- whitening stage: stages tile it + 1, loads tile it + 2, whitens tile it
+        if (nt > 0) {
+            load_point(t0);
+            store_point(0);
+            if (nt > 1) load_point(t0 + 1);
+        }
+        __syncthreads();
+        for (int it = 0; it <= nt; ++it) {
+            if (it < nt) {
+                if (it + 1 < nt) store_point((it + 1) % 3);
+                if (it + 2 < nt) load_point(t0 + it + 2);
+                const uint16_t* xt = xr_s[it % 3];
+                float(*gs)[kGS] = g_s[it & 1];
+#pragma unroll 1
+                for (int kk = 0; kk < KP / 4; ++kk) {
+                    const int k = 4 * w + kk;
+                    half8 wp[NV];
+#pragma unroll
+                    for (int vv = 0; vv < NV; ++vv) {
+                        const int ks = vv % NKS, ob = (vv / NKS) % NOB;
+                        if (ks > 2 * ob + 1) continue;   // above the diagonal
+                        wp[vv] = __builtin_bit_cast(half8, wpk[((int64_t)k * NV + vv) * 64 + lane]);
+                    }
+                    const float cvk = cv_s[k], hqk = hq_s[k];
+#pragma unroll 1
+                    for (int st = 0; st < T / 32; ++st) {
+                        __asm__ volatile("" ::: "memory");   // -W mu re-read per block
+                        f32x16 acc[NOB];
+#pragma unroll
+                        for (int ob = 0; ob < NOB; ++ob)
+                            acc[ob] = *reinterpret_cast<const f32x16*>(&wb_s[k][ob][lane >> 5][0]);
+                        const int row = 32 * st + (lane & 31);
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            const half8 xb = __builtin_bit_cast(
+                                half8, *reinterpret_cast<const uint4*>(&xt[xoff(row, 2 * ks + (lane >> 5))]));
+#pragma unroll
+                            for (int ob = 0; ob < NOB; ++ob) {
+                                if (ks > 2 * ob + 1) continue;
+                                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wp[ob * NKS + ks], xb, acc[ob], 0, 0, 0);
+                                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wp[(NOB + ob) * NKS + ks], xb, acc[ob], 0, 0, 0);
+                            }
+                        }
+                        float q0 = 0.0f, q1 = 0.0f;
+#pragma unroll
+                        for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                            for (int r = 0; r < 16; r += 2) {
+                                q0 = fmaf(acc[ob][r], acc[ob][r], q0);
+                                q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
+                            }
+                        float q = q0 + q1;
+                        q += __shfl_xor(q, 32);
+                        if (lane < 32) gs[k][32 * st + lane] = cvk - hqk * q;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- moment stage: tile it - 1 (accumulators live only in these waves)
+    f32x4 acc2[EM ? 2 : 1][EM ? NBLK : 1];
+    f32x4 acc1[EM ? NB : 1];
+    float s0r[2] = {0.0f, 0.0f};
+    if constexpr (EM) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int q = 0; q < NBLK; ++q) acc2[c][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) acc1[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    double ll = 0.0;
+    __syncthreads();
+    for (int it = 0; it <= nt; ++it) {
+        if (it >= 1) {
+            const int jt = it - 1;                  // tile of this stage
+            const int64_t tt = t0 + jt;
+            const uint16_t* xt = xr_s[jt % 3];
+            const float(*gs)[kGS] = g_s[jt & 1];
+            // base-2 LSE of the 256 points (4 per lane); gamma of components 2v, 2v + 1
+#pragma unroll 1
+            for (int m = 0; m < 4; ++m) {
+                const int pt = lane + 64 * m;
+                const int64_t p = tt * T + pt;
+                const bool valid = p < n;
+                float sv[KP];
+                float M = -INFINITY;
+#pragma unroll
+                for (int k = 0; k < KP; ++k) {
+                    sv[k] = gs[k][pt];
+                    M = fmaxf(M, sv[k]);
+                }
+                const float Ms = M == -INFINITY ? 0.0f : M;
+                float Z = 0.0f;
+#pragma unroll
+                for (int k = 0; k < KP; ++k) Z += fast_exp2(sv[k] - Ms);
+                const float lse2 = Ms + fast_log2(Z);
+                if (v == 0 && valid) ll += (double)lse2;
+                if constexpr (EM) {
+                    const float lsafe = lse2 == -INFINITY ? INFINITY : lse2;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const float svc = gs[2 * v + c][pt];   // read again: sv[] is dead by now
+                        const float gk = valid ? fast_exp2(svc - lsafe) : 0.0f;
+                        s0r[c] += gk;
+                        gp_s[v][c][pt] = gk;
+                    }
+                } else if (v == 0 && valid) {
+                    if (out_lse) out_lse[p] = lse2 * kLn2f;
+                    if (out_arg) {
+                        int a = 0;
+#pragma unroll
+                        for (int k = KP - 1; k >= 0; --k)
+                            if (sv[k] == M) a = k;
+                        out_arg[p] = a;
+                    }
+                }
+            }
+            if constexpr (EM) {
+                // this wave's gamma row is read back by its own lanes: LDS operations of
+                // one wave complete in order
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+                for (int ks = 0; ks < T / 32; ++ks) {
+                    const int pc = 32 * ks + 8 * g;   // this lane's 8 points of the K-step
+                    uint4 xb[NB];
+#pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) {
+                        const int r0 = 32 * ks + 8 * g + (j >> 2), cu = 2 * bb + ((j & 3) >> 1);
+                        const int co = 4 * (j & 1);   // halves within the 16-byte unit
+                        const uint2 lo = tr16(&xt[xoff(r0, cu) + co]);
+                        const uint2 hi = tr16(&xt[xoff(r0 + 4, cu) + co]);
+                        xb[bb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    }
+                    {   // s1 of components 2v, 2v + 1: rows 0, 1 of gamma^T x (rows 2.. zero)
+                        half8 ga = {0, 0, 0, 0, 0, 0, 0, 0};
+                        if (j < 2) {
+                            const float4 g0 = *reinterpret_cast<const float4*>(&gp_s[v][j][pc]);
+                            const float4 g1 = *reinterpret_cast<const float4*>(&gp_s[v][j][pc + 4]);
+                            ga = half8{(_Float16)g0.x, (_Float16)g0.y, (_Float16)g0.z, (_Float16)g0.w,
+                                       (_Float16)g1.x, (_Float16)g1.y, (_Float16)g1.z, (_Float16)g1.w};
+                        }
+#pragma unroll
+                        for (int bb = 0; bb < NB; ++bb)
+                            acc1[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga, __builtin_bit_cast(half8, xb[bb]),
+                                                                            acc1[bb], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        __asm__ volatile("" ::: "memory");   // one component's operands at a time
+                        const int k = 2 * v + c;
+                        const float4 g0 = *reinterpret_cast<const float4*>(&gp_s[v][c][pc]);
+                        const float4 g1 = *reinterpret_cast<const float4*>(&gp_s[v][c][pc + 4]);
+                        const half8 gh = {(_Float16)g0.x, (_Float16)g0.y, (_Float16)g0.z, (_Float16)g0.w,
+                                          (_Float16)g1.x, (_Float16)g1.y, (_Float16)g1.z, (_Float16)g1.w};
+                        half8 yc[NB];
+#pragma unroll
+                        for (int bb = 0; bb < NB; ++bb) {
+                            const half2v nm = __builtin_bit_cast(half2v, nm_s[k][16 * bb + j]);
+                            yc[bb] = __builtin_bit_cast(half8, xb[bb]) +
+                                     __builtin_shufflevector(nm, nm, 0, 1, 0, 1, 0, 1, 0, 1);
+                        }
+#pragma unroll
+                        for (int ab = 0; ab < NB; ++ab) {
+                            const half8 ya = yc[ab] * gh;   // gamma (x - mu_k)
+#pragma unroll
+                            for (int bb = 0; bb <= ab; ++bb)
+                                acc2[c][blk_index(ab, bb)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    ya, yc[bb], acc2[c][blk_index(ab, bb)], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: per-workgroup partials [KP][1 + D + D(D+1)/2], one writer each
+    if constexpr (EM) {
+        if (!p1) {
+            const int ncolp = 1 + d + d * (d + 1) / 2;
+            float* dst = part + (int64_t)b * KP * ncolp;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float sv0 = s0r[c];
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) sv0 += __shfl_xor(sv0, o);
+                if (lane == 0) dst[(int64_t)(2 * v + c) * ncolp] = sv0;
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int dd = 16 * bb + j;
+                        if (dd < d) dst[(int64_t)(2 * v + r) * ncolp + 1 + dd] = acc1[bb][r];
+                    }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int k = 2 * v + c;
+#pragma unroll
+                for (int ab = 0; ab < NB; ++ab)
+#pragma unroll
+                    for (int bb = 0; bb <= ab; ++bb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = 16 * ab + 4 * g + r, col = 16 * bb + j;
+                            if (row >= col && row < d)
+                                dst[(int64_t)k * ncolp + 1 + d + tri_idx(row, col)] =
+                                    acc2[c][blk_index(ab, bb)][r];
+                        }
+            }
+        }
+    }
+    // LL: moment wave 0 holds it
+    if (w == 4) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ll += __shfl_xor(ll, o);
+        if (lane == 0) part_ll[b] = ll * kLn2;
+    }
+}
+
 template <int DP, bool VEC>
 hipError_t launch_dv(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
                      int* arg, hipStream_t s) {
@@ -363,6 +672,17 @@ template <int DP>
 hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
                      int* arg, hipStream_t s) {
     const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
+    if (DP == 64 && vec) {   // the pipelined kernel
+        if (em)
+            hipLaunchKernelGGL((k_full_pipe<true>), dim3(grid), dim3(pipe::kThreads), 0, s,
+                               (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
+                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr);
+        else
+            hipLaunchKernelGGL((k_full_pipe<false>), dim3(grid), dim3(pipe::kThreads), 0, s,
+                               (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
+                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, lse, arg);
+        return hipGetLastError();
+    }
     return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, s)
                : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, s);
 }
