@@ -450,7 +450,7 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                         wp[vv] = __builtin_bit_cast(half8, wpk[((int64_t)k * NV + vv) * 64 + lane]);
                     }
                     const float cvk = cv_s[k], hqk = hq_s[k];
-#pragma unroll 1
+#pragma unroll 2
                     for (int st = 0; st < T / 32; ++st) {
                         __asm__ volatile("" ::: "memory");   // -W mu re-read per block
                         f32x16 acc[NOB];
