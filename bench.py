@@ -61,8 +61,8 @@ TRAFFIC = {
         sources="ce19b0a7f4b0509a", fetch_kib=113572333.8, write_kib=4044007.5,
         copy_bytes=51.2e9, copy_fetch_kib=25000258.125, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="394ead4f32243a26", fetch_kib=63521.0, write_kib=34404.8,
-        copy_bytes=128e6, copy_fetch_kib=62515.0, copy_write_kib=125000.0),
+        sources="ea7527334556e7ac", fetch_kib=64063.7, write_kib=36283.3,
+        copy_bytes=128e6, copy_fetch_kib=62514.9375, copy_write_kib=125000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
 FAMILY_SOURCES = {
@@ -220,7 +220,7 @@ def main(argv=None):
     if fp32_path:
         kname = "k_diag_split (+ k_sum_ll)"
     elif full_path:
-        kname = "k_full_fused (+ k_full_sum_ll)"
+        kname = ("k_full_pipe (+ k_full_sum_ll)" if w.d > 32 else "k_full_fused (+ k_full_sum_ll)")
     elif w.k <= 256:
         kname = "k_lk<fused E+M> (+ k_lk_scan, k_lk_centre, k_lk_panel, k_lk_sum)"
     else:

@@ -14,8 +14,11 @@
 // (v_mfma_f32_16x16x32_f16) with fp32 accumulation; the M-step turns them into
 // raw moments and the new covariance in fp64.
 //
-// Work split: a workgroup of 256 threads takes 256-point tiles.  Each thread
-// loads one point into a row-major and a transposed LDS copy of the tile.
+// Work split (k_full_fused, any D): a workgroup of 256 threads takes 256-point
+// tiles.  At D = 64 with aligned X, k_full_pipe below splits the same work
+// between whitening waves and moment waves instead.  Each thread
+// loads one point into the row-major LDS tile (the moments read it
+// transposed, with ds_read_b64_tr_b16).
 // Phase 1: wave w whitens the tile against components 4w..4w+3 (the
 // component's panel in registers, the next component's panel loading behind
 // it), writing the base-2 scores to LDS.  Then each thread forms the
