@@ -142,6 +142,8 @@ CASES = [
     (4097, 64, 16, 0, False),
     (3000, 64, 7, 8, False),
     (2500, 48, 12, 0, True),
+    (100, 64, 16, 0, False),     # one tile: the two-stage kernel's prologue and drain only
+    (700, 56, 9, 0, False),      # D < 64 on the two-stage kernel (aligned rows)
 ]
 
 
