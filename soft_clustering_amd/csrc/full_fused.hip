@@ -481,7 +481,11 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                                 q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
                             }
                         float q = q0 + q1;
-                        q += __shfl_xor(q, 32);
+                        {   // lanes l < 32 add lane l + 32's half (a cross-half swap, no LDS trip)
+                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q),
+                                                                             false, false);
+                            q += __uint_as_float(sw[1]);
+                        }
                         if (lane < 32) gs[k][32 * st + lane] = cvk - hqk * q;
                     }
                 }
