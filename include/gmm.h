@@ -105,8 +105,9 @@ gmm_status gmm_workspace_bytes(const gmm_desc* desc, size_t* bytes /* host */);
 
 /* Load parameters theta = (pi, mu, cov) and precompute per-component
  * quantities ([LP-GMM] 3.1, Preprocess kernel): log-normaliser, precisions
- * and the score panel; for full covariance the ridged Cholesky factor L
- * ([LP-GMM] 1.2 route 2, 4.1).  pi/mu/cov are device fp32; they are copied,
+ * and the score panel; for full covariance the ridged Cholesky factor L and
+ * its inverse, which the E-step applies to x - mu in place of the forward
+ * solve ([LP-GMM] 1.2 route 2, 4.1).  pi/mu/cov are device fp32; they are copied,
  * so the caller may reuse them after the call is stream-ordered. */
 gmm_status gmm_prepare(const gmm_desc* desc, void* ws, size_t ws_bytes,
                        const float* pi, const float* mu, const float* cov,

@@ -1,6 +1,7 @@
-"""Parity of the full-covariance HIP path (X, mu and the Cholesky factor
-stored in fp16; forward solve, exp / log / normalisers and statistics in
-fp32) against the fp64 oracle.
+"""Parity of the full-covariance HIP path (X stored in fp16; the inverse
+Cholesky factor as an fp16 hi + lo pair, whitening and second moments on fp16
+MFMA with fp32 accumulation; exp / log / normalisers in fp32) against the
+fp64 oracle.
 
 Gate for reduced-precision storage (the operator write-up's acceptance bar,
 section 2.3): LL(theta_t) relative error <= 9e-3 and argmax agreement
