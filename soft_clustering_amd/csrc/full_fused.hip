@@ -381,7 +381,7 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     __shared__ float cv_s[KP], hq_s[KP];
     __shared__ __attribute__((aligned(16))) float g_s[2][KP][kGS];     // scores of two tiles
     __shared__ __attribute__((aligned(16))) uint16_t xr_s[3][T * DP];  // three tiles, swizzled
-    __shared__ __attribute__((aligned(16))) float gp_s[EM ? 8 : 1][2][kGS];   // gamma, per moment wave
+    __shared__ __attribute__((aligned(16))) uint16_t gp_s[EM ? 8 : 1][2][T + 8];   // fp16 gamma, per moment wave
     __shared__ double red[T];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                         const float svc = gs[2 * v + c][pt];   // read again: sv[] is dead by now
                         const float gk = valid ? fast_exp2(svc - lsafe) : 0.0f;
                         s0r[c] += gk;
-                        gp_s[v][c][pt] = gk;
+                        gp_s[v][c][pt] = __builtin_bit_cast(uint16_t, (_Float16)gk);   // the MFMA operand
                     }
                 } else if (v == 0 && valid) {
                     if (out_lse) out_lse[p] = lse2 * kLn2f;
@@ -574,12 +574,7 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                     }
                     {   // s1 of components 2v, 2v + 1: rows 0, 1 of gamma^T x (rows 2.. zero)
                         half8 ga = {0, 0, 0, 0, 0, 0, 0, 0};
-                        if (j < 2) {
-                            const float4 g0 = *reinterpret_cast<const float4*>(&gp_s[v][j][pc]);
-                            const float4 g1 = *reinterpret_cast<const float4*>(&gp_s[v][j][pc + 4]);
-                            ga = half8{(_Float16)g0.x, (_Float16)g0.y, (_Float16)g0.z, (_Float16)g0.w,
-                                       (_Float16)g1.x, (_Float16)g1.y, (_Float16)g1.z, (_Float16)g1.w};
-                        }
+                        if (j < 2) ga = *reinterpret_cast<const half8*>(&gp_s[v][j][pc]);
 #pragma unroll
                         for (int bb = 0; bb < NB; ++bb)
                             acc1[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga, __builtin_bit_cast(half8, xb[bb]),
@@ -589,10 +584,7 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                     for (int c = 0; c < 2; ++c) {
                         __asm__ volatile("" ::: "memory");   // one component's operands at a time
                         const int k = 2 * v + c;
-                        const float4 g0 = *reinterpret_cast<const float4*>(&gp_s[v][c][pc]);
-                        const float4 g1 = *reinterpret_cast<const float4*>(&gp_s[v][c][pc + 4]);
-                        const half8 gh = {(_Float16)g0.x, (_Float16)g0.y, (_Float16)g0.z, (_Float16)g0.w,
-                                          (_Float16)g1.x, (_Float16)g1.y, (_Float16)g1.z, (_Float16)g1.w};
+                        const half8 gh = *reinterpret_cast<const half8*>(&gp_s[v][c][pc]);
                         half8 yc[NB];
 #pragma unroll
                         for (int bb = 0; bb < NB; ++bb) {
