@@ -218,7 +218,7 @@ def main(argv=None):
         roof = {"bound": "hbm", "achieved": hbm, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": hbm / PEAK_HBM_GBPS, "traffic": None if traffic is None else traffic["bytes"]}
     if fp32_path:
-        kname = "k_diag_split (+ k_sum_ll)"
+        kname = "k_diag_split (the LL sum in its last workgroup)"
     elif full_path:
         kname = ("k_full_pipe (+ k_full_sum_ll)" if w.d > 32 else "k_full_fused (+ k_full_sum_ll)")
     elif w.k <= 256:
