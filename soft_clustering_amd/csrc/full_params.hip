@@ -429,36 +429,43 @@ __global__ __launch_bounds__(256) void k_full_mstep(const double* __restrict__ c
                                                     float* __restrict__ th_cov, float* out_pi,
                                                     float* out_mu, float* out_cov, int* flags) {
     __shared__ double red[256];
+    __shared__ double cen[64], s1v[64], dlt[64];   // centre, s1, mu' - centre (d <= 64)
     const int k = blockIdx.x, tid = threadIdx.x;
     const int ncolp = 1 + d + d * (d + 1) / 2;
     const double* cs = colsum + (int64_t)k * ncolp;
     const double s0 = cs[0];
     const bool empty = !(s0 >= kEmptyNk);
+    const double is0 = 1.0 / s0;
     double* st = stats + (int64_t)k * (1 + d + (int64_t)d * d);
     double nonfin = isfinite(s0) ? 0.0 : 1.0;
     for (int i = tid; i < d; i += 256) {
         const double s1 = cs[1 + i];
+        const double ci = muh[k * dp + i];
+        cen[i] = ci;
+        s1v[i] = s1;
+        dlt[i] = s1 * is0 - ci;
         st[1 + i] = s1;
         if (!isfinite(s1)) nonfin = 1.0;
         float mf = th_mu[(int64_t)k * d + i];
-        if (!empty) mf = (float)(s1 / s0);
+        if (!empty) mf = (float)(s1 * is0);
         th_mu[(int64_t)k * d + i] = mf;
         if (out_mu) out_mu[(int64_t)k * d + i] = mf;
     }
+    __syncthreads();
+    // row i = q / d from a float estimate (exact here: q < 64^2 and the quotient's
+    // distance to the next integer is at least 1 / (2 d))
+    const float inv_d = 1.0f / (float)d;
+#pragma unroll 4
     for (int q = tid; q < d * d; q += 256) {
-        const int i = q / d, c = q % d;
+        const int i = (int)(((float)q + 0.5f) * inv_d), c = q - i * d;
         const int r0 = i > c ? i : c, c0 = i > c ? c : i;
         const double m2 = cs[1 + d + tri_idx(r0, c0)];     // about the stored centre
-        const double ci = muh[k * dp + i], cc = muh[k * dp + c];
-        const double s1i = cs[1 + i], s1c = cs[1 + c];
+        const double ci = cen[i], cc = cen[c];
         // raw moment: sum g x x^T = M2 + c s1^T + s1 c^T - s0 c c^T
-        st[1 + d + q] = m2 + ci * s1c + s1i * cc - s0 * ci * cc;
+        st[1 + d + q] = m2 + ci * s1v[c] + s1v[i] * cc - s0 * ci * cc;
         if (!isfinite(m2)) nonfin = 1.0;
         float v = th_cov[(int64_t)k * d * d + q];
-        if (!empty) {
-            const double di = s1i / s0 - ci, dc = s1c / s0 - cc;
-            v = (float)(m2 / s0 - di * dc);
-        }
+        if (!empty) v = (float)(m2 * is0 - dlt[i] * dlt[c]);
         th_cov[(int64_t)k * d * d + q] = v;
         if (out_cov) out_cov[(int64_t)k * d * d + q] = v;
     }
