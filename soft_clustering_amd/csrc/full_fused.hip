@@ -361,7 +361,6 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
 namespace pipe {
 constexpr int kWaves = 12;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kP1 = 256;                 // threads of the whitening stage
 constexpr int DP = 64, NB = 4, NBLK = 10, NOB = 2, NKS = 4, DPO = 64, NV = 16;
 constexpr int kGS = T + 4;
 // 16-byte unit u of tile row r sits at unit u ^ ((r >> 1) & 7): 16 consecutive
@@ -382,7 +381,6 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     __shared__ __attribute__((aligned(16))) float g_s[2][KP][kGS];     // scores of two tiles
     __shared__ __attribute__((aligned(16))) uint16_t xr_s[3][T * DP];  // three tiles, swizzled
     __shared__ __attribute__((aligned(16))) uint16_t gp_s[EM ? 8 : 1][2][T + 8];   // fp16 gamma, per moment wave
-    __shared__ double red[T];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
     const bool p1 = w < 4;
