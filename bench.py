@@ -8,20 +8,23 @@ then the reduction / M-step kernel.  Workloads specified as a single EM
 iteration time every step from the initial parameters (gmm_prepare is then
 part of the step); the others chain the iterations.
 
-The default workload is the diagonal fp32 mixture with 1e6 points, D=64,
-K=16.  `value` is EM iterations/s; points*components/s and the achieved HBM
-bandwidth are reported beside it.  `roofline` prices the dominant kernel
-(gmm_em_step: the fused E+M kernel, or for more than 256 components the two
-sweeps and the slice merge, plus the small scan / panel / LL-sum launches) with
-its algorithmic work (8*D*K flops per point diagonal, 4*D*K isotropic)
-against the dense peak of the contraction's operand type (fp32 matrix for the
-fp32 family, fp16 for the large-K family), timed with HIP events recorded on
-the stream the kernels run on.  `cpu_baseline` times the fp64
-oracle on a bounded prefix of the same workload on the host cores.
+The default workload is the largest one that fits a single GPU: the diagonal
+mixture of 2e8 points, D=128, K=1024, stored in bf16 (51.2 GB), whose fused
+iteration takes two sweeps over X.  `value` is EM iterations/s;
+points*components/s and the achieved HBM bandwidth are reported beside it.
+`roofline` prices gmm_em_step (all its launches) with its algorithmic work
+(8*D*K flops per point diagonal, 4*D*K isotropic, (2 D(D+1) + 4D) K full)
+against the dense fp16 matrix-core peak, timed with HIP events recorded on
+the stream the kernels run on.  `calibration` measures the device's own
+ceilings (a streaming read of X, register-resident fp16 MFMA chains) and
+reports the fractions against them too.  `cpu_baseline` times the fp64
+oracle, as it stands, on a bounded prefix of the same workload with one
+worker process per host core.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -40,6 +43,7 @@ PEAK_TFLOPS = {                 # MI355X dense peaks, published
     "f32_vector": 157.3,
 }
 METRIC = "GMM EM iterations/sec & points·components/s at N,D,K; % of HBM or MFMA roofline"
+DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 
 # HBM traffic of one gmm_em_step (every launch it makes), measured with two
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
@@ -74,7 +78,6 @@ FAMILY_SOURCES = {
 
 def sources_digest(family):
     """SHA-256 (first 16 hex digits) over the family's kernel sources."""
-    import hashlib
     h = hashlib.sha256()
     for f in FAMILY_SOURCES[family]:
         with open(os.path.join(ROOT, "soft_clustering_amd", "csrc", f), "rb") as fh:
@@ -106,32 +109,132 @@ def algorithmic_work(w):
     return float(per_pt) * w.n, float(w.n) * w.d * es
 
 
-def cpu_baseline(w, x_dev, theta, target_s=12.0):
-    """The oracle, as it stands, on a prefix of the workload; scaled to
-    EM iterations/s of the whole workload."""
-    import torch
+# ---- CPU baseline: the oracle on every host core -----------------------------
+# The worker processes are started (spawned: a fresh interpreter each) before
+# this process touches the GPU, and never use it; each runs the oracle's
+# em_step, as it stands, over its share of a prefix of X.
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _worker_init():
     from threadpoolctl import threadpool_limits
+    global _LIMITS
+    _LIMITS = threadpool_limits(limits=1)   # one thread per worker process
+
+
+def _worker_step(args):
     import oracle
+    xs, pi, mu, cov, cov_type = args
+    t = time.perf_counter()
+    oracle.em_step(xs, oracle.Params(pi, mu, cov, cov_type))
+    return time.perf_counter() - t
+
+
+def _worker_ready(_):
+    import oracle  # noqa: F401  (imported before anything is timed)
+    return os.getpid()
+
+
+def start_cpu_pool(cores):
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    pool = ctx.Pool(cores, initializer=_worker_init)
+    pool.map(_worker_ready, range(cores), chunksize=1)   # every worker up, oracle imported
+    return pool
+
+
+def cpu_baseline(pool, cores, w, x_dev, theta, target_s=15.0):
+    """The oracle on a prefix of the workload, one share per worker; scaled
+    to EM iterations/s and points*components/s of the whole workload."""
     pi, mu, cov = theta
-    p = oracle.Params(pi, mu, cov, w.cov)
-    # calibration prefix of 1024 points, then a prefix sized to ~target_s
-    m = min(1024, w.n)
-    with threadpool_limits(limits=1):
+    par = (np.asarray(pi, np.float64), np.asarray(mu, np.float64), np.asarray(cov, np.float64), w.cov)
+
+    def run(m):
         xs = x_dev[:m].double().cpu().numpy()
+        parts = np.array_split(xs, cores)
         t = time.perf_counter()
-        oracle.em_step(xs, p)
-        dt = time.perf_counter() - t
-        m2 = int(min(w.n, max(m, m * target_s / max(dt, 1e-3))))
-        m2 = max(m, (m2 // 256) * 256)
-        xs = x_dev[:m2].double().cpu().numpy()
-        t = time.perf_counter()
-        oracle.em_step(xs, p)
-        dt = time.perf_counter() - t
-    it_s = (m2 / w.n) / dt
-    return {"value": it_s, "unit": "EM iterations/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {m2} of {w.n} points, one em_step (fp64 numpy, 1 thread), "
-                      f"{dt:.1f} s, scaled by {w.n}/{m2}",
-            "points_components_per_s": m2 * w.k / dt}
+        pool.map(_worker_step, [(p, *par) for p in parts], chunksize=1)
+        return time.perf_counter() - t, xs
+
+    m = min(w.n, 64 * cores)
+    dt, _ = run(m)                                          # calibration
+    m2 = int(min(w.n, max(m, m * target_s / max(dt, 1e-3))))
+    m2 = max(m, (m2 // (64 * cores)) * 64 * cores)
+    dt, xs = run(m2)
+    import torch
+    digest = hashlib.sha256(x_dev[:m2].contiguous().cpu().view(-1).view(torch.uint8).numpy()).hexdigest()
+    return {"value": (m2 / w.n) / dt, "unit": "EM iterations/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"first {m2} of {w.n} points (prefix), one fp64 numpy em_step per worker over "
+                      f"{cores} equal shares, {cores} worker processes x 1 thread, {dt:.1f} s wall, "
+                      f"scaled by {w.n}/{m2}",
+            "points_components_per_s": m2 * w.k / dt,
+            "sample_sha256": digest}
+
+
+def x_digest(x, chunk_rows=1 << 20, workers=8):
+    """SHA-256 over the SHA-256 digests of consecutive 2^20-row chunks of X's
+    stored bytes (the chunks are hashed in parallel; hashlib releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    n = x.shape[0]
+
+    def one(lo):
+        b = x[lo:lo + chunk_rows].contiguous().cpu().view(-1).view(torch.uint8).numpy()
+        return hashlib.sha256(b).digest()
+
+    with ThreadPoolExecutor(workers) as ex:
+        ds = list(ex.map(one, range(0, n, chunk_rows)))
+    return hashlib.sha256(b"".join(ds)).hexdigest()
+
+
+def calibrate(gmm, x, reps=3):
+    """Measured ceilings: streaming read of X, register-resident MFMA chains."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    grid_r = 8 * cus
+    sink = gmm.calib_sink(grid_r)
+    buf = x if x.is_contiguous() else x.contiguous()
+    best_bw = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nb = gmm.calib_read(buf, grid_r, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best_bw = max(best_bw, nb / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    grid_m = 2 * cus
+    sinkm = gmm.calib_sink(grid_m)
+    iters = 400_000
+    best_tf = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fl = gmm.calib_mfma(iters, grid_m, sinkm)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best_tf = max(best_tf, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return {"hbm_read_GBps": best_bw, "hbm_read_bytes": int(nb),
+            "mfma_f16_TFLOPs": best_tf, "mfma_instruction": "v_mfma_f32_32x32x16_f16",
+            "kernels": "k_calib_read (16-byte grid-stride loads), k_calib_mfma (4 register chains per wave)",
+            "best_of": reps}
 
 
 def main(argv=None):
@@ -139,8 +242,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="diag-f32-n1e6-d64-k16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--no-digest", action="store_true", help="skip the SHA-256 digest of X")
     ap.add_argument("--from-init", choices=("auto", "yes", "no"), default="auto",
                     help="time every step from the initial parameters (prepare + em_step + "
                          "finalize); auto: for workloads specified as one EM iteration")
@@ -152,6 +257,9 @@ def main(argv=None):
         print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the fused EM "
               "iteration is single-GPU and multi-GPU sharding is not built.", file=sys.stderr)
         return 2
+
+    cores = host_cores()
+    pool = None if a.no_cpu_baseline else start_cpu_pool(cores)   # before the GPU is touched
 
     import torch
     from soft_clustering_amd import gmm, synth
@@ -169,6 +277,7 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     gm.prepare(pi, mu, cov)
     for i in range(a.warmup):
         if from_init:
@@ -195,6 +304,8 @@ def main(argv=None):
     fused_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     ms_step = total_ms / a.steps
     fused_avg = float(np.mean(fused_ms))
+    peak_mem = torch.cuda.max_memory_allocated()
+    diag = gm.diagnostics()
 
     flops, nbytes = algorithmic_work(w)
     fp32_path = w.cov == "diag" and w.k <= 64          # fp32-accurate split-fp16 MFMA family
@@ -262,7 +373,15 @@ def main(argv=None):
         "points_components_per_s": w.n * w.k * 1000.0 / ms_step,
         "wall_s": wall,
         "ll_first_last": [float(ll_hist[0]), float(ll_hist[-1])],
+        "peak_device_bytes": int(peak_mem),
+        "x_bytes": int(w.x_bytes),
+        "workspace_bytes": int(gm.ws_bytes),
+        "nk_fp32_bytes": int(w.n * w.k * 4),
+        "health": {"ill_cond": diag.ill_cond, "x_range": diag.x_range, "empty": diag.empty,
+                   "nonfinite": diag.nonfinite, "bad_params": diag.bad_params},
         "roofline": roof,
+        "calibration": None,
+        "x_sha256": None,
         "cpu_baseline": None,
     }
     if a.copy_calibration:
@@ -271,9 +390,20 @@ def main(argv=None):
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         out["copy_calibration_bytes"] = int(nbytes)
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x, (pi0, mu0, cov0))
+    if not a.no_calibration:
+        cal = calibrate(gmm, x)
+        cal["frac_of_measured"] = (achieved_tflops / cal["mfma_f16_TFLOPs"] if roof["bound"] == "mfma"
+                                   else hbm / cal["hbm_read_GBps"])
+        out["calibration"] = cal
+    if not a.no_digest:
+        out["x_sha256"] = {"digest": x_digest(x), "recipe": "sha256 over the sha256 of consecutive "
+                           "2^20-row chunks of X's stored bytes"}
+    if pool is not None:
+        out["cpu_baseline"] = cpu_baseline(pool, cores, w, x, (pi0, mu0, cov0))
+        pool.close()
+        pool.join()
     print(json.dumps(out), flush=True)
     return 0
 

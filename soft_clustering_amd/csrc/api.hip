@@ -3,6 +3,7 @@
 // allocates memory; every launch goes to the caller's stream.
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "common.h"
@@ -26,6 +27,19 @@ int device_cu_count() {
         cached[dev] = cus;
     }
     return cached[dev];
+}
+
+// Tuning: GMM_SEGMENT_TILES (environment, positive integer) overrides the
+// length of the fp32 accumulation runs of the statistics passes (tiles per
+// workgroup or wave and launch segment); unset or invalid: each family's
+// default.  Read at every call, so a process can change it between calls.
+static int64_t segment_tiles_override() {
+    const char* v = getenv("GMM_SEGMENT_TILES");
+    if (v == nullptr || *v == 0) return 0;
+    char* end = nullptr;
+    const long long t = strtoll(v, &end, 10);
+    if (end == v || *end != 0 || t < 1 || t > ((int64_t)1 << 40)) return 0;
+    return (int64_t)t;
 }
 
 static int pad_dim(int64_t d) {
@@ -54,6 +68,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
     if (p->xdt < GMM_F32 || p->xdt > GMM_F16) return GMM_E_ARG;
     if (!(p->var_floor >= 0.0f) || !isfinite(p->var_floor)) return GMM_E_ARG;
     if (!(p->ridge_rel >= 0.0f) || !isfinite(p->ridge_rel)) return GMM_E_ARG;
+    p->seg_tiles = segment_tiles_override();
 
     const size_t A = 256;
     size_t off = 0;
@@ -257,43 +272,50 @@ gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes
     if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
     if (out == nullptr) return GMM_E_ARG;
     if (hipStreamSynchronize(stream) != hipSuccess) return GMM_E_HIP;
-    const size_t nint = 2 * p.k + 2;
-    int small[2 * 64 + 4];
-    int* host = (size_t)nint <= sizeof(small) / sizeof(int) ? small : new int[nint];
+    // The flags are read in fixed-size pieces into stack buffers, so this
+    // call allocates nothing whatever K is.
+    constexpr int kPiece = 256;
+    int fl[kPiece], rt[kPiece], misc[2];
+    double ck[kPiece * 4];
+    const char* base = (const char*)ws;
+    const int* dflags = (const int*)(base + p.off_diag);
     double ll = 0.0;
-    hipError_t e = hipMemcpy(host, (const char*)ws + p.off_diag, sizeof(int) * nint,
-                             hipMemcpyDeviceToHost);
+    hipError_t e = hipMemcpy(&ll, base + p.off_ll, sizeof(double), hipMemcpyDeviceToHost);
     if (e == hipSuccess)
-        e = hipMemcpy(&ll, (const char*)ws + p.off_ll, sizeof(double), hipMemcpyDeviceToHost);
-    if (e == hipSuccess) {
-        memset(out, 0, sizeof(*out));
-        // diagonal fp32 path: per-(component, chunk) counts of bad / non-finite values
-        const bool dg = p.path == PATH_DIAG_F32;
-        const int nch = dg ? diag_chunks(p) : 0;
-        const size_t nck = (size_t)p.k * nch * 4;
-        double* ck = new double[nck + 1];
-        if (nck)
-            e = hipMemcpy(ck, (const char*)ws + p.off_chunk, sizeof(double) * nck,
-                          hipMemcpyDeviceToHost);
-        for (int64_t k = 0; k < p.k && e == hipSuccess; ++k) {
-            int f = host[k];
-            for (int c = 0; c < nch; ++c) {
-                if (ck[(k * nch + c) * 4 + 2] > 0.0) f |= 1;
-                if (ck[(k * nch + c) * 4 + 3] > 0.0) f |= 8;
+        e = hipMemcpy(misc, dflags + 2 * p.k, sizeof(misc), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return GMM_E_HIP;
+    memset(out, 0, sizeof(*out));
+    // diagonal fp32 path: per-(component, chunk) counts of bad / non-finite values
+    const bool dg = p.path == PATH_DIAG_F32;
+    const int nch = dg ? diag_chunks(p) : 0;
+    const double* dchunk = (const double*)(base + p.off_chunk);
+    for (int64_t k0 = 0; k0 < p.k && e == hipSuccess; k0 += kPiece) {
+        const int m = (int)(p.k - k0 < kPiece ? p.k - k0 : kPiece);
+        e = hipMemcpy(fl, dflags + k0, sizeof(int) * m, hipMemcpyDeviceToHost);
+        if (e == hipSuccess)
+            e = hipMemcpy(rt, dflags + p.k + k0, sizeof(int) * m, hipMemcpyDeviceToHost);
+        for (int i = 0; i < m && e == hipSuccess; ++i) {
+            int f = fl[i];
+            for (int c0 = 0; c0 < nch && e == hipSuccess; c0 += kPiece) {
+                const int mc = nch - c0 < kPiece ? nch - c0 : kPiece;
+                e = hipMemcpy(ck, dchunk + ((k0 + i) * nch + c0) * 4, sizeof(double) * 4 * mc,
+                              hipMemcpyDeviceToHost);
+                for (int c = 0; c < mc; ++c) {
+                    if (ck[4 * c + 2] > 0.0) f |= 1;
+                    if (ck[4 * c + 3] > 0.0) f |= 8;
+                }
             }
             if (f & 1) out->bad_params++;
             if (f & 2) out->not_pd++;
             if (f & 4) out->empty++;
             if (f & 8) out->nonfinite = 1;
             if (f & 16) out->ill_cond++;
-            if (host[p.k + k] > out->ridge_retries) out->ridge_retries = host[p.k + k];
+            if (rt[i] > out->ridge_retries) out->ridge_retries = rt[i];
         }
-        delete[] ck;
-        if (host[2 * p.k]) out->nonfinite = 1;
-        if (p.path == PATH_LARGEK) out->x_range = host[2 * p.k + 1];
-        out->ll = ll;
     }
-    if (host != small) delete[] host;
+    if (misc[0]) out->nonfinite = 1;
+    if (p.path == PATH_LARGEK) out->x_range = misc[1];
+    out->ll = ll;
     return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 

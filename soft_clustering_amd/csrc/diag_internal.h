@@ -23,6 +23,11 @@ __host__ __device__ constexpr int diag_split_waves(int dp, int kb) {
     return (dp <= 64 && dp * kb <= 64) ? 8 : 4;
 }
 
+// Tiles one wave accumulates in fp32 before its run is closed: the E+M pass
+// is launched in segments of at most this many tiles per wave, each adding
+// its fp32 sums into the workgroups' fp64 partial slots.
+constexpr int64_t kDiagSegTiles = 256;
+
 // |y| bound of the split-fp16 operands: y^2 stays below the fp16 maximum
 // (65504) with margin; a tile with any larger |y| takes the fp32 route.
 constexpr float kSplitLim = 224.0f;

@@ -260,7 +260,8 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     const float* __restrict__ panel32, const float* __restrict__ shift,
     float* __restrict__ scale, double* __restrict__ part, double* __restrict__ part_ll,
     unsigned* __restrict__ done, double* __restrict__ ll_ws, double* __restrict__ ll_out,
-    int* __restrict__ nonfinite_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
+    int* __restrict__ nonfinite_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
+    int64_t tlo, int64_t thi, int seg_first) {
     using S = SplitShape<DP, KB, XT>;
     constexpr int WAVES = S::kWaves, THREADS = S::kThreads;
     constexpr int KS = S::kKS, NCB = S::kNCB, EV = S::kEV, P = S::kPitch;
@@ -276,12 +277,13 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     const int lane = tid & 63, g = lane >> 4, j = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
 
-    // this wave's run of tiles (wave-uniform; the 64-bit division expands to
-    // vector code, so its results are moved back to scalar registers)
-    const int64_t tiles = (n + kST - 1) / kST;
+    // this wave's run of the segment's tiles [tlo, thi) (wave-uniform; the
+    // 64-bit division expands to vector code, so its results are moved back
+    // to scalar registers)
+    const int64_t tiles = thi - tlo;
     const int64_t nw = (int64_t)gridDim.x * WAVES, gw = (int64_t)blockIdx.x * WAVES + w;
     const int64_t tb = tiles / nw, tr = tiles % nw;
-    const int64_t t0 = uniform64(gw * tb + (gw < tr ? gw : tr));
+    const int64_t t0 = uniform64(tlo + gw * tb + (gw < tr ? gw : tr));
     const int nt = __builtin_amdgcn_readfirstlane((int)(tb + (gw < tr ? 1 : 0)));
     const int64_t tlast = t0 + nt - 1;
 
@@ -684,7 +686,8 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
                 for (int w2 = 0; w2 < WAVES; ++w2)
                     v += (double)red[(w2 * 16 * KB + k) * (2 * DP) + col];
             }
-            part[(wg * k_real + k) * ncol + c] = v;
+            double* o = part + (wg * k_real + k) * ncol + c;
+            *o = seg_first ? v : *o + v;   // later segments add to the slot
         }
     }
     // LL of the whole pass: the last workgroup to finish sums the
@@ -693,7 +696,7 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     // the next launch)
     __shared__ int last_wg;
     if (tid == 0) {
-        part_ll[wg] = ll_wg * kLn2;
+        part_ll[wg] = seg_first ? ll_wg * kLn2 : part_ll[wg] + ll_wg * kLn2;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const unsigned prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_wg = prev == gridDim.x - 1;
@@ -713,15 +716,28 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     }
 }
 
+// EM: the pass in segments of at most seg_tiles tiles per wave (each closes
+// the waves' fp32 runs into the fp64 partial slots); E-step alone: one pass.
 template <int DP, int KB, typename XT, bool VEC, bool EM>
 hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, double* ll_out,
                     float* lse, int* arg, hipStream_t s) {
     constexpr int W = diag_split_waves(DP, KB);
-    hipLaunchKernelGGL((k_diag_split<DP, KB, XT, VEC, EM>), dim3(grid), dim3(64 * W), 0, s,
-                       (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.pi, w.mu, w.var,
-                       w.chunk_part, diag_chunks(p), w.panel, w.shift, w.scale, w.part, w.part_ll,
-                       (unsigned*)w.done, w.ll, ll_out, w.nonfinite_ll, lse, arg);
-    return hipGetLastError();
+    const int64_t tiles = (p.n + kST - 1) / kST;
+    const int64_t M = p.seg_tiles > 0 ? p.seg_tiles : kDiagSegTiles;
+    const int64_t per = (int64_t)grid * W * M;
+    const int64_t nseg = EM ? (tiles + per - 1) / per : 1;
+    const int64_t len = nseg > 1 ? (tiles + nseg - 1) / nseg : tiles;
+    for (int64_t i = 0; i < (nseg < 1 ? 1 : nseg); ++i) {
+        const int64_t lo = i * len, hi = lo + len < tiles ? lo + len : tiles;
+        hipLaunchKernelGGL((k_diag_split<DP, KB, XT, VEC, EM>), dim3(grid), dim3(64 * W), 0, s,
+                           (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.pi, w.mu, w.var,
+                           w.chunk_part, diag_chunks(p), w.panel, w.shift, w.scale, w.part, w.part_ll,
+                           (unsigned*)w.done, w.ll, ll_out, w.nonfinite_ll, lse, arg, lo, hi,
+                           i == 0 ? 1 : 0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DP, int KB, bool EM>

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
-    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
+    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
+    int64_t tlo, int64_t thi, int seg_first) {
     using Sh = FullShape<DP>;
     constexpr int NB = Sh::kNB, NBLK = Sh::kNBlk;
     constexpr int NOB = Sh::kNOB, NKS = Sh::kNKS, DPO = Sh::kDPO, NV = Sh::kNV;
@@ -100,10 +101,10 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     }
 
     const int G = gridDim.x;
-    const int64_t tiles = (n + T - 1) / T;
+    const int64_t tiles = thi - tlo;   // this segment's tiles
     const int64_t tb = tiles / G, tr = tiles % G;
     const int b = blockIdx.x;
-    const int64_t t0 = b * tb + (b < tr ? b : tr);
+    const int64_t t0 = tlo + b * tb + (b < tr ? b : tr);
     const int64_t t1 = t0 + tb + (b < tr ? 1 : 0);
 
     float s0acc[KP];
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
         if (tid < s2) red[tid] += red[tid + s2];
         __syncthreads();
     }
-    if (tid == 0) part_ll[b] = red[0] * kLn2;
+    if (tid == 0) part_ll[b] = seg_first ? red[0] * kLn2 : part_ll[b] + red[0] * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -373,7 +374,8 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
-    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg) {
+    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
+    int64_t tlo, int64_t thi, int seg_first) {
     using namespace pipe;
     __shared__ __attribute__((aligned(16))) uint32_t nm_s[KP][DP];     // (-mu, -mu) fp16 pairs
     __shared__ __attribute__((aligned(16))) float wb_s[KP][NOB][2][16];  // -W mu, accumulator layout
@@ -401,10 +403,10 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     }
 
     const int G = gridDim.x;
-    const int64_t tiles = (n + T - 1) / T;
+    const int64_t tiles = thi - tlo;   // this segment's tiles
     const int64_t tb = tiles / G, tr = tiles % G;
     const int b = blockIdx.x;
-    const int64_t t0 = b * tb + (b < tr ? b : tr);
+    const int64_t t0 = tlo + b * tb + (b < tr ? b : tr);
     const int nt = (int)(tb + (b < tr ? 1 : 0));
 
     // the whitening stage's point loads: thread tid < 256 holds point tid of a tile
@@ -647,41 +649,41 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     if (w == 4) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ll += __shfl_xor(ll, o);
-        if (lane == 0) part_ll[b] = ll * kLn2;
+        if (lane == 0) part_ll[b] = seg_first ? ll * kLn2 : part_ll[b] + ll * kLn2;
     }
 }
 
 template <int DP, bool VEC>
 hipError_t launch_dv(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
-                     int* arg, hipStream_t s) {
+                     int* arg, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
     if (em)
         hipLaunchKernelGGL((k_full_fused<DP, true, VEC>), dim3(grid), dim3(256), 0, s,
                            (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
-                           w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr);
+                           w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first);
     else
         hipLaunchKernelGGL((k_full_fused<DP, false, VEC>), dim3(grid), dim3(256), 0, s,
                            (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
-                           w.cvec, w.rscale, w.part, w.part_ll, lse, arg);
+                           w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first);
     return hipGetLastError();
 }
 
 template <int DP>
 hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
-                     int* arg, hipStream_t s) {
+                     int* arg, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
     const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
     if (DP == 64 && vec) {   // the pipelined kernel
         if (em)
             hipLaunchKernelGGL((k_full_pipe<true>), dim3(grid), dim3(pipe::kThreads), 0, s,
                                (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
-                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr);
+                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first);
         else
             hipLaunchKernelGGL((k_full_pipe<false>), dim3(grid), dim3(pipe::kThreads), 0, s,
                                (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
-                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, lse, arg);
+                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first);
         return hipGetLastError();
     }
-    return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, s)
-               : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, s);
+    return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s)
+               : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
 }
 
 }  // namespace
@@ -695,11 +697,12 @@ int full_grid(const Plan& p) {
 }
 
 hipError_t full_launch_fused(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
-                             float* lse, int* arg, hipStream_t s) {
+                             float* lse, int* arg, int64_t tlo, int64_t thi, int seg_first,
+                             hipStream_t s) {
     switch (p.dp) {
-        case 16: return launch_dp<16>(p, w, x, em, grid, lse, arg, s);
-        case 32: return launch_dp<32>(p, w, x, em, grid, lse, arg, s);
-        case 64: return launch_dp<64>(p, w, x, em, grid, lse, arg, s);
+        case 16: return launch_dp<16>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
+        case 32: return launch_dp<32>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
+        case 64: return launch_dp<64>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
     }
     return hipErrorInvalidValue;
 }

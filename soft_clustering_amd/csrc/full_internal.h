@@ -61,10 +61,33 @@ inline FullWs full_ws(const Plan& p, char* ws) {
     return w;
 }
 
-// Launch the fused kernel (full_fused.hip).  em: statistics + LL partials;
-// otherwise E-step only with optional per-point outputs.
+// Launch the fused kernel (full_fused.hip) over tiles [tlo, thi).  em:
+// statistics + LL partials (fp32 partials of this segment; the LL slot is
+// written by the first segment and added to by later ones); otherwise E-step
+// only with optional per-point outputs.
 hipError_t full_launch_fused(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
-                             float* lse, int* arg, hipStream_t s);
+                             float* lse, int* arg, int64_t tlo, int64_t thi, int seg_first,
+                             hipStream_t s);
 int full_grid(const Plan& p);
+
+// Tiles (of kFullT points) one workgroup accumulates in fp32 before its run
+// is closed: the E+M pass runs in segments of at most this many tiles per
+// workgroup, and the fp32 partials of each segment are added into fp64
+// column sums before the next one.
+constexpr int64_t kFullSegTiles = 64;
+
+struct FullSegs {
+    int64_t tiles, len;
+    int n;
+};
+inline FullSegs full_segs(const Plan& p, int grid) {
+    FullSegs s;
+    s.tiles = (p.n + kFullT - 1) / kFullT;
+    const int64_t per = (int64_t)grid * (p.seg_tiles > 0 ? p.seg_tiles : kFullSegTiles);
+    s.n = (int)((s.tiles + per - 1) / per);
+    if (s.n < 1) s.n = 1;
+    s.len = (s.tiles + s.n - 1) / s.n;
+    return s;
+}
 
 }  // namespace gmm

@@ -395,7 +395,8 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
 // the workgroups for column c in four interleaved chains, and the quarters are
 // added in a fixed order.
 __global__ __launch_bounds__(256) void k_full_reduce(const float* __restrict__ part, int P,
-                                                     int ncolp, double* __restrict__ colsum) {
+                                                     int ncolp, double* __restrict__ colsum,
+                                                     int add) {
     __shared__ double qs[4][64];
     const int k = blockIdx.y, c = threadIdx.x % 64, q = threadIdx.x / 64;
     const int col = blockIdx.x * 64 + c;
@@ -415,8 +416,11 @@ __global__ __launch_bounds__(256) void k_full_reduce(const float* __restrict__ p
     }
     qs[q][c] = (a0 + a1) + (a2 + a3);
     __syncthreads();
-    if (q == 0 && col < ncolp)
-        colsum[(int64_t)k * ncolp + col] = (qs[0][c] + qs[1][c]) + (qs[2][c] + qs[3][c]);
+    if (q == 0 && col < ncolp) {
+        const double v = (qs[0][c] + qs[1][c]) + (qs[2][c] + qs[3][c]);
+        double* o = colsum + (int64_t)k * ncolp + col;
+        *o = add ? *o + v : v;   // add: a later segment of the same pass
+    }
 }
 
 // M-step per component (grid K, 256 threads) and the raw statistics
@@ -531,7 +535,18 @@ gmm_status full_prepare(const Plan& p, char* ws, const float* pi, const float* m
 gmm_status full_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
     FullWs w = full_ws(p, ws);
     const int G = full_grid(p);
-    if (full_launch_fused(p, w, x, true, G, nullptr, nullptr, s) != hipSuccess) return GMM_E_HIP;
+    const FullSegs sg = full_segs(p, G);
+    const int ncolp = (int)full_ncolp(p.d);
+    for (int i = 0; i < sg.n; ++i) {
+        const int64_t lo = (int64_t)i * sg.len, hi = lo + sg.len < sg.tiles ? lo + sg.len : sg.tiles;
+        if (full_launch_fused(p, w, x, true, G, nullptr, nullptr, lo, hi, i == 0, s) != hipSuccess)
+            return GMM_E_HIP;
+        // every segment but the last is closed here; finalize adds the last one
+        if (i + 1 < sg.n)
+            hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 63) / 64, p.k), dim3(256), 0, s, w.part,
+                               G, ncolp, w.colsum, i > 0 ? 1 : 0);
+    }
+    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
     return sum_ll(p, w, G, ll_out, s);
 }
 
@@ -541,7 +556,7 @@ gmm_status full_finalize(const Plan& p, char* ws, float* pi, float* mu, float* c
     const int G = full_grid(p);
     const int ncolp = (int)full_ncolp(p.d);
     hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 63) / 64, p.k), dim3(256), 0, s, w.part, G,
-                       ncolp, w.colsum);
+                       ncolp, w.colsum, full_segs(p, G).n > 1 ? 1 : 0);
     hipLaunchKernelGGL(k_full_mstep, dim3(p.k), dim3(256), 0, s, w.colsum, p.n, (int)p.d, p.dp,
                        w.muh, w.stats, w.pi, w.mu, w.cov, pi, mu, cov, w.flags);
     if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
@@ -553,7 +568,9 @@ gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
     FullWs w = full_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int G = full_grid(p);
-    if (full_launch_fused(p, w, x, false, G, lse, argmax, s) != hipSuccess) return GMM_E_HIP;
+    if (full_launch_fused(p, w, x, false, G, lse, argmax, 0, (p.n + kFullT - 1) / kFullT, 1, s) !=
+        hipSuccess)
+        return GMM_E_HIP;
     return sum_ll(p, w, G, ll_out, s);
 }
 

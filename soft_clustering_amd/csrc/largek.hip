@@ -201,10 +201,10 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
         dsc_l[(i % 8) * Sh::kCB + i / 8] = kIso ? cs : make_float2(cs.y, -cs.x * cs.y);
     }
 
-    // ---- this chunk's tiles
-    const int64_t tiles = (n + kT - 1) / kT;
+    // ---- this chunk's tiles of the segment [tlo, thi)
+    const int64_t tiles = a.thi - a.tlo;
     const int64_t tb = tiles / nchunks, tr = tiles % nchunks;
-    const int64_t t0 = chunk * tb + (chunk < tr ? chunk : tr);
+    const int64_t t0 = a.tlo + chunk * tb + (chunk < tr ? chunk : tr);
     const int64_t t1 = t0 + tb + (chunk < tr ? 1 : 0);
 
     f32x16 acc[kStats ? CB : 1][kStats ? NFB : 1];
@@ -587,7 +587,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
 
     // ---- epilogue: per-workgroup partials, one writer per value
     const int flag = __syncthreads_or(rng > kF16Max ? 1 : 0);
-    if (tid == 0) a.part_flag[blockIdx.x] = flag;
+    const bool first = a.seg_first != 0;
+    if (tid == 0) a.part_flag[blockIdx.x] = first ? flag : (a.part_flag[blockIdx.x] | flag);
     if constexpr (kStats) {
         const int ncol = kIso ? 2 + d : 1 + 2 * d;
         double* dst = a.part + (int64_t)blockIdx.x * kLkSlice * ncol;
@@ -604,7 +605,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kl = w * KW + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        dst[(int64_t)kl * ncol + col] = (double)acc[cb][fb][r];
+                        double* o = dst + (int64_t)kl * ncol + col;
+                        *o = first ? (double)acc[cb][fb][r] : *o + (double)acc[cb][fb][r];
                     }
                 }
             }
@@ -615,7 +617,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int kl = w * KW + 16 * b + 4 * gq + r;
-                    dst[(int64_t)kl * ncol + (gi == 0 ? 0 : 1 + d)] = (double)aux[b][r] * scl;
+                    double* o = dst + (int64_t)kl * ncol + (gi == 0 ? 0 : 1 + d);
+                    *o = first ? (double)aux[b][r] * scl : *o + (double)aux[b][r] * scl;
                 }
         }
     }
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
             if (tid < s2) llred[tid] += llred[tid + s2];
             __syncthreads();
         }
-        if (tid == 0) a.part_ll[blockIdx.x] = llred[0] * kLn2;
+        if (tid == 0) a.part_ll[blockIdx.x] = first ? llred[0] * kLn2 : a.part_ll[blockIdx.x] + llred[0] * kLn2;
     }
 }
 

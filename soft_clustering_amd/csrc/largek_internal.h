@@ -28,6 +28,12 @@ constexpr float kF16Max = 65504.0f;
 // this many nats is reported as ill-conditioned (flag bit 4).
 constexpr double kLkIllCondNats = 4.0;
 
+// Tiles one workgroup accumulates in fp32 before its run is closed: the
+// statistics passes are launched in segments of at most this many tiles per
+// point chunk, and each segment adds its fp32 sums into the workgroup's fp64
+// partial slot.
+constexpr int64_t kLkSegTiles = 2048;
+
 // Slots for per-workgroup LL partials and range flags (fused kernel and the
 // slice-merge kernel), and workgroups of the slice-merge kernel.
 constexpr int kLkLLSlots = 1024;
@@ -98,7 +104,27 @@ struct LkArgs {
     int* part_flag;
     float* out_lse;              // E-only: natural-log LSE per point (nullable)
     int* out_arg;                // E-only: argmax per point (nullable)
+    // segment: tiles [tlo, thi) split over the point chunks; the first
+    // segment writes the partial slots, later ones add to them
+    int64_t tlo, thi;
+    int seg_first;
 };
+
+// Segments of a statistics pass: tiles split into `nseg` ranges of nearly
+// equal length, each at most seg_tiles per chunk.
+struct LkSegs {
+    int64_t tiles, len;
+    int n;
+};
+inline LkSegs lk_segs(int64_t n_points, int chunks, int64_t seg_tiles) {
+    LkSegs s;
+    s.tiles = (n_points + kLkT - 1) / kLkT;
+    const int64_t per = (int64_t)chunks * (seg_tiles > 0 ? seg_tiles : 1);
+    s.n = (int)((s.tiles + per - 1) / per);
+    if (s.n < 1) s.n = 1;
+    s.len = (s.tiles + s.n - 1) / s.n;
+    return s;
+}
 
 // Statistic columns per component: diag [s0, s1(D), s2(D)], iso [s0, s1(D), s2].
 inline int64_t lk_ncols(int cov, int64_t d) { return cov == GMM_COV_ISO ? 2 + d : 1 + 2 * d; }

@@ -326,7 +326,10 @@ __global__ __launch_bounds__(256) void k_lk_merge(int64_t n, int S, float* part_
     if (threadIdx.x == 0) part_ll[blockIdx.x] = ll * kLn2;
 }
 
-// LL = fixed-order sum of the LL partials; OR of the range flags.
+// LL = fixed-order sum of the LL partials; OR of the range flags.  A pass
+// that met a value of X outside the fp16 operand range (clamped staging) has
+// invalid scores for that point, so its LL is reported as NaN (and the
+// finalize that follows keeps theta): the failure is visible in the result.
 __global__ __launch_bounds__(256) void k_lk_sum(const double* part_ll, int P, const int* part_flag,
                                                 int Pf, double* ll_ws, double* ll_out, int* misc) {
     __shared__ double red[256];
@@ -336,6 +339,7 @@ __global__ __launch_bounds__(256) void k_lk_sum(const double* part_ll, int P, co
     int f = 0;
     for (int p = threadIdx.x; p < Pf; p += 256) f |= part_flag[p];
     f = __syncthreads_or(f);
+    if (f) v = __builtin_nan("");
     if (threadIdx.x == 0) {
         *ll_ws = v;
         if (ll_out) *ll_out = v;
@@ -352,7 +356,8 @@ __global__ __launch_bounds__(256) void k_lk_reduce(
     const double* __restrict__ part, int G, int S, int64_t n, int d, bool iso, float var_floor,
     const float2* __restrict__ dsc, double* __restrict__ stats, float* __restrict__ th_pi,
     float* __restrict__ th_mu, float* __restrict__ th_var, float* __restrict__ out_pi,
-    float* __restrict__ out_mu, float* __restrict__ out_var, int* __restrict__ flags) {
+    float* __restrict__ out_mu, float* __restrict__ out_var, int* __restrict__ flags,
+    const int* __restrict__ misc) {
     extern __shared__ double colsum[];   // [ncol]
     __shared__ double red[256];
     const int k = blockIdx.x, tid = threadIdx.x;
@@ -369,8 +374,10 @@ __global__ __launch_bounds__(256) void k_lk_reduce(
     }
     __syncthreads();
     const double s0 = colsum[0];
-    const bool empty = s0 < kEmptyNk;
-    double nonfin = isfinite(s0) ? 0.0 : 1.0;
+    // a pass with clamped operands (misc[1]) updates nothing: theta is kept
+    const bool clamped = misc[1] != 0;
+    const bool empty = s0 < kEmptyNk || clamped;
+    double nonfin = (isfinite(s0) && !clamped) ? 0.0 : 1.0;
     // per dimension: t1 = sum gamma y, t2 = sum gamma y^2 (diag)
     double mu2 = 0.0, c_t1 = 0.0, cc = 0.0;
     for (int dd = tid; dd < d; dd += 256) {
@@ -416,13 +423,13 @@ __global__ __launch_bounds__(256) void k_lk_reduce(
             th_var[k] = vf;
             if (out_var) out_var[k] = vf;
         }
-        const float pf = (float)(s0 / (double)n);
+        const float pf = clamped ? th_pi[k] : (float)(s0 / (double)n);
         th_pi[k] = pf;
         if (out_pi) out_pi[k] = pf;
         int f = 0;
         if (!(pf >= 0.0f) || !isfinite(pf)) f |= 1 | 8;
         if (nonfin > 0.0) f |= 8;
-        if (empty) f |= 4;
+        if (empty && !clamped) f |= 4;
         flags[k] = f | (flags[k] & 16);   // keep the conditioning flag of this pass's theta
     }
 }
@@ -466,6 +473,9 @@ LkArgs make_args(const Plan& p, const LkWs& w, const void* x) {
     a.part = w.part;
     a.part_ll = w.part_ll;
     a.part_flag = w.part_flag;
+    a.tlo = 0;
+    a.thi = (p.n + kLkT - 1) / kLkT;
+    a.seg_first = 1;
     return a;
 }
 
@@ -473,6 +483,22 @@ int merge_grid(const Plan& p) {
     int64_t g = (p.n + 255) / 256;
     if (g > kLkMergeWgs) g = kLkMergeWgs;
     return (int)(g < 1 ? 1 : g);
+}
+
+// A statistics pass (fused E+M or sweep 2) in segments of at most
+// seg_tiles tiles per point chunk: every workgroup's fp32 accumulators are
+// closed at the end of each segment and added into its fp64 partial slot.
+hipError_t launch_segments(const Plan& p, LkArgs a, int mode, int G, hipStream_t s) {
+    const int64_t M = p.seg_tiles > 0 ? p.seg_tiles : kLkSegTiles;
+    const LkSegs sg = lk_segs(p.n, G / p.lk_slices, M);
+    for (int i = 0; i < sg.n; ++i) {
+        a.tlo = (int64_t)i * sg.len;
+        a.thi = a.tlo + sg.len < sg.tiles ? a.tlo + sg.len : sg.tiles;
+        a.seg_first = i == 0 ? 1 : 0;
+        const hipError_t e = lk_launch(p, a, mode, G, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 gmm_status lk_sum(const Plan& p, const LkWs& w, int P, int Pf, double* ll_out, hipStream_t s) {
@@ -513,7 +539,7 @@ gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hi
     LkArgs a = make_args(p, w, x);
     if (p.lk_slices == 1) {
         const int G = lk_grid(p, LK_FUSED_EM);
-        if (lk_launch(p, a, LK_FUSED_EM, G, s) != hipSuccess) return GMM_E_HIP;
+        if (launch_segments(p, a, LK_FUSED_EM, G, s) != hipSuccess) return GMM_E_HIP;
         return lk_sum(p, w, G, G, ll_out, s);
     }
     const int G1 = lk_grid(p, LK_SWEEP1), G = lk_grid(p, LK_SWEEP2);
@@ -526,7 +552,7 @@ gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hi
     if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
     a.part_lse = nullptr;
     a.lse_in = w.part_lse;
-    if (lk_launch(p, a, LK_SWEEP2, G, s) != hipSuccess) return GMM_E_HIP;
+    if (launch_segments(p, a, LK_SWEEP2, G, s) != hipSuccess) return GMM_E_HIP;
     // range flags: sweep 1 wrote slots [0, G1), sweep 2 rewrote [0, G)
     return lk_sum(p, w, M, G1 > G ? G1 : G, ll_out, s);
 }
@@ -537,7 +563,7 @@ gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var
     const size_t shm = sizeof(double) * (size_t)p.ncols;
     hipLaunchKernelGGL(k_lk_reduce, dim3(p.k), dim3(256), shm, s, w.part, G, p.lk_slices, p.n,
                        (int)p.d, p.cov == GMM_COV_ISO, p.var_floor, w.dsc, w.stats, w.pi, w.mu,
-                       w.var, pi, mu, var, w.flags);
+                       w.var, pi, mu, var, w.flags, w.misc);
     return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 

@@ -40,6 +40,8 @@ struct Plan {
     int64_t ncols;                    // statistic columns per component
     int lk_slices;                    // large K: 256-component slices
     int lk_kpad;                      // large K: K padded to whole slices
+    int64_t seg_tiles;                // statistics passes: tiles per workgroup (or wave)
+                                      // and launch segment, 0 = the family's default
 };
 
 gmm_status make_plan(const gmm_desc* desc, Plan* plan);

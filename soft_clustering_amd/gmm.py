@@ -62,13 +62,23 @@ def _load():
     lib.gmm_status_str.restype = ctypes.c_char_p
     lib.gmm_version.argtypes = []
     lib.gmm_version.restype = ctypes.c_char_p
+    # calibration kernels (include/gmm_calib.h)
+    lib.gmm_calib_sink_bytes.argtypes = [ctypes.c_int]
+    lib.gmm_calib_sink_bytes.restype = ctypes.c_size_t
+    lib.gmm_calib_read.argtypes = [P, S, ctypes.c_int, P, P]
+    lib.gmm_calib_read.restype = ctypes.c_int
+    lib.gmm_calib_mfma.argtypes = [ctypes.c_int64, ctypes.c_int, P, P]
+    lib.gmm_calib_mfma.restype = ctypes.c_int
+    lib.gmm_calib_mfma_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.gmm_calib_mfma_flops.restype = ctypes.c_double
     return lib
 
 
 _lib = _load()
 
 EXPORTED = ("gmm_workspace_bytes", "gmm_prepare", "gmm_em_step", "gmm_finalize", "gmm_loglik",
-            "gmm_get_stats", "gmm_diagnostics", "gmm_status_str", "gmm_version")
+            "gmm_get_stats", "gmm_diagnostics", "gmm_status_str", "gmm_version",
+            "gmm_calib_sink_bytes", "gmm_calib_read", "gmm_calib_mfma", "gmm_calib_mfma_flops")
 
 
 def status_str(status: int) -> str:
@@ -191,3 +201,22 @@ class Gmm:
         """gmm_em_step then gmm_finalize (the finalize also prepares the next step)."""
         self.em_step(x, ll_out, stream)
         self.finalize(pi_out, mu_out, cov_out, stream)
+
+
+# --- calibration kernels (measured ceilings; include/gmm_calib.h) -----------
+def calib_sink(grid, device="cuda"):
+    return torch.empty(int(_lib.gmm_calib_sink_bytes(int(grid))), dtype=torch.uint8, device=device)
+
+
+def calib_read(buf, grid, sink, stream=None):
+    """Streaming read of every byte of the device tensor `buf` (launch only)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.gmm_calib_read(_ptr(buf), nbytes, int(grid), _ptr(sink), _stream(stream)),
+           "gmm_calib_read")
+    return nbytes // 16 * 16
+
+
+def calib_mfma(iters, grid, sink, stream=None):
+    """Register-resident fp16 MFMA chains (launch only); returns their flops."""
+    _check(_lib.gmm_calib_mfma(int(iters), int(grid), _ptr(sink), _stream(stream)), "gmm_calib_mfma")
+    return float(_lib.gmm_calib_mfma_flops(int(iters), int(grid)))

@@ -2,6 +2,7 @@
 rejects bad arguments on the host before launching anything.  CPU only: no
 call here reaches a kernel."""
 import ctypes
+import glob
 import os
 import re
 
@@ -13,18 +14,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "gmm.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gmm_[a-z_0-9]+)\s*\(", src)))
+    """Every gmm_* function declared in include/*.h."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gmm_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) >= 9
+    assert len(names) >= 13
     lib = ctypes.CDLL(gmm.LIB_PATH)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in gmm.h but not exported"
-    assert set(gmm.EXPORTED) <= set(names)
+        assert hasattr(lib, n), f"{n} declared in include/*.h but not exported"
+    assert set(gmm.EXPORTED) == set(names)
 
 
 def test_status_strings():

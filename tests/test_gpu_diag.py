@@ -29,7 +29,7 @@ def test_tiny_workload_ten_iterations(gmm_lib):
     for it in range(w.iters):
         ll, st, th = gpu_step(gm, xg, pi, mu, cov, prepare=False)
         ref = oracle.em_step(xd, params64("diag", pi, mu, cov))
-        check_step(ref, ll, st, th, what=f"iter {it}")
+        check_step(ref, ll, st, th, what=f"iter {it}", xd=xd)
         traj_gpu.append(ll)
         r_free = oracle.em_step(xd, p_ref)
         traj_ref.append(r_free.ll)
@@ -88,11 +88,11 @@ def test_ragged_shapes_one_step(gmm_lib, n, d, k, x_dtype, ldx_pad, misalign):
     pi, mu, cov = to_dev(*th0)
     ll, st, th = gpu_step(gm, xg, pi, mu, cov)
     ref = oracle.em_step(xd, params64("diag", pi, mu, cov))
-    check_step(ref, ll, st, th, what=f"n{n} d{d} k{k} {x_dtype}")
+    check_step(ref, ll, st, th, what=f"n{n} d{d} k{k} {x_dtype}", xd=xd)
     # second iteration from the GPU's parameters (finalize prepared them)
     ll2, st2, th2 = gpu_step(gm, xg, *th, prepare=False)
     ref2 = oracle.em_step(xd, params64("diag", *th))
-    check_step(ref2, ll2, st2, th2, what="  second step")
+    check_step(ref2, ll2, st2, th2, what="  second step", xd=xd)
 
 
 @pytest.mark.parametrize("n,d,k,x_dtype,ldx_pad,misalign", RAGGED[1:9:2])
@@ -157,7 +157,7 @@ def test_degenerate_cases(gmm_lib):
     ll, st, th = gpu_step(gm, torch.from_numpy(x).cuda(), pi, mu, cov)
     ref = oracle.em_step(x.astype(np.float64), params64("diag", pi, mu, cov))
     assert np.isfinite(ll)
-    check_step(ref, ll, st, th, what="outlier+empty")
+    check_step(ref, ll, st, th, what="outlier+empty", xd=x)
     dg = gm.diagnostics()
     assert dg.empty == 1 and dg.nonfinite == 0 and dg.bad_params == 0
     assert torch.equal(th[1][2].cpu(), mu[2].cpu()) and torch.equal(th[2][2].cpu(), cov[2].cpu())
@@ -188,7 +188,7 @@ def test_outlier_tiles_take_the_fp32_route(gmm_lib, x_dtype):
     pi, mu, cov = to_dev(*th0)
     ll, st, th = gpu_step(gm, xg, pi, mu, cov)
     ref = oracle.em_step(xd, params64("diag", pi, mu, cov))
-    check_step(ref, ll, st, th, what=f"outliers {x_dtype}")
+    check_step(ref, ll, st, th, what=f"outliers {x_dtype}", xd=xd)
     gm.prepare(pi, mu, cov)
     ll2 = torch.zeros(1, dtype=torch.float64, device="cuda")
     lse = torch.full((n,), float("nan"), device="cuda")
@@ -246,8 +246,9 @@ def test_full_size_diag_workload(gmm_lib):
     ll, st, th = gpu_step(gm, xg, pi, mu, cov)
     assert abs(st.s0.sum().item() - w.n) <= 1e-6 * w.n
     print("running the oracle on 1e6 points...", flush=True)
-    ref = oracle.em_step(x.double().numpy(), params64("diag", pi, mu, cov))
-    check_step(ref, ll, st, th, what="1e6 x 64 x 16")
+    xd = x.double().numpy()
+    ref = oracle.em_step(xd, params64("diag", pi, mu, cov))
+    check_step(ref, ll, st, th, what="1e6 x 64 x 16", xd=xd)
     # sampled points of the E-step
     lse = torch.empty(w.n, device="cuda")
     gm.prepare(pi, mu, cov)
