@@ -9,3 +9,6 @@ from .gmm_oracle import (  # noqa: F401
     log_normaliser, responsibilities, loglik, em_step, fit,
     DEFAULT_VAR_FLOOR, DEFAULT_RIDGE_REL, EMPTY_NK, LOG_2PI,
 )
+from .gmm_assign_fit import (  # noqa: F401
+    splitmix64, sample_distinct, init_random_points, assign_topm, fit_tol,
+)

@@ -83,3 +83,55 @@ class _quiet:
         self._e.__exit__(*a)
         self._w.__exit__(*a)
         return False
+
+
+# ---- the assignment / start / fit-loop module --------------------------------
+SRC_AF = os.path.join(os.path.dirname(SRC), "gmm_assign_fit.py")
+MUTANTS_AF = {
+    "topm_ties_high_index_first": ("np.lexsort((ks, -a[i]))", "np.lexsort((-ks, -a[i]))"),
+    "topm_ascending": ("np.lexsort((ks, -a[i]))", "np.lexsort((ks, a[i]))"),
+    "topm_gamma_without_lse": ("np.exp(a[i, order] - lse[i])", "np.exp(a[i, order])"),
+    "floyd_range_off_by_one": ("t = r % (j + 1)", "t = r % j if j else 0"),
+    "floyd_keeps_duplicate_draw": ("chosen.add(j if t in chosen else t)", "chosen.add(t)"),
+    "splitmix_shift": ("z = ((z ^ (z >> 30))", "z = ((z ^ (z >> 31))"),
+    "splitmix_no_increment": ("state = (state + GOLDEN) & MASK64", "state = state & MASK64"),
+    "fit_tolerance_not_per_point": ("abs(lls[-1] - lls[-2]) / n < tol", "abs(lls[-1] - lls[-2]) < tol"),
+    "fit_returns_previous_params": ("        p = r.params\n        if len(lls)", "        if len(lls)"),
+    "start_half_variance": ('"diag": np.ones((k, d)), "iso"', '"diag": 0.5 * np.ones((k, d)), "iso"'),
+}
+
+
+def load_mutant_af(name):
+    old, new = MUTANTS_AF[name]
+    src = open(SRC_AF).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    src = src.replace(old, new).replace("from .gmm_oracle import", "from oracle.gmm_oracle import")
+    modname = f"_oracle_af_mutant_{name}"
+    mod = types.ModuleType(modname)
+    mod.__file__ = SRC_AF
+    sys.modules[modname] = mod
+    try:
+        exec(compile(src, SRC_AF, "exec"), mod.__dict__)
+    except Exception:
+        del sys.modules[modname]
+        raise
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_AF))
+def test_assign_fit_mutant_is_caught(name):
+    import oracle
+    from tests import oracle_pins_assign_fit as P
+    mod = load_mutant_af(name)
+    failed = []
+    try:
+        for pin in P.ALL_PINS:
+            try:
+                with _quiet():
+                    pin(mod, oracle.gmm_oracle)
+            except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError, OverflowError,
+                    IndexError):
+                failed.append(pin.__name__)
+    finally:
+        sys.modules.pop(mod.__name__, None)
+    assert failed, f"mutant {name} passed every pin"
