@@ -143,6 +143,63 @@ gmm_status gmm_loglik(const gmm_desc* desc, void* ws, size_t ws_bytes,
                       const void* x, double* ll_out, float* point_lse,
                       int32_t* point_argmax, hipStream_t stream);
 
+/* Largest m of gmm_assign. */
+#define GMM_MAX_TOPM 16
+
+/* Top-m soft assignment under the prepared parameters (E-step only).
+ * [Flash-GMM] Key findings: the soft responsibilities let a point near a
+ * cluster boundary belong to several clusters; Deployment: the coarse
+ * quantiser of an IVF index assigns each vector to several lists.  For every
+ * point n the m components with the largest responsibility gamma_nk, in
+ * decreasing order (ties: the lower component index first), are written to
+ * out_idx[n*m + i] (device int32) and gamma_nk to out_gamma[n*m + i] (device
+ * fp32).  Components with log-joint -inf (zero weight) are never listed:
+ * columns past the listed components hold index -1 and 0.  1 <= m <=
+ * GMM_MAX_TOPM, else GMM_E_ARG.  ll_out (device double, nullable) gets the LL
+ * as gmm_loglik does.  N = 0 is allowed.  Large-K plans: the outputs also
+ * carry intermediate values between the passes over X of one call. */
+gmm_status gmm_assign(const gmm_desc* desc, void* ws, size_t ws_bytes, const void* x,
+                      int32_t m, int32_t* out_idx, float* out_gamma, double* ll_out,
+                      hipStream_t stream);
+
+/* Start of gmm_fit. */
+typedef enum {
+    GMM_INIT_GIVEN = 0,          /* theta_0 is read from pi / mu / cov */
+    GMM_INIT_RANDOM_POINTS = 1   /* K distinct rows of X (seeded) as means, unit
+                                    (co)variances, weights 1/K; needs K <= N */
+} gmm_init;
+
+typedef struct {
+    int32_t max_iter;   /* iterations at most, >= 1 */
+    int32_t init;       /* gmm_init */
+    uint64_t seed;      /* GMM_INIT_RANDOM_POINTS: generator state */
+    double tol;         /* stop after iteration t >= 1 once |LL_t - LL_t-1| / N < tol
+                           (0: run max_iter iterations) */
+    int32_t batch;      /* iterations launched between two host checks, >= 1 */
+    int32_t use_graph;  /* 1: capture one iteration into a HIP graph and replay it
+                           (needs a non-null stream) */
+} gmm_fit_opts;
+
+/* EM iterations to convergence ([Flash-GMM] Method, outputs: the fused step is
+ * called repeatedly until the log-likelihood converges; [LP-GMM] 1.1:
+ * training alternates E and M steps).  Iteration t = gmm_em_step (LL_t under
+ * theta_t) + gmm_finalize (theta_t+1); the loop stops after iteration t once
+ * t >= 1 and |LL_t - LL_t-1| / N < tol, after max_iter iterations, or on a
+ * non-finite LL (theta_t+1 is then not taken).  The device decides and
+ * records; the host synchronises once per `batch` iterations.
+ * GMM_INIT_RANDOM_POINTS draws K distinct rows with Floyd's K-subset
+ * algorithm (Bentley and Floyd, CACM 1987) from SplitMix64 (Steele, Lea and
+ * Flood, OOPSLA 2014) seeded with opts->seed, the draw in [0, j] being the
+ * output modulo j + 1, and writes that start into pi / mu / cov.
+ * pi / mu / cov: device fp32, in: theta_0 (GMM_INIT_GIVEN), out: the final
+ * theta.  ll_hist: device double [max_iter] (nullable), LL_t per iteration.
+ * n_iter: host (nullable), iterations taken.  Synchronous: returns after the
+ * loop, with the workspace prepared for the final theta.  Creates and
+ * destroys a HIP graph when use_graph is set; allocates no memory itself. */
+gmm_status gmm_fit(const gmm_desc* desc, void* ws, size_t ws_bytes, const void* x,
+                   const gmm_fit_opts* opts, float* pi, float* mu, float* cov,
+                   double* ll_hist, int32_t* n_iter, hipStream_t stream);
+
 /* Copy the sufficient statistics of the last EM iteration into device fp64
  * buffers (each nullable): s0 [K]; s1 [K*D]; s2 [K*D] (diag: sum gamma x^2),
  * [K] (iso: sum gamma |x|^2) or [K*D*D] (full: sum gamma x x^T).  The

@@ -83,7 +83,9 @@ def init_random_points(x: np.ndarray, k: int, seed: int, cov_type: str) -> Param
 def assign_topm(x: np.ndarray, p: Params, m: int, ridge_rel: float = DEFAULT_RIDGE_REL):
     """Per point the m components with the largest responsibilities, in
     decreasing order (ties: lower component index first), and those
-    responsibilities gamma_nk = exp(a_nk - lse_n).  Columns beyond K hold
+    responsibilities gamma_nk = exp(a_nk - lse_n).  A component whose
+    log-joint is -inf (zero weight) has responsibility exactly 0 and is not a
+    member: it is never listed.  Columns past the listed components hold
     index -1 and responsibility 0.  Returns (idx [N, m], gamma [N, m], lse [N])."""
     x = np.asarray(x, dtype=np.float64)
     a = log_joint(x, p, prepare(p, ridge_rel))
@@ -95,8 +97,9 @@ def assign_topm(x: np.ndarray, p: Params, m: int, ridge_rel: float = DEFAULT_RID
     take = min(m, kk)
     for i in range(n):
         order = np.lexsort((ks, -a[i]))[:take]   # primary: larger a; then lower k
-        idx[i, :take] = order
-        gam[i, :take] = np.exp(a[i, order] - lse[i])
+        order = order[np.isfinite(a[i, order])]
+        idx[i, :order.size] = order
+        gam[i, :order.size] = np.exp(a[i, order] - lse[i])
     return idx, gam, lse
 
 

@@ -100,6 +100,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_ll = take(sizeof(double));
         p->off_diag = take(sizeof(int) * (2 * p->k + 2));
         p->off_chunk = take(sizeof(double) * 4 * p->k * diag_chunks(*p));
+        p->off_ctl = take(fit_ctl_bytes(*p));
         p->total = off;
         return GMM_OK;
     }
@@ -128,15 +129,15 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         // panel: (features + 16 bias slots) / 16 MFMA steps x Kpad / 32 blocks x 64 lanes x 16 B
         p->off_panel = take((size_t)(((iso ? 1 : 2) * dp + 16) / 16) * (p->lk_kpad / 32) * 64 * 16);
         p->off_chunk = take(sizeof(float) * (p->lk_kpad + 4));
-        if (S > 1) {
-            p->off_lse = take(sizeof(float) * (size_t)S * p->n);
-            p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)S * p->n);
-        }
+        // per-(slice, point) LSE: the two sweeps, and top-m assignment at any S
+        p->off_lse = take(sizeof(float) * (size_t)S * p->n);
+        if (S > 1) p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)S * p->n);
         p->off_part = take(sizeof(double) * (size_t)p->p_max * kLkSlice * p->ncols);
         p->off_part_ll = take((sizeof(double) + sizeof(int)) * kLkLLSlots);
         p->off_stats = take(sizeof(double) * p->k * p->ncols);
         p->off_ll = take(sizeof(double));
         p->off_diag = take(sizeof(int) * (2 * p->k + 4));
+        p->off_ctl = take(fit_ctl_bytes(*p));
         p->total = off;
         return GMM_OK;
     }
@@ -162,6 +163,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_stats = take(sizeof(double) * p->k * p->ncols);
         p->off_ll = take(sizeof(double));
         p->off_diag = take(sizeof(int) * (2 * p->k + 4));
+        p->off_ctl = take(fit_ctl_bytes(*p));
         p->total = off;
         return GMM_OK;
     }
@@ -239,6 +241,19 @@ gmm_status gmm_loglik(const gmm_desc* desc, void* ws, size_t ws_bytes, const voi
     if (p.path == PATH_FULL)
         return full_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
     return diag_loglik(p, (char*)ws, x, ll_out, point_lse, point_argmax, stream);
+}
+
+gmm_status gmm_assign(const gmm_desc* desc, void* ws, size_t ws_bytes, const void* x, int32_t m,
+                      int32_t* out_idx, float* out_gamma, double* ll_out, hipStream_t stream) {
+    Plan p;
+    gmm_status st = make_plan(desc, &p);
+    if (st != GMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GMM_OK) return st;
+    if (m < 1 || m > GMM_MAX_TOPM) return GMM_E_ARG;
+    if (p.n > 0 && (x == nullptr || out_idx == nullptr || out_gamma == nullptr)) return GMM_E_ARG;
+    if (p.path == PATH_LARGEK) return lk_assign(p, (char*)ws, x, m, out_idx, out_gamma, ll_out, stream);
+    if (p.path == PATH_FULL) return full_assign(p, (char*)ws, x, m, out_idx, out_gamma, ll_out, stream);
+    return diag_assign(p, (char*)ws, x, m, out_idx, out_gamma, ll_out, stream);
 }
 
 gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes, double* s0,

@@ -75,11 +75,19 @@ inline DiagWs diag_ws(const Plan& p, char* ws) {
 // Number of workgroups (= partial slots) of the fused kernel for this plan.
 int diag_grid(const Plan& p);
 
+// Top-m output of the E-step alone (m = 0: none): out_idx / out_gamma [N][m].
+struct DiagTopm {
+    int m;
+    int* idx;
+    float* gamma;
+};
+
 // Launch the fused split-fp16 kernel (diag_split.hip): EM = statistics
 // partials (moments of y = (x - c) s, undone by the reduction); otherwise
-// E-step only with optional per-point outputs.  Either way the kernel
-// leaves the LL in the workspace and in ll_out (nullable).
+// E-step only with optional per-point outputs (LSE, argmax, top-m).  Either
+// way the kernel leaves the LL in the workspace and in ll_out (nullable).
 hipError_t diag_launch_split(const Plan& p, const DiagWs& w, const void* x, bool em, int grid,
-                             double* ll_out, float* lse, int* arg, hipStream_t s);
+                             double* ll_out, float* lse, int* arg, const DiagTopm& tm,
+                             hipStream_t s);
 
 }  // namespace gmm

@@ -278,7 +278,7 @@ static gmm_status sum_ll(const Plan& p, const DiagWs& w, int P, double* ll_out, 
 gmm_status diag_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
     DiagWs w = diag_ws(p, ws);
     const int P = diag_grid(p);
-    hipError_t e = diag_launch_split(p, w, x, true, P, ll_out, nullptr, nullptr, s);
+    hipError_t e = diag_launch_split(p, w, x, true, P, ll_out, nullptr, nullptr, DiagTopm{0, nullptr, nullptr}, s);
     return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
@@ -305,7 +305,16 @@ gmm_status diag_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
     DiagWs w = diag_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int P = diag_grid(p);
-    hipError_t e = diag_launch_split(p, w, x, false, P, ll_out, lse, argmax, s);
+    hipError_t e = diag_launch_split(p, w, x, false, P, ll_out, lse, argmax, DiagTopm{0, nullptr, nullptr}, s);
+    return e == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+gmm_status diag_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx, float* gamma,
+                       double* ll_out, hipStream_t s) {
+    DiagWs w = diag_ws(p, ws);
+    if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
+    const int P = diag_grid(p);
+    hipError_t e = diag_launch_split(p, w, x, false, P, ll_out, nullptr, nullptr, DiagTopm{m, idx, gamma}, s);
     return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 

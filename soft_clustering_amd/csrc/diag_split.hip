@@ -261,7 +261,8 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     float* __restrict__ scale, double* __restrict__ part, double* __restrict__ part_ll,
     unsigned* __restrict__ done, double* __restrict__ ll_ws, double* __restrict__ ll_out,
     int* __restrict__ nonfinite_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
-    int64_t tlo, int64_t thi, int seg_first) {
+    int64_t tlo, int64_t thi, int seg_first, int topm, int* __restrict__ out_idx,
+    float* __restrict__ out_gamma) {
     using S = SplitShape<DP, KB, XT>;
     constexpr int WAVES = S::kWaves, THREADS = S::kThreads;
     constexpr int KS = S::kKS, NCB = S::kNCB, EV = S::kEV, P = S::kPitch;
@@ -560,6 +561,34 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
                         best = row16_min_i(best);
                         if (j == 0 && valid[g2][r]) out_arg[pt] = best;
                     }
+                    if (topm > 0) {
+                        // the topm largest scores of the point (lower component first
+                        // on ties): repeated max over the 16 lanes of the row, the
+                        // lane holding the winner drops it from its candidates
+                        float cur[KB];
+#pragma unroll
+                        for (int b = 0; b < KB; ++b) cur[b] = 16 * b + j < k_real ? s[g2][b][r] : -INFINITY;
+                        for (int i = 0; i < topm; ++i) {
+                            float bv = -INFINITY;
+                            int bk = 0x7fffffff;
+#pragma unroll
+                            for (int b = 0; b < KB; ++b)
+                                if (cur[b] > bv) {
+                                    bv = cur[b];
+                                    bk = 16 * b + j;
+                                }
+                            const float mv = row16_max(bv);
+                            const int kb = row16_min_i(bv == mv ? bk : 0x7fffffff);
+#pragma unroll
+                            for (int b = 0; b < KB; ++b)
+                                if (16 * b + j == kb) cur[b] = -INFINITY;
+                            if (j == 0 && valid[g2][r]) {
+                                const bool live = mv != -INFINITY;
+                                out_idx[pt * topm + i] = live ? kb : -1;
+                                out_gamma[pt * topm + i] = live ? fast_exp2(mv - lse2) : 0.0f;
+                            }
+                        }
+                    }
                 }
             }
         ll2 += (double)tll;
@@ -720,7 +749,7 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
 // the waves' fp32 runs into the fp64 partial slots); E-step alone: one pass.
 template <int DP, int KB, typename XT, bool VEC, bool EM>
 hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, double* ll_out,
-                    float* lse, int* arg, hipStream_t s) {
+                    float* lse, int* arg, const DiagTopm& tm, hipStream_t s) {
     constexpr int W = diag_split_waves(DP, KB);
     const int64_t tiles = (p.n + kST - 1) / kST;
     const int64_t M = p.seg_tiles > 0 ? p.seg_tiles : kDiagSegTiles;
@@ -733,7 +762,7 @@ hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, dou
                            (const XT*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.pi, w.mu, w.var,
                            w.chunk_part, diag_chunks(p), w.panel, w.shift, w.scale, w.part, w.part_ll,
                            (unsigned*)w.done, w.ll, ll_out, w.nonfinite_ll, lse, arg, lo, hi,
-                           i == 0 ? 1 : 0);
+                           i == 0 ? 1 : 0, tm.m, tm.idx, tm.gamma);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -742,17 +771,17 @@ hipError_t launch_t(const Plan& p, const DiagWs& w, const void* x, int grid, dou
 
 template <int DP, int KB, bool EM>
 hipError_t launch_x(const Plan& p, const DiagWs& w, const void* x, bool vec, int grid,
-                    double* ll_out, float* lse, int* arg, hipStream_t s) {
+                    double* ll_out, float* lse, int* arg, const DiagTopm& tm, hipStream_t s) {
     switch (p.xdt) {
         case GMM_F32:
-            return vec ? launch_t<DP, KB, float, true, EM>(p, w, x, grid, ll_out, lse, arg, s)
-                       : launch_t<DP, KB, float, false, EM>(p, w, x, grid, ll_out, lse, arg, s);
+            return vec ? launch_t<DP, KB, float, true, EM>(p, w, x, grid, ll_out, lse, arg, tm, s)
+                       : launch_t<DP, KB, float, false, EM>(p, w, x, grid, ll_out, lse, arg, tm, s);
         case GMM_BF16:
-            return vec ? launch_t<DP, KB, bf16_t, true, EM>(p, w, x, grid, ll_out, lse, arg, s)
-                       : launch_t<DP, KB, bf16_t, false, EM>(p, w, x, grid, ll_out, lse, arg, s);
+            return vec ? launch_t<DP, KB, bf16_t, true, EM>(p, w, x, grid, ll_out, lse, arg, tm, s)
+                       : launch_t<DP, KB, bf16_t, false, EM>(p, w, x, grid, ll_out, lse, arg, tm, s);
         default:
-            return vec ? launch_t<DP, KB, _Float16, true, EM>(p, w, x, grid, ll_out, lse, arg, s)
-                       : launch_t<DP, KB, _Float16, false, EM>(p, w, x, grid, ll_out, lse, arg, s);
+            return vec ? launch_t<DP, KB, _Float16, true, EM>(p, w, x, grid, ll_out, lse, arg, tm, s)
+                       : launch_t<DP, KB, _Float16, false, EM>(p, w, x, grid, ll_out, lse, arg, tm, s);
     }
 }
 
@@ -765,12 +794,13 @@ bool x_vec_ok(const Plan& p, const void* x) {
 }  // namespace
 
 hipError_t diag_launch_split(const Plan& p, const DiagWs& w, const void* x, bool em, int grid,
-                             double* ll_out, float* lse, int* arg, hipStream_t s) {
+                             double* ll_out, float* lse, int* arg, const DiagTopm& tm,
+                             hipStream_t s) {
     const bool vec = x_vec_ok(p, x);
 #define CASE(DP_, KB_)                                                                          \
     if (p.dp == DP_ && p.kb == KB_)                                                             \
-        return em ? launch_x<DP_, KB_, true>(p, w, x, vec, grid, ll_out, lse, arg, s)          \
-                  : launch_x<DP_, KB_, false>(p, w, x, vec, grid, ll_out, lse, arg, s);
+        return em ? launch_x<DP_, KB_, true>(p, w, x, vec, grid, ll_out, lse, arg, tm, s)      \
+                  : launch_x<DP_, KB_, false>(p, w, x, vec, grid, ll_out, lse, arg, tm, s);
     GMM_DIAG_SHAPES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -69,13 +69,35 @@ static_assert(KP == 16, "four components per wave, four waves");
 
 // VEC: d % 8 == 0 and 16-byte aligned rows (whole-vector loads); otherwise
 // per-element loads.  A template parameter, so that each kernel holds one path.
+// The topm largest of a point's KP base-2 scores (lower component first on
+// ties) as (index, responsibility exp2(score - lse2)); index -1 and 0 once no
+// live component is left (padding components score -inf).
+__device__ __forceinline__ void write_topm(const float (&sv)[KP], float lse2, int topm, int64_t p,
+                                           int* __restrict__ out_idx, float* __restrict__ out_gamma) {
+    uint32_t taken = 0;
+    for (int i = 0; i < topm; ++i) {
+        float bv = -INFINITY;
+        int bk = -1;
+#pragma unroll
+        for (int k = 0; k < KP; ++k)
+            if (!((taken >> k) & 1u) && sv[k] > bv) {
+                bv = sv[k];
+                bk = k;
+            }
+        if (bk >= 0) taken |= 1u << bk;
+        out_idx[p * topm + i] = bk;
+        out_gamma[p * topm + i] = bk >= 0 ? fast_exp2(bv - lse2) : 0.0f;
+    }
+}
+
 template <int DP, bool EM, bool VEC>
 __global__ __launch_bounds__(256, 1) void k_full_fused(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
     double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
-    int64_t tlo, int64_t thi, int seg_first) {
+    int64_t tlo, int64_t thi, int seg_first, int topm, int* __restrict__ out_idx,
+    float* __restrict__ out_gamma) {
     using Sh = FullShape<DP>;
     constexpr int NB = Sh::kNB, NBLK = Sh::kNBlk;
     constexpr int NOB = Sh::kNOB, NKS = Sh::kNKS, DPO = Sh::kDPO, NV = Sh::kNV;
@@ -253,6 +275,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                         if (sv[k] == M) a = k;
                     out_arg[p] = a;
                 }
+                if (topm > 0) write_topm(sv, lse2, topm, p, out_idx, out_gamma);
             }
         }
 
@@ -375,7 +398,8 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
     double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
-    int64_t tlo, int64_t thi, int seg_first) {
+    int64_t tlo, int64_t thi, int seg_first, int topm, int* __restrict__ out_idx,
+    float* __restrict__ out_gamma) {
     using namespace pipe;
     __shared__ __attribute__((aligned(16))) uint32_t nm_s[KP][DP];     // (-mu, -mu) fp16 pairs
     __shared__ __attribute__((aligned(16))) float wb_s[KP][NOB][2][16];  // -W mu, accumulator layout
@@ -552,6 +576,7 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                             if (sv[k] == M) a = k;
                         out_arg[p] = a;
                     }
+                    if (topm > 0) write_topm(sv, lse2, topm, p, out_idx, out_gamma);
                 }
             }
             if constexpr (EM) {
@@ -655,35 +680,37 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
 
 template <int DP, bool VEC>
 hipError_t launch_dv(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
-                     int* arg, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
+                     int* arg, int64_t tlo, int64_t thi, int seg_first, const FullTopm& tm,
+                     hipStream_t s) {
     if (em)
         hipLaunchKernelGGL((k_full_fused<DP, true, VEC>), dim3(grid), dim3(256), 0, s,
                            (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
-                           w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first);
+                           w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first, 0, (int*)nullptr, (float*)nullptr);
     else
         hipLaunchKernelGGL((k_full_fused<DP, false, VEC>), dim3(grid), dim3(256), 0, s,
                            (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
-                           w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first);
+                           w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first, tm.m, tm.idx, tm.gamma);
     return hipGetLastError();
 }
 
 template <int DP>
 hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
-                     int* arg, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
+                     int* arg, int64_t tlo, int64_t thi, int seg_first, const FullTopm& tm,
+                     hipStream_t s) {
     const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
     if (DP == 64 && vec) {   // the pipelined kernel
         if (em)
             hipLaunchKernelGGL((k_full_pipe<true>), dim3(grid), dim3(pipe::kThreads), 0, s,
                                (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
-                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first);
+                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first, 0, (int*)nullptr, (float*)nullptr);
         else
             hipLaunchKernelGGL((k_full_pipe<false>), dim3(grid), dim3(pipe::kThreads), 0, s,
                                (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
-                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first);
+                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first, tm.m, tm.idx, tm.gamma);
         return hipGetLastError();
     }
-    return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s)
-               : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
+    return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s)
+               : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
 }
 
 }  // namespace
@@ -698,11 +725,11 @@ int full_grid(const Plan& p) {
 
 hipError_t full_launch_fused(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
                              float* lse, int* arg, int64_t tlo, int64_t thi, int seg_first,
-                             hipStream_t s) {
+                             const FullTopm& tm, hipStream_t s) {
     switch (p.dp) {
-        case 16: return launch_dp<16>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
-        case 32: return launch_dp<32>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
-        case 64: return launch_dp<64>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, s);
+        case 16: return launch_dp<16>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
+        case 32: return launch_dp<32>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
+        case 64: return launch_dp<64>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
     }
     return hipErrorInvalidValue;
 }

@@ -65,9 +65,14 @@ inline FullWs full_ws(const Plan& p, char* ws) {
 // statistics + LL partials (fp32 partials of this segment; the LL slot is
 // written by the first segment and added to by later ones); otherwise E-step
 // only with optional per-point outputs.
+struct FullTopm {   // top-m output of the E-step alone (m = 0: none), [N][m]
+    int m;
+    int* idx;
+    float* gamma;
+};
 hipError_t full_launch_fused(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
                              float* lse, int* arg, int64_t tlo, int64_t thi, int seg_first,
-                             hipStream_t s);
+                             const FullTopm& tm, hipStream_t s);
 int full_grid(const Plan& p);
 
 // Tiles (of kFullT points) one workgroup accumulates in fp32 before its run

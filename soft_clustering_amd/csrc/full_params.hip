@@ -539,7 +539,8 @@ gmm_status full_em_step(const Plan& p, char* ws, const void* x, double* ll_out, 
     const int ncolp = (int)full_ncolp(p.d);
     for (int i = 0; i < sg.n; ++i) {
         const int64_t lo = (int64_t)i * sg.len, hi = lo + sg.len < sg.tiles ? lo + sg.len : sg.tiles;
-        if (full_launch_fused(p, w, x, true, G, nullptr, nullptr, lo, hi, i == 0, s) != hipSuccess)
+        if (full_launch_fused(p, w, x, true, G, nullptr, nullptr, lo, hi, i == 0, FullTopm{0, nullptr, nullptr},
+                              s) != hipSuccess)
             return GMM_E_HIP;
         // every segment but the last is closed here; finalize adds the last one
         if (i + 1 < sg.n)
@@ -568,8 +569,19 @@ gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
     FullWs w = full_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int G = full_grid(p);
-    if (full_launch_fused(p, w, x, false, G, lse, argmax, 0, (p.n + kFullT - 1) / kFullT, 1, s) !=
-        hipSuccess)
+    if (full_launch_fused(p, w, x, false, G, lse, argmax, 0, (p.n + kFullT - 1) / kFullT, 1,
+                          FullTopm{0, nullptr, nullptr}, s) != hipSuccess)
+        return GMM_E_HIP;
+    return sum_ll(p, w, G, ll_out, s);
+}
+
+gmm_status full_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx, float* gamma,
+                       double* ll_out, hipStream_t s) {
+    FullWs w = full_ws(p, ws);
+    if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
+    const int G = full_grid(p);
+    if (full_launch_fused(p, w, x, false, G, nullptr, nullptr, 0, (p.n + kFullT - 1) / kFullT, 1,
+                          FullTopm{m, idx, gamma}, s) != hipSuccess)
         return GMM_E_HIP;
     return sum_ll(p, w, G, ll_out, s);
 }

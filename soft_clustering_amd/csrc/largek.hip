@@ -142,7 +142,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     constexpr int RG = KW;                      // halves per row of the responsibility tile
     constexpr int IPT = (Sh::kItems + NT - 1) / NT;   // staging items per thread
     constexpr bool kStats = MODE == LK_FUSED_EM || MODE == LK_SWEEP2;
-    constexpr bool kExchange = MODE != LK_SWEEP2;
+    constexpr bool kExchange = MODE != LK_SWEEP2 && MODE != LK_TOPM;
+    constexpr bool kTopm = MODE == LK_TOPM;
     // diagonal statistics at D = 128: the accumulators fill the AGPRs, so the
     // y'^2 half of the panel (KL steps) is kept in LDS instead of registers
     constexpr bool kTight = kStats && !kIso && DP == 128;
@@ -157,13 +158,22 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     __shared__ float2 wpart[WV][kT];   // per-wave (max, sum) of each point, base-2 score units
     __shared__ int warg[WV][kT];
     __shared__ double llred[NT];
+    // top-m mode: the slice's base-2 scores of the tile, each point's partial
+    // lists (8 threads per point, 32 components each) and the running list
+    // of the earlier slices (list 8), and the heads of the 9 sorted lists
+    __shared__ float stile[kTopm ? kT : 1][kTopm ? kLkSlice + 1 : 1];
+    __shared__ float2 cand[kTopm ? kT : 1][kTopm ? 9 : 1][kTopm ? kLkMaxTopm : 1];
+    __shared__ int8_t chead[kTopm ? kT : 1][kTopm ? 9 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int pn = lane & 31, hf = lane >> 5;           // point column, wave half
     const int gq = lane >> 4, gi = lane & 15;           // 16-lane group, lane in group
     const int G = gridDim.x, S = a.S;
     int slice, chunk;
-    {
+    if constexpr (kTopm) {
+        slice = a.topm_slice;
+        chunk = blockIdx.x;
+    } else {
         const int b = blockIdx.x;
         if (G % (8 * S) == 0) {
             const int r = b >> 3;
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
             chunk = b / S;
         }
     }
-    const int nchunks = G / S;
+    const int nchunks = kTopm ? G : G / S;
     const int kbase = slice * kLkSlice + w * KW;
     const int64_t n = a.n;
     const int d = a.d;
@@ -252,6 +262,74 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     };
     // sweep 2: merged LSE of point pn of tile t (+inf beyond N: gamma = 0)
     auto load_lse = [&](int64_t t) { const int64_t p = t * kT + pn; return p < n ? a.lse_in[p] : INFINITY; };
+
+    // Top-m of the tile's points over this slice, merged with the running
+    // list of the slices before it (the outputs).  An entry is better when its
+    // score is larger, or equal with a lower component index; components
+    // scoring -inf (zero weight, padding) are never listed.  Thread (p, q),
+    // p = tid / 8, first selects the best m of components 32 q .. 32 q + 31;
+    // thread p < 32 then merges the 8 sorted lists and the running one.
+    auto topm_tile = [&](int64_t prow) {
+        const int m = a.topm;
+        {
+            const int pt = tid >> 3, q = tid & 7;
+            uint32_t taken = 0;
+            for (int i = 0; i < m; ++i) {
+                float bv = -INFINITY;
+                int bc = -1;
+                for (int c = 0; c < 32; ++c) {
+                    const float v = stile[pt][32 * q + c];
+                    if (!((taken >> c) & 1u) && v > bv) {
+                        bv = v;
+                        bc = c;
+                    }
+                }
+                if (bc >= 0) taken |= 1u << bc;
+                const int kg = bc >= 0 ? slice * kLkSlice + 32 * q + bc : -1;
+                cand[pt][q][i] = make_float2(bv, __int_as_float(kg));
+            }
+            if (q == 0) {
+                const int64_t pg = prow + pt;
+                for (int i = 0; i < m; ++i) {
+                    float2 e = make_float2(-INFINITY, __int_as_float(-1));
+                    if (slice > 0 && pg < n) {
+                        const int kr = a.out_idx[pg * m + i];
+                        if (kr >= 0) e = make_float2(a.out_gamma[pg * m + i], __int_as_float(kr));
+                    }
+                    cand[pt][8][i] = e;
+                }
+            }
+            if (tid < kT)
+                for (int l = 0; l < 9; ++l) chead[tid][l] = 0;
+        }
+        __syncthreads();
+        if (tid < kT) {
+            const int pt = tid;
+            const int64_t pg = prow + pt;
+            const bool last = slice == a.S - 1;
+            const float lse2 = (last && pg < n) ? a.lse_in[pg] : 0.0f;
+            for (int i = 0; i < m; ++i) {
+                float bv = -INFINITY;
+                int bk = -1, bl = -1;
+                for (int l = 0; l < 9; ++l) {
+                    const int h = chead[pt][l];
+                    if (h >= m) continue;
+                    const float2 e = cand[pt][l][h];
+                    const int k = __float_as_int(e.y);
+                    if (k >= 0 && (e.x > bv || (e.x == bv && (bk < 0 || k < bk)))) {
+                        bv = e.x;
+                        bk = k;
+                        bl = l;
+                    }
+                }
+                if (bl >= 0) chead[pt][bl] = (int8_t)(chead[pt][bl] + 1);
+                if (pg < n) {
+                    a.out_idx[pg * m + i] = bk;
+                    a.out_gamma[pg * m + i] = bk < 0 ? 0.0f : (last ? fast_exp2(bv - lse2) : bv);
+                }
+            }
+        }
+    };
 
     // isotropic bias slots of a row, [yh, yl, yh, 1, 1, 0...]: this lane's 16 / kCB of them
     constexpr int kSlots = 16 / Sh::kCB;
@@ -444,6 +522,11 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                         acb[cb] = min(bi, __shfl_xor(bi, 32, 64));
                     }
                 }
+            } else if constexpr (kTopm) {
+                // base-2 scores of the slice's components -> LDS [point][component]
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    stile[pn][w * KW + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)] = F * sc[r];
             } else {
                 // sweep 2: gamma = exp2(S - lse) (lse = +inf beyond N) -> LDS [point][component]
 #pragma unroll
@@ -523,6 +606,11 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                     }
                 }
             }
+        }
+
+        if constexpr (kTopm) {
+            __syncthreads();   // the tile's scores are in stile
+            topm_tile(prow);
         }
 
         // ---- statistics MFMAs from the responsibility tile (wave-private)
@@ -664,6 +752,7 @@ hipError_t launch1(const Plan& p, const LkArgs& a, int mode, int grid, hipStream
         case LK_SWEEP1: return launch2<COV, LK_SWEEP1>(p, a, grid, s);
         case LK_SWEEP2: return launch2<COV, LK_SWEEP2>(p, a, grid, s);
         case LK_FUSED_E: return launch2<COV, LK_FUSED_E>(p, a, grid, s);
+        case LK_TOPM: return launch2<COV, LK_TOPM>(p, a, grid, s);
     }
     return hipErrorInvalidValue;
 }

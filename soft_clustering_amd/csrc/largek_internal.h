@@ -19,7 +19,12 @@ enum LkMode : int {
     LK_SWEEP1 = 1,     // per (slice, point) base-2 LSE (+ argmax) over the slice
     LK_SWEEP2 = 2,     // merge the slices' LSE, statistics of this slice
     LK_FUSED_E = 3,    // K fits one slice: E-step only (LL, per-point outputs)
+    LK_TOPM = 4,       // one slice per launch: the m largest responsibilities per
+                       // point, merged with those of the slices before it
 };
+
+// Largest m of gmm_assign.
+constexpr int kLkMaxTopm = 16;
 
 // fp16 operand range: squares and entries are clamped / scaled below this.
 constexpr float kF16Max = 65504.0f;
@@ -51,7 +56,8 @@ struct LkWs {
     float* kmax;                 // [Kpad] largest panel magnitude of each component
     float* prm;                  // [4] panel scale F = 2^f, |y|^2 scale 2^-g, 2^g, unused
     float* part_lse;             // [S][N] base-2 LSE of each slice; row 0 is then
-                                 // overwritten with the merged LSE (two-sweep only)
+                                 // overwritten with the merged LSE (two sweeps, and
+                                 // top-m assignment at any S)
     int* part_arg;               // [S][N] argmax within each slice (two-sweep only)
     float* part_max;             // [S][N] largest score within each slice
     double *part, *part_ll;      // per-workgroup partials
@@ -73,7 +79,7 @@ inline LkWs lk_ws(const Plan& p, char* ws) {
     w.kmax = (float*)(ws + p.off_chunk);
     w.prm = w.kmax + p.lk_kpad;
     const bool two = p.lk_slices > 1;
-    w.part_lse = two ? (float*)(ws + p.off_lse) : nullptr;
+    w.part_lse = (float*)(ws + p.off_lse);
     w.part_arg = two ? (int*)(ws + p.off_arg) : nullptr;
     w.part_max = two ? (float*)(w.part_arg + (size_t)p.lk_slices * p.n) : nullptr;
     w.part = (double*)(ws + p.off_part);
@@ -108,6 +114,12 @@ struct LkArgs {
     // segment writes the partial slots, later ones add to them
     int64_t tlo, thi;
     int seg_first;
+    // top-m mode: slice of this launch, m, outputs [N][m] (between slices
+    // out_gamma holds base-2 scores; the last slice turns them into
+    // responsibilities with lse_in)
+    int topm, topm_slice;
+    int* out_idx;
+    float* out_gamma;
 };
 
 // Segments of a statistics pass: tiles split into `nseg` ranges of nearly

@@ -513,7 +513,7 @@ gmm_status lk_sum(const Plan& p, const LkWs& w, int P, int Pf, double* ll_out, h
 // each chunk's slices share an XCD; never more chunks than tiles, partial
 // slots (statistics modes) or LL / flag slots.
 int lk_grid(const Plan& p, int mode) {
-    const int S = p.lk_slices;
+    const int S = mode == LK_TOPM ? 1 : p.lk_slices;   // top-m: one slice per launch
     const int64_t tiles = (p.n + kLkT - 1) / kLkT;
     int64_t chunks = (int64_t)lk_wg_per_cu(mode) * device_cu_count() / S;
     if (chunks >= 8) chunks = chunks / 8 * 8;
@@ -565,6 +565,36 @@ gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var
                        (int)p.d, p.cov == GMM_COV_ISO, p.var_floor, w.dsc, w.stats, w.pi, w.mu,
                        w.var, pi, mu, var, w.flags, w.misc);
     return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
+}
+
+// Top-m assignment: sweep 1 and the slice merge give every point's LSE, then
+// one top-m launch per slice, each merging its slice's candidates into the
+// running list (the outputs) in slice order.
+gmm_status lk_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx, float* gamma,
+                     double* ll_out, hipStream_t s) {
+    LkWs w = lk_ws(p, ws);
+    if (p.n == 0) return lk_sum(p, w, 0, 0, ll_out, s);
+    if (refresh_panel(p, w, x, s) != hipSuccess) return GMM_E_HIP;
+    LkArgs a = make_args(p, w, x);
+    const int G1 = lk_grid(p, LK_SWEEP1);
+    a.part_lse = w.part_lse;
+    if (lk_launch(p, a, LK_SWEEP1, G1, s) != hipSuccess) return GMM_E_HIP;
+    const int M = merge_grid(p);
+    hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
+                       (const int*)nullptr, (const float*)nullptr, w.part_ll, (float*)nullptr,
+                       (int*)nullptr);
+    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
+    a.part_lse = nullptr;
+    a.lse_in = w.part_lse;
+    a.topm = m;
+    a.out_idx = idx;
+    a.out_gamma = gamma;
+    const int GT = lk_grid(p, LK_TOPM);
+    for (int sl = 0; sl < p.lk_slices; ++sl) {
+        a.topm_slice = sl;
+        if (lk_launch(p, a, LK_TOPM, GT, s) != hipSuccess) return GMM_E_HIP;
+    }
+    return lk_sum(p, w, M, G1 > GT ? G1 : GT, ll_out, s);
 }
 
 gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,

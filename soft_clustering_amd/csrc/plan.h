@@ -36,6 +36,7 @@ struct Plan {
                                       // large K: per-component score constants
     size_t off_lse, off_arg;          // large K, two sweeps: per-(slice, point) LSE,
                                       // argmax and maximum
+    size_t off_ctl;                   // gmm_fit control block and the start's indices
     size_t total;
     int64_t ncols;                    // statistic columns per component
     int lk_slices;                    // large K: 256-component slices
@@ -48,6 +49,9 @@ gmm_status make_plan(const gmm_desc* desc, Plan* plan);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Bytes of the gmm_fit control block (fit.hip).
+size_t fit_ctl_bytes(const Plan& p);
+
 // Entry points of the diagonal family (diag_params.hip, diag_split.hip).
 gmm_status diag_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
                         const float* var, hipStream_t s);
@@ -56,6 +60,8 @@ gmm_status diag_finalize(const Plan& p, char* ws, float* pi, float* mu, float* v
                          hipStream_t s);
 gmm_status diag_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
                        int32_t* argmax, hipStream_t s);
+gmm_status diag_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx, float* gamma,
+                       double* ll_out, hipStream_t s);
 int device_cu_count();
 
 // Entry points of the large-K family (largek_params.hip, largek.hip).
@@ -66,6 +72,8 @@ gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var
                        hipStream_t s);
 gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
                      int32_t* argmax, hipStream_t s);
+gmm_status lk_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx, float* gamma,
+                     double* ll_out, hipStream_t s);
 
 // Entry points of the full-covariance family (full_params.hip, full_fused.hip).
 gmm_status full_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
@@ -75,5 +83,7 @@ gmm_status full_finalize(const Plan& p, char* ws, float* pi, float* mu, float* c
                          hipStream_t s);
 gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, float* lse,
                        int32_t* argmax, hipStream_t s);
+gmm_status full_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx, float* gamma,
+                       double* ll_out, hipStream_t s);
 
 }  // namespace gmm

@@ -33,6 +33,14 @@ class Desc(ctypes.Structure):
                 ("var_floor", ctypes.c_float), ("ridge_rel", ctypes.c_float)]
 
 
+class FitOpts(ctypes.Structure):
+    _fields_ = [("max_iter", ctypes.c_int32), ("init", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("tol", ctypes.c_double), ("batch", ctypes.c_int32), ("use_graph", ctypes.c_int32)]
+
+
+INIT = {"given": 0, "random_points": 1}
+
+
 class Diag(ctypes.Structure):
     _fields_ = [("bad_params", ctypes.c_int32), ("not_pd", ctypes.c_int32),
                 ("ridge_retries", ctypes.c_int32), ("empty", ctypes.c_int32),
@@ -53,6 +61,8 @@ def _load():
         "gmm_loglik": [D, P, S, P, P, P, P, P],
         "gmm_get_stats": [D, P, S, P, P, P, P],
         "gmm_diagnostics": [D, P, S, ctypes.POINTER(Diag), P],
+        "gmm_assign": [D, P, S, P, ctypes.c_int32, P, P, P, P],
+        "gmm_fit": [D, P, S, P, ctypes.POINTER(FitOpts), P, P, P, P, ctypes.POINTER(ctypes.c_int32), P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -77,7 +87,7 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("gmm_workspace_bytes", "gmm_prepare", "gmm_em_step", "gmm_finalize", "gmm_loglik",
-            "gmm_get_stats", "gmm_diagnostics", "gmm_status_str", "gmm_version",
+            "gmm_assign", "gmm_fit", "gmm_get_stats", "gmm_diagnostics", "gmm_status_str", "gmm_version",
             "gmm_calib_sink_bytes", "gmm_calib_read", "gmm_calib_mfma", "gmm_calib_mfma_flops")
 
 
@@ -177,6 +187,41 @@ class Gmm:
         _check(_lib.gmm_loglik(ctypes.byref(self.desc), ws, nb, _ptr(x) if self.n > 0 else None,
                                _ptr(ll_out), _ptr(point_lse), _ptr(point_argmax), _stream(stream)),
                "gmm_loglik")
+
+    def assign(self, x, m, out_idx=None, out_gamma=None, ll_out=None, stream=None):
+        """Top-m soft assignment: (idx int32 [n, m], gamma fp32 [n, m])."""
+        if self.n > 0:
+            self._check_x(x)
+        if out_idx is None:
+            out_idx = torch.empty((self.n, m), dtype=torch.int32, device=self.device)
+        if out_gamma is None:
+            out_gamma = torch.empty((self.n, m), dtype=torch.float32, device=self.device)
+        ws, nb = self._ws()
+        _check(_lib.gmm_assign(ctypes.byref(self.desc), ws, nb, _ptr(x) if self.n > 0 else None,
+                               int(m), _ptr(out_idx), _ptr(out_gamma), _ptr(ll_out), _stream(stream)),
+               "gmm_assign")
+        return out_idx, out_gamma
+
+    def fit(self, x, pi, mu, cov, max_iter=100, tol=1e-6, init="given", seed=0, batch=8,
+            use_graph=True, ll_hist=None, stream=None):
+        """EM to convergence; pi / mu / cov (device fp32) are the start (init
+        "given") and receive the final parameters.  Returns (iterations, LL per
+        iteration as a device fp64 tensor [max_iter])."""
+        self._check_x(x)
+        for t in (pi, mu, cov):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError("parameters must be contiguous fp32 device tensors")
+        if ll_hist is None:
+            ll_hist = torch.full((max_iter,), float("nan"), dtype=torch.float64, device=self.device)
+        opts = FitOpts(int(max_iter), INIT[init], int(seed) & ((1 << 64) - 1), float(tol), int(batch),
+                       1 if use_graph else 0)
+        nit = ctypes.c_int32(0)
+        if stream is None and use_graph:
+            stream = torch.cuda.current_stream()
+        ws, nb = self._ws()
+        _check(_lib.gmm_fit(ctypes.byref(self.desc), ws, nb, _ptr(x), ctypes.byref(opts), _ptr(pi), _ptr(mu),
+                            _ptr(cov), _ptr(ll_hist), ctypes.byref(nit), _stream(stream)), "gmm_fit")
+        return int(nit.value), ll_hist
 
     def get_stats(self, stream=None) -> Stats:
         f64 = dict(dtype=torch.float64, device=self.device)

@@ -95,6 +95,12 @@ def pin_topm(A, O):
         # beyond K: empty columns
         idx9, gam9, _ = A.assign_topm(x[:10], p, k + 2, ridge_rel=0.0)
         assert np.all(idx9[:, k:] == -1) and np.all(gam9[:, k:] == 0.0)
+    # a zero-weight component (log-joint -inf) is never listed
+    x, p = _problem(O, "iso", k=3, seed=7)
+    p.pi[1] = 0.0
+    p.pi /= p.pi.sum()
+    idx, gam, _ = A.assign_topm(x[:20], p, 3)
+    assert np.all(idx[:, :2] != 1) and np.all(idx[:, 2] == -1) and np.all(gam[:, 2] == 0.0)
     # identical components: equal responsibilities, lower index first
     x, p = _problem(O, "diag", k=3, seed=6)
     p.mu[2], p.cov[2], p.pi[2] = p.mu[0], p.cov[0], p.pi[0]

@@ -78,21 +78,23 @@ def test_workspace_has_no_nk_term():
     ("full", "f16", 10 ** 6, 64, 16),          # full covariance
 ])
 def test_workspace_far_below_nk(cov, x_dtype, n, d, k):
-    """The benchmark workloads' workspaces: the single-sweep and full paths
-    do not grow with N (per-workgroup partial slots are capped); the two-sweep
-    path keeps 12 bytes per point and 256-component slice, a small fraction of
-    the fp32 N x K matrix it replaces."""
+    """The benchmark workloads' workspaces: the full path does not grow with N
+    (per-workgroup partial slots are capped); the large-K paths keep one fp32
+    LSE per point and 256-component slice (top-m assignment and the two
+    sweeps), plus an argmax and a maximum when there are several slices: 4 or
+    12 bytes per point and slice, a small fraction of the fp32 N x K matrix."""
     ws = gmm.workspace_bytes(gmm.make_desc(n, d, k, cov, x_dtype))
     if cov == "full":   # O(P K D^2): 256 partial slots of 16 x (1 + D + D(D+1)/2) fp64
         assert ws <= 256 * 16 * (1 + d + d * (d + 1) // 2) * 8 + (8 << 20), ws
     else:
         assert ws < n * k * 4 / 20, (ws, n * k * 4)
     ws10 = gmm.workspace_bytes(gmm.make_desc(10 * n, d, k, cov, x_dtype))
-    if k <= 256:
+    if cov == "full":
         assert ws10 == ws
     else:
         slices = (k + 255) // 256
-        assert ws10 - ws == 9 * n * 12 * slices + (ws10 - ws) % 256   # linear in N, 12 B/point/slice
+        per = 4 if slices == 1 else 12
+        assert ws10 - ws == 9 * n * per * slices + (ws10 - ws) % 256   # linear in N
 
 
 def test_null_arguments_rejected_before_launch():

@@ -1,0 +1,152 @@
+"""gmm_assign: the m largest responsibilities of every point ([Flash-GMM] Key
+findings and Deployment: multi-cluster assignment), against the oracle's
+assign_topm on the same stored X and parameters.
+
+Per point and rank the component must be the oracle's, or a near-tie of it:
+both orders are then correct within the score precision, so the check is
+that the oracle's log-joints of the two components differ by at most GAP
+nats.  The responsibility reported for the component the GPU chose must match
+the oracle's responsibility of that component.  Exact rank-by-rank agreement
+must reach the argmax bar of the path (fp32: every non-tie; fp16 operands:
+the pages' 99.5 %).  Also: m = 1 reproduces gmm_loglik's argmax bit for bit,
+the responsibilities are non-increasing along a row, and m >= K lists every
+live component with responsibilities summing to 1.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from soft_clustering_amd import synth
+from tests.gpu_common import params64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (gap nats, |d gamma|, exact agreement) per arithmetic
+BARS = {"f32": (1e-2, 2e-4, 0.999), "f16ops": (0.5, 6e-2, 0.995)}
+
+
+def _make(n, d, k, cov, x_dtype, seed, spread=5.0):
+    rng = np.random.default_rng(seed)
+    kt = max(1, min(k, 48))
+    mu_t = rng.uniform(-spread, spread, size=(kt, d))
+    z = rng.integers(0, kt, size=n)
+    if cov == "full":
+        xf = mu_t[z] + rng.standard_normal((n, d)) @ (0.3 * rng.standard_normal((d, d)) + np.eye(d))
+    else:
+        xf = mu_t[z] + rng.standard_normal((n, d)) * rng.uniform(0.5, 1.5, size=(kt, d))[z]
+    xt = torch.from_numpy(xf.astype(np.float32)).to(synth.torch_dtype(x_dtype))
+    idx = rng.choice(n, size=k, replace=False)
+    mu0 = xt[torch.as_tensor(idx)].float().numpy()
+    pi0 = rng.dirichlet(np.ones(k)).astype(np.float32)
+    if cov == "diag":
+        cv = rng.uniform(0.5, 2.0, size=(k, d))
+    elif cov == "iso":
+        cv = rng.uniform(0.5, 2.0, size=k)
+    else:
+        cv = np.tile(np.eye(d), (k, 1, 1)) * rng.uniform(0.5, 2.0, size=(k, 1, 1))
+    return xt, (pi0, mu0, cv.astype(np.float32))
+
+
+def check_assign(gm, xg, xd, th, cov, m, bar, what):
+    gap, dg, agree_min = bar
+    idx, gam = gm.assign(xg, m)
+    ll = torch.zeros(1, dtype=torch.float64, device="cuda")
+    arg = torch.full((gm.n,), -1, dtype=torch.int32, device="cuda")
+    gm.loglik(xg, ll, None, arg)
+    torch.cuda.synchronize()
+    idx, gam, arg = idx.cpu().numpy(), gam.cpu().numpy(), arg.cpu().numpy()
+    p = params64(cov, *th)
+    ridx, rgam, lse = oracle.assign_topm(xd, p, m)
+    a = oracle.log_joint(xd, p, oracle.prepare(p))
+    # m = 1 is the E-step's argmax, bit for bit
+    assert np.array_equal(idx[:, 0], arg), what
+    same = idx == ridx
+    agree = float(np.mean(same))
+    rows, cols = np.nonzero(~same)
+    bad = []
+    for r, c in zip(rows, cols):
+        kg, kr = idx[r, c], ridx[r, c]
+        if kg < 0 or kr < 0:
+            bad.append((r, c, kg, kr))
+        elif abs(a[r, kg] - a[r, kr]) > gap:
+            bad.append((r, c, kg, kr, a[r, kg] - a[r, kr]))
+    live = idx >= 0
+    g_ref = np.where(live, np.exp(np.take_along_axis(a, np.maximum(idx, 0), axis=1) - lse[:, None]), 0.0)
+    derr = float(np.max(np.abs(gam - g_ref)))
+    print(f"{what}: rank agreement {agree * 100:.3f}%, non-tie mismatches {len(bad)}, "
+          f"max |d gamma| {derr:.2e}", flush=True)
+    assert not bad, (what, bad[:5])
+    assert agree >= agree_min, (what, agree)
+    assert derr <= dg, (what, derr)
+    assert np.all(np.diff(gam, axis=1) <= 1e-6 + 1e-6 * gam[:, :-1]), what
+    if m >= p.k:
+        np.testing.assert_allclose(gam.sum(axis=1), 1.0, rtol=0, atol=1e-3 if bar is BARS["f32"] else 5e-2)
+    return agree
+
+
+CASES = [
+    # n, d, k, cov, x_dtype, m
+    (3001, 16, 5, "diag", "f32", 8),        # m > K: trailing -1
+    (4097, 64, 16, "diag", "f32", 3),
+    (2000, 32, 64, "diag", "bf16", 4),
+    (1, 8, 3, "diag", "f32", 2),
+    (3000, 48, 100, "iso", "bf16", 4),       # large K, one slice
+    (2500, 64, 600, "diag", "f16", 5),       # large K, three slices
+    (1800, 128, 1024, "diag", "bf16", 16),   # four slices, largest m
+    (777, 32, 300, "iso", "f16", 1),
+    (3000, 32, 16, "full", "f16", 4),
+    (2000, 64, 9, "full", "f16", 12),        # m > K
+]
+
+
+@pytest.mark.parametrize("n,d,k,cov,x_dtype,m", CASES,
+                         ids=[f"n{a}-d{b}-k{c}-{e}-{f}-m{g}" for a, b, c, e, f, g in CASES])
+def test_assign_topm(gmm_lib, n, d, k, cov, x_dtype, m):
+    xt, th0 = _make(n, d, k, cov, x_dtype, seed=n + 7 * k + m)
+    gm = gmm_lib.Gmm(n, d, k, cov, x_dtype)
+    th = to_dev(*th0)
+    gm.prepare(*th)
+    bar = BARS["f32"] if (x_dtype == "f32" and cov == "diag") or (cov == "diag" and k <= 64) else BARS["f16ops"]
+    check_assign(gm, xt.cuda(), xt.double().numpy(), th, cov, m, bar, f"n{n} d{d} k{k} {cov} {x_dtype} m{m}")
+
+
+def test_assign_zero_weight_component_not_listed(gmm_lib):
+    xt, (pi0, mu0, cv) = _make(1000, 16, 6, "diag", "f32", seed=3)
+    pi0[2] = 0.0
+    pi0 /= pi0.sum()
+    gm = gmm_lib.Gmm(1000, 16, 6, "diag", "f32")
+    th = to_dev(pi0, mu0, cv)
+    gm.prepare(*th)
+    idx, gam = gm.assign(xt.cuda(), 6)
+    idx = idx.cpu().numpy()
+    assert not np.any(idx == 2) and np.all(idx[:, 5] == -1)
+    check_assign(gm, xt.cuda(), xt.double().numpy(), th, "diag", 6, BARS["f32"], "zero weight")
+
+
+def test_assign_full_size_workload(gmm_lib):
+    """2e8 points, D = 128, K = 1024 (the benchmark's mixture), m = 4: the
+    per-point lists on sampled points against the oracle, and the rank-1
+    column against the E-step's argmax over all points."""
+    w = synth.WORKLOADS["diag-bf16-n2e8-d128-k1024"]
+    mix = synth.make_mixture(w)
+    print(f"sampling {w.n} points on the GPU...", flush=True)
+    xg = synth.sample_points(w, mix, device="cuda")
+    th = to_dev(*synth.init_params(w, xg))
+    gm = gmm_lib.Gmm(w.n, w.d, w.k, w.cov, w.x_dtype)
+    gm.prepare(*th)
+    idx, gam = gm.assign(xg, 4)
+    arg = torch.full((w.n,), -1, dtype=torch.int32, device="cuda")
+    gm.loglik(xg, None, None, arg)
+    torch.cuda.synchronize()
+    assert torch.equal(idx[:, 0], arg)
+    s = np.sort(np.random.default_rng(1).choice(w.n, 2000, replace=False))
+    st = torch.as_tensor(s, device="cuda")
+    xs = xg[st].double().cpu().numpy()
+    p = params64(w.cov, *th)
+    ridx, rgam, _ = oracle.assign_topm(xs, p, 4)
+    agree = float(np.mean(idx[st].cpu().numpy() == ridx))
+    derr = float(np.max(np.abs(gam[st].cpu().numpy() - rgam)[idx[st].cpu().numpy() == ridx]))
+    print(f"full size: rank agreement {agree * 100:.2f}% on 2000 sampled points, max |d gamma| {derr:.2e}",
+          flush=True)
+    assert agree >= 0.995 and derr <= BARS["f16ops"][1]
