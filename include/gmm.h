@@ -212,6 +212,25 @@ gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes,
 gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes,
                            gmm_diag* out /* host */, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one EM
+ * iteration, gmm_prepare(pi, mu, cov) + gmm_em_step(x) + gmm_finalize, with no
+ * workspace argument and no allocation.  The workspace is a fixed device
+ * array of gmm_noalloc_max_workspace() bytes (128 MiB) inside the library,
+ * one copy per device, held until the process ends; a descriptor whose
+ * gmm_workspace_bytes exceeds it returns GMM_E_WORKSPACE before anything is
+ * launched.  All calls on one device share that array: calls that overlap on
+ * a device race (serialise them, e.g. on one stream).  Arguments as in
+ * gmm_prepare / gmm_em_step / gmm_finalize (ll_out and the three outputs
+ * nullable); the results equal those of that sequence on a caller workspace. */
+gmm_status gmm_em_iteration_noalloc(const gmm_desc* desc, const float* pi, const float* mu,
+                                    const float* cov, const void* x, double* ll_out,
+                                    float* pi_out, float* mu_out, float* cov_out,
+                                    hipStream_t stream);
+
+/* Bytes of the internal workspace of gmm_em_iteration_noalloc. */
+size_t gmm_noalloc_max_workspace(void);
+
 /* Static string for a status code. */
 const char* gmm_status_str(gmm_status status);
 

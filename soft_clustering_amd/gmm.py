@@ -68,6 +68,10 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    lib.gmm_em_iteration_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P]
+    lib.gmm_em_iteration_noalloc.restype = ctypes.c_int
+    lib.gmm_noalloc_max_workspace.argtypes = []
+    lib.gmm_noalloc_max_workspace.restype = ctypes.c_size_t
     lib.gmm_status_str.argtypes = [ctypes.c_int]
     lib.gmm_status_str.restype = ctypes.c_char_p
     lib.gmm_version.argtypes = []
@@ -88,7 +92,8 @@ _lib = _load()
 
 EXPORTED = ("gmm_workspace_bytes", "gmm_prepare", "gmm_em_step", "gmm_finalize", "gmm_loglik",
             "gmm_assign", "gmm_fit", "gmm_get_stats", "gmm_diagnostics", "gmm_status_str", "gmm_version",
-            "gmm_calib_sink_bytes", "gmm_calib_read", "gmm_calib_mfma", "gmm_calib_mfma_flops")
+            "gmm_calib_sink_bytes", "gmm_calib_read", "gmm_calib_mfma", "gmm_calib_mfma_flops",
+            "gmm_em_iteration_noalloc", "gmm_noalloc_max_workspace")
 
 
 def status_str(status: int) -> str:
