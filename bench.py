@@ -47,26 +47,27 @@ DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 
 # HBM traffic of one gmm_em_step (every launch it makes), measured with two
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
-#   bench.py --workload W --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
-# summed over the em_step kernels' per-dispatch averages (KiB).  The same run
-# copies a buffer of the size of X once (torch's copy kernel: reads and writes
-# copy_bytes), and each counter is scaled by copy_bytes / (what it read for
-# that copy).  "sources" is a digest of the kernel sources the figures were
+#   bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --no-digest
+#            --no-calibration --copy-calibration
+# summed over the em_step kernels' per-dispatch averages (KiB; a segmented
+# pass's launches summed).  The same run copies a buffer of the size of X once
+# (a device-to-device copy: reads and writes copy_bytes), and each counter is
+# scaled by copy_bytes / (what it read for that copy).  "sources" is a digest of the kernel sources the figures were
 # taken on: once they change, the figures are stale and traffic is reported
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="437d3889ed6ec5e7", fetch_kib=125183.4, write_kib=4144.3,
-        copy_bytes=256e6, copy_fetch_kib=125021.25, copy_write_kib=250000.0),
+        sources="5103003437b3811e", fetch_kib=125182.2, write_kib=4144.3,
+        copy_bytes=2.56e+08, copy_fetch_kib=125018.1875, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="027ea6c1b365e451", fetch_kib=1251255.1, write_kib=66743.4,
-        copy_bytes=2.56e9, copy_fetch_kib=1250036.9375, copy_write_kib=2500000.0),
+        sources="134550805c3d2c7f", fetch_kib=1251280.2, write_kib=68095.5,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250037.75, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="027ea6c1b365e451", fetch_kib=114227215.7, write_kib=4043816.5,
-        copy_bytes=51.2e9, copy_fetch_kib=25000258.0625, copy_write_kib=50000000.0),
+        sources="134550805c3d2c7f", fetch_kib=100045778.3, write_kib=7364216.2,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000259.0625, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="481f08114fdf7145", fetch_kib=63933.1, write_kib=35528.6,
-        copy_bytes=128e6, copy_fetch_kib=62514.9375, copy_write_kib=125000.0),
+        sources="70217c6d857fc3dd", fetch_kib=63934.1, write_kib=35516.4,
+        copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
 FAMILY_SOURCES = {

@@ -37,7 +37,7 @@ constexpr double kLkIllCondNats = 4.0;
 // statistics passes are launched in segments of at most this many tiles per
 // point chunk, and each segment adds its fp32 sums into the workgroup's fp64
 // partial slot.
-constexpr int64_t kLkSegTiles = 2048;
+constexpr int64_t kLkSegTiles = 4096;
 
 // Slots for per-workgroup LL partials and range flags (fused kernel and the
 // slice-merge kernel), and workgroups of the slice-merge kernel.
