@@ -143,21 +143,27 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
     }
     if (p->cov == GMM_COV_FULL && p->xdt == GMM_F16) {
         // full covariance: fp16 X, split fp16 whitening panel, fp16 MFMA whitening and moments
-        if (p->d > 64 || p->k > kFullKP) return GMM_E_UNSUPPORTED;
+        if (p->d > 64 || p->k > kFullMaxK) return GMM_E_UNSUPPORTED;
         int dp = pad_dim(p->d);
         const int64_t tiles = (p->n + kFullT - 1) / kFullT;
+        const int G = full_groups(p->k);          // groups of 16 components
+        const int64_t kpad = (int64_t)kFullKP * G;
         p->path = PATH_FULL;
         p->dp = dp;
-        p->kb = 1;
+        p->kb = G;
         p->p_max = (int)(tiles < 1 ? 1 : (tiles > 256 ? 256 : tiles));
         p->ncols = 1 + p->d + p->d * p->d;
         const int64_t ncolp = full_ncolp(p->d);
         p->off_pi = take(sizeof(float) * p->k);
         p->off_mu = take(sizeof(float) * p->k * p->d);
         p->off_cov = take(sizeof(float) * p->k * p->d * p->d);
-        p->off_panel = take(sizeof(uint4) * full_w_vecs(dp));
-        p->off_shift = take(sizeof(float) * (kFullKP * full_dpo(dp) + kFullKP * dp + 2 * kFullKP));
-        p->off_part = take(sizeof(float) * (size_t)p->p_max * kFullKP * ncolp);
+        p->off_panel = take(sizeof(uint4) * full_w_vecs(dp) * G);
+        p->off_shift = take(sizeof(float) * (kpad * full_dpo(dp) + kpad * dp + 2 * kpad));
+        if (G > 1) {   // per-(group, point) LSE, argmax and maximum
+            p->off_lse = take(sizeof(float) * (size_t)G * p->n);
+            p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)G * p->n);
+        }
+        p->off_part = take(sizeof(float) * (size_t)G * p->p_max * kFullKP * ncolp);
         p->off_part_ll = take(sizeof(double) * kFullLLSlots);
         p->off_chunk = take(sizeof(double) * p->k * ncolp);
         p->off_stats = take(sizeof(double) * p->k * p->ncols);

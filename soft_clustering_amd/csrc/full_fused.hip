@@ -69,24 +69,50 @@ static_assert(KP == 16, "four components per wave, four waves");
 
 // VEC: d % 8 == 0 and 16-byte aligned rows (whole-vector loads); otherwise
 // per-element loads.  A template parameter, so that each kernel holds one path.
-// The topm largest of a point's KP base-2 scores (lower component first on
-// ties) as (index, responsibility exp2(score - lse2)); index -1 and 0 once no
-// live component is left (padding components score -inf).
-__device__ __forceinline__ void write_topm(const float (&sv)[KP], float lse2, int topm, int64_t p,
-                                           int* __restrict__ out_idx, float* __restrict__ out_gamma) {
-    uint32_t taken = 0;
-    for (int i = 0; i < topm; ++i) {
+constexpr int kMaxTopm = 16;
+constexpr float kLog2ef = 1.44269504088896340736f;
+
+// Top-m list of point p over this group's KP base-2 scores merged with the
+// running list of the groups before it (ps.out_idx / ps.out_gamma, which hold
+// base-2 scores until the last group).  Better = larger score, or equal with a
+// lower component index (the running entries, from earlier groups, are
+// checked first); components scoring -inf (zero weight, padding) are never
+// listed: index -1 and 0 past the live ones.  The last group writes the
+// responsibilities exp2(score - lse2).
+__device__ __forceinline__ void write_topm(const float (&sv)[KP], float lse2, const FullPass& ps,
+                                           int64_t p) {
+    const int m = ps.topm, k0 = KP * ps.group;
+    float rv[kMaxTopm];
+    int ri[kMaxTopm];
+#pragma unroll
+    for (int r = 0; r < kMaxTopm; ++r) {
+        const bool ok = !ps.tm_first && r < m;
+        ri[r] = ok ? ps.out_idx[p * m + r] : -1;
+        rv[r] = (ok && ri[r] >= 0) ? ps.out_gamma[p * m + r] : -INFINITY;
+    }
+    uint32_t taken = 0;   // bits 0..15: this group's components; 16..31: running entries
+#pragma unroll
+    for (int i = 0; i < kMaxTopm; ++i) {
+        if (i >= m) break;
         float bv = -INFINITY;
-        int bk = -1;
+        int bk = -1, bs = -1;
+#pragma unroll
+        for (int r = 0; r < kMaxTopm; ++r)
+            if (!((taken >> (16 + r)) & 1u) && ri[r] >= 0 && rv[r] > bv) {
+                bv = rv[r];
+                bk = ri[r];
+                bs = 16 + r;
+            }
 #pragma unroll
         for (int k = 0; k < KP; ++k)
             if (!((taken >> k) & 1u) && sv[k] > bv) {
                 bv = sv[k];
-                bk = k;
+                bk = k0 + k;
+                bs = k;
             }
-        if (bk >= 0) taken |= 1u << bk;
-        out_idx[p * topm + i] = bk;
-        out_gamma[p * topm + i] = bk >= 0 ? fast_exp2(bv - lse2) : 0.0f;
+        if (bs >= 0) taken |= 1u << bs;
+        ps.out_idx[p * m + i] = bk;
+        ps.out_gamma[p * m + i] = bk < 0 ? 0.0f : (ps.tm_last ? fast_exp2(bv - lse2) : bv);
     }
 }
 
@@ -95,9 +121,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
-    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
-    int64_t tlo, int64_t thi, int seg_first, int topm, int* __restrict__ out_idx,
-    float* __restrict__ out_gamma) {
+    double* __restrict__ part_ll, const FullPass ps, int64_t tlo, int64_t thi, int seg_first) {
     using Sh = FullShape<DP>;
     constexpr int NB = Sh::kNB, NBLK = Sh::kNBlk;
     constexpr int NOB = Sh::kNOB, NKS = Sh::kNKS, DPO = Sh::kDPO, NV = Sh::kNV;
@@ -256,8 +280,10 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
             float Z = 0.0f;
 #pragma unroll
             for (int k = 0; k < KP; ++k) Z += fast_exp2(sv[k] - Ms);
-            const float lse2 = Ms + fast_log2(Z);
-            if (valid) ll += (double)lse2;
+            const float own = Ms + fast_log2(Z);
+            // several groups: normalise with the merged LSE of all of them
+            const float lse2 = ps.lse_in != nullptr ? (valid ? ps.lse_in[p] * kLog2ef : 0.0f) : own;
+            if (valid) ll += (double)own;
             if constexpr (EM) {
                 const float lsafe = lse2 == -INFINITY ? INFINITY : lse2;   // no live component
 #pragma unroll
@@ -267,15 +293,16 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                     g_s[k][tid] = gk;
                 }
             } else if (valid) {
-                if (out_lse) out_lse[p] = lse2 * kLn2f;
-                if (out_arg) {
+                if (ps.out_lse) ps.out_lse[p] = lse2 * kLn2f;
+                if (ps.out_arg) {
                     int a = 0;
 #pragma unroll
                     for (int k = KP - 1; k >= 0; --k)
                         if (sv[k] == M) a = k;
-                    out_arg[p] = a;
+                    ps.out_arg[p] = KP * ps.group + a;
                 }
-                if (topm > 0) write_topm(sv, lse2, topm, p, out_idx, out_gamma);
+                if (ps.out_max) ps.out_max[p] = M;
+                if (ps.topm > 0) write_topm(sv, lse2, ps, p);
             }
         }
 
@@ -369,7 +396,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
         if (tid < s2) red[tid] += red[tid + s2];
         __syncthreads();
     }
-    if (tid == 0) part_ll[b] = seg_first ? red[0] * kLn2 : part_ll[b] + red[0] * kLn2;
+    if (tid == 0 && part_ll != nullptr) part_ll[b] = seg_first ? red[0] * kLn2 : part_ll[b] + red[0] * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -392,14 +419,12 @@ constexpr int kGS = T + 4;
 __device__ __forceinline__ int xoff(int r, int u) { return r * DP + 8 * (u ^ ((r >> 1) & 7)); }
 }  // namespace pipe
 
-template <bool EM>
+template <bool EM, bool EXT>   // EXT: normalise with the merged LSE of several groups
 __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
     const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
     const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
-    double* __restrict__ part_ll, float* __restrict__ out_lse, int* __restrict__ out_arg,
-    int64_t tlo, int64_t thi, int seg_first, int topm, int* __restrict__ out_idx,
-    float* __restrict__ out_gamma) {
+    double* __restrict__ part_ll, const FullPass ps, int64_t tlo, int64_t thi, int seg_first) {
     using namespace pipe;
     __shared__ __attribute__((aligned(16))) uint32_t nm_s[KP][DP];     // (-mu, -mu) fp16 pairs
     __shared__ __attribute__((aligned(16))) float wb_s[KP][NOB][2][16];  // -W mu, accumulator layout
@@ -556,8 +581,11 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                 float Z = 0.0f;
 #pragma unroll
                 for (int k = 0; k < KP; ++k) Z += fast_exp2(sv[k] - Ms);
-                const float lse2 = Ms + fast_log2(Z);
-                if (v == 0 && valid) ll += (double)lse2;
+                const float own = Ms + fast_log2(Z);
+                // several groups: normalise with the merged LSE of all of them
+                float lse2 = own;
+                if constexpr (EXT) lse2 = valid ? ps.lse_in[p] * kLog2ef : 0.0f;
+                if (v == 0 && valid) ll += (double)own;
                 if constexpr (EM) {
                     const float lsafe = lse2 == -INFINITY ? INFINITY : lse2;
 #pragma unroll
@@ -568,15 +596,16 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                         gp_s[v][c][pt] = __builtin_bit_cast(uint16_t, (_Float16)gk);   // the MFMA operand
                     }
                 } else if (v == 0 && valid) {
-                    if (out_lse) out_lse[p] = lse2 * kLn2f;
-                    if (out_arg) {
+                    if (ps.out_lse) ps.out_lse[p] = lse2 * kLn2f;
+                    if (ps.out_arg) {
                         int a = 0;
 #pragma unroll
                         for (int k = KP - 1; k >= 0; --k)
                             if (sv[k] == M) a = k;
-                        out_arg[p] = a;
+                        ps.out_arg[p] = KP * ps.group + a;
                     }
-                    if (topm > 0) write_topm(sv, lse2, topm, p, out_idx, out_gamma);
+                    if (ps.out_max) ps.out_max[p] = M;
+                    if (ps.topm > 0) write_topm(sv, lse2, ps, p);
                 }
             }
             if constexpr (EM) {
@@ -674,43 +703,67 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     if (w == 4) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ll += __shfl_xor(ll, o);
-        if (lane == 0) part_ll[b] = seg_first ? ll * kLn2 : part_ll[b] + ll * kLn2;
+        if (lane == 0 && part_ll != nullptr) part_ll[b] = seg_first ? ll * kLn2 : part_ll[b] + ll * kLn2;
     }
 }
 
+// Group g's slice of the per-component arrays and partial slots.
+struct FullGroupPtrs {
+    const uint4* wpk;
+    const float *wbias, *muh, *cvec, *rscale;
+    float* part;
+};
+template <int DP>
+FullGroupPtrs group_ptrs(const Plan& p, const FullWs& w, int g) {
+    constexpr int NV = FullShape<DP>::kNV;
+    FullGroupPtrs q;
+    q.wpk = w.wpk + (size_t)g * KP * NV * 64;
+    q.wbias = w.wbias + (size_t)g * KP * full_dpo(DP);
+    q.muh = w.muh + (size_t)g * KP * DP;
+    q.cvec = w.cvec + (size_t)g * KP;
+    q.rscale = w.rscale + (size_t)g * KP;
+    q.part = w.part + (size_t)g * w.slots * KP * full_ncolp(p.d);
+    return q;
+}
+
 template <int DP, bool VEC>
-hipError_t launch_dv(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
-                     int* arg, int64_t tlo, int64_t thi, int seg_first, const FullTopm& tm,
+hipError_t launch_dv(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
+                     const FullPass& ps, double* pll, int64_t tlo, int64_t thi, int seg_first,
                      hipStream_t s) {
+    const FullGroupPtrs q = group_ptrs<DP>(p, w, ps.group);
     if (em)
         hipLaunchKernelGGL((k_full_fused<DP, true, VEC>), dim3(grid), dim3(256), 0, s,
-                           (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
-                           w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first, 0, (int*)nullptr, (float*)nullptr);
+                           (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, q.wpk, q.wbias, q.muh,
+                           q.cvec, q.rscale, q.part, pll, ps, tlo, thi, seg_first);
     else
         hipLaunchKernelGGL((k_full_fused<DP, false, VEC>), dim3(grid), dim3(256), 0, s,
-                           (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias, w.muh,
-                           w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first, tm.m, tm.idx, tm.gamma);
+                           (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, q.wpk, q.wbias, q.muh,
+                           q.cvec, q.rscale, q.part, pll, ps, tlo, thi, seg_first);
     return hipGetLastError();
 }
 
 template <int DP>
-hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int grid, float* lse,
-                     int* arg, int64_t tlo, int64_t thi, int seg_first, const FullTopm& tm,
-                     hipStream_t s) {
+hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
+                     const FullPass& ps, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
     const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
+    // LL partials only from a group that is the only one (several: the merge sums the LL)
+    double* pll = w.groups == 1 ? w.part_ll : nullptr;
     if (DP == 64 && vec) {   // the pipelined kernel
-        if (em)
-            hipLaunchKernelGGL((k_full_pipe<true>), dim3(grid), dim3(pipe::kThreads), 0, s,
-                               (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
-                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, (float*)nullptr, (int*)nullptr, tlo, thi, seg_first, 0, (int*)nullptr, (float*)nullptr);
-        else
-            hipLaunchKernelGGL((k_full_pipe<false>), dim3(grid), dim3(pipe::kThreads), 0, s,
-                               (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, w.wpk, w.wbias,
-                               w.muh, w.cvec, w.rscale, w.part, w.part_ll, lse, arg, tlo, thi, seg_first, tm.m, tm.idx, tm.gamma);
+        const FullGroupPtrs q = group_ptrs<64>(p, w, ps.group);
+#define FULL_PIPE(EM_, EXT_)                                                                     \
+    hipLaunchKernelGGL((k_full_pipe<EM_, EXT_>), dim3(grid), dim3(pipe::kThreads), 0, s,          \
+                       (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, q.wpk, q.wbias, q.muh, \
+                       q.cvec, q.rscale, q.part, pll, ps, tlo, thi, seg_first)
+        const bool ext = ps.lse_in != nullptr;
+        if (em && ext) FULL_PIPE(true, true);
+        else if (em) FULL_PIPE(true, false);
+        else if (ext) FULL_PIPE(false, true);
+        else FULL_PIPE(false, false);
+#undef FULL_PIPE
         return hipGetLastError();
     }
-    return vec ? launch_dv<DP, true>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s)
-               : launch_dv<DP, false>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
+    return vec ? launch_dv<DP, true>(p, w, x, em, grid, ps, pll, tlo, thi, seg_first, s)
+               : launch_dv<DP, false>(p, w, x, em, grid, ps, pll, tlo, thi, seg_first, s);
 }
 
 }  // namespace
@@ -724,12 +777,12 @@ int full_grid(const Plan& p) {
 }
 
 hipError_t full_launch_fused(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
-                             float* lse, int* arg, int64_t tlo, int64_t thi, int seg_first,
-                             const FullTopm& tm, hipStream_t s) {
+                             const FullPass& ps, int64_t tlo, int64_t thi, int seg_first,
+                             hipStream_t s) {
     switch (p.dp) {
-        case 16: return launch_dp<16>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
-        case 32: return launch_dp<32>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
-        case 64: return launch_dp<64>(p, w, x, em, grid, lse, arg, tlo, thi, seg_first, tm, s);
+        case 16: return launch_dp<16>(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
+        case 32: return launch_dp<32>(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
+        case 64: return launch_dp<64>(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
     }
     return hipErrorInvalidValue;
 }

@@ -18,6 +18,7 @@
 // A component with s0 < 1e-6 keeps its mean and covariance.
 
 #include <math.h>
+#include <string.h>
 
 #include "full_internal.h"
 
@@ -500,9 +501,81 @@ __global__ __launch_bounds__(256) void k_full_sum_ll(const double* part_ll, int 
     }
 }
 
+// Several groups: per point the natural-log LSE over the groups' LSEs
+// (written over row 0), the LL partial of each workgroup (fixed order), and
+// for the E-step the caller's LSE and argmax (lowest component on ties: the
+// first group whose largest score is the overall largest).
+__global__ __launch_bounds__(256) void k_full_merge(int64_t n, int G, float* glse, const int* garg,
+                                                    const float* gmax, double* part_ll,
+                                                    float* out_lse, int* out_arg) {
+    __shared__ double red[256];
+    constexpr float kL2e = 1.44269504088896340736f, kLn2f = 0.69314718055994530942f;
+    double ll = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += stride) {
+        float M = -INFINITY;
+        for (int g = 0; g < G; ++g) M = fmaxf(M, glse[(int64_t)g * n + p]);
+        const float Ms = M == -INFINITY ? 0.0f : M;
+        float Z = 0.0f;
+        for (int g = 0; g < G; ++g) Z += fast_exp2((glse[(int64_t)g * n + p] - Ms) * kL2e);
+        const float lse = Ms + fast_log2(Z) * kLn2f;
+        glse[p] = lse;
+        ll += (double)lse;
+        if (out_lse) out_lse[p] = lse;
+        if (out_arg) {
+            float bm = -INFINITY;
+            int a = 0;
+            for (int g = 0; g < G; ++g) {
+                const float v = gmax[(int64_t)g * n + p];
+                if (v > bm) {
+                    bm = v;
+                    a = garg[(int64_t)g * n + p];
+                }
+            }
+            out_arg[p] = a;
+        }
+    }
+    ll = block_sum_f64(ll, red);
+    if (threadIdx.x == 0) part_ll[blockIdx.x] = ll;
+}
+
+int merge_grid(const Plan& p) {
+    int64_t g = (p.n + 255) / 256;
+    if (g > kFullLLSlots) g = kFullLLSlots;
+    return (int)(g < 1 ? 1 : g);
+}
+
+FullPass pass_of(int g) {
+    FullPass ps;
+    memset(&ps, 0, sizeof(ps));
+    ps.group = g;
+    return ps;
+}
+
+// Several groups, first loop: every group's LSE per point (and, on request,
+// its argmax and largest score), then the merge.
+hipError_t group_lse(const Plan& p, const FullWs& w, const void* x, float* out_lse, int* out_arg,
+                     hipStream_t s) {
+    const int G = full_grid(p);
+    const int64_t tiles = (p.n + kFullT - 1) / kFullT;
+    for (int g = 0; g < w.groups; ++g) {
+        FullPass ps = pass_of(g);
+        ps.out_lse = w.glse + (size_t)g * p.n;
+        if (out_arg) {
+            ps.out_arg = w.garg + (size_t)g * p.n;
+            ps.out_max = w.gmax + (size_t)g * p.n;
+        }
+        const hipError_t e = full_launch_fused(p, w, x, false, G, ps, 0, tiles, 1, s);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_full_merge, dim3(merge_grid(p)), dim3(256), 0, s, p.n, w.groups, w.glse,
+                       (const int*)w.garg, (const float*)w.gmax, w.part_ll, out_lse, out_arg);
+    return hipGetLastError();
+}
+
 hipError_t chol(const Plan& p, const FullWs& w, hipStream_t s) {
 #define FULL_CHOL(DP_)                                                                            \
-    hipLaunchKernelGGL((k_full_chol<DP_>), dim3(kFullKP), dim3(256), 0, s, (int)p.k, (int)p.d,     \
+    hipLaunchKernelGGL((k_full_chol<DP_>), dim3(kFullKP * w.groups), dim3(256), 0, s, (int)p.k, (int)p.d, \
                        p.ridge_rel, w.pi, w.mu, w.cov, w.wpk, w.wbias, w.muh, w.cvec, w.rscale,    \
                        w.flags)
     switch (p.dp) {
@@ -532,32 +605,44 @@ gmm_status full_prepare(const Plan& p, char* ws, const float* pi, const float* m
     return chol(p, w, s) == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
+// Reduce group g's partial slots into its components' column sums (add:
+// onto the sums of the earlier segments of the same pass).
+hipError_t reduce_group(const Plan& p, const FullWs& w, int g, int P, int add, hipStream_t s) {
+    const int ncolp = (int)full_ncolp(p.d);
+    const int64_t k0 = (int64_t)kFullKP * g;
+    const int kc = (int)(p.k - k0 < kFullKP ? p.k - k0 : kFullKP);
+    hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 63) / 64, kc), dim3(256), 0, s,
+                       w.part + (size_t)g * w.slots * kFullKP * ncolp, P, ncolp,
+                       w.colsum + k0 * ncolp, add);
+    return hipGetLastError();
+}
+
 gmm_status full_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hipStream_t s) {
     FullWs w = full_ws(p, ws);
     const int G = full_grid(p);
     const FullSegs sg = full_segs(p, G);
-    const int ncolp = (int)full_ncolp(p.d);
-    for (int i = 0; i < sg.n; ++i) {
-        const int64_t lo = (int64_t)i * sg.len, hi = lo + sg.len < sg.tiles ? lo + sg.len : sg.tiles;
-        if (full_launch_fused(p, w, x, true, G, nullptr, nullptr, lo, hi, i == 0, FullTopm{0, nullptr, nullptr},
-                              s) != hipSuccess)
-            return GMM_E_HIP;
-        // every segment but the last is closed here; finalize adds the last one
-        if (i + 1 < sg.n)
-            hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 63) / 64, p.k), dim3(256), 0, s, w.part,
-                               G, ncolp, w.colsum, i > 0 ? 1 : 0);
+    const bool many = w.groups > 1;
+    if (many && group_lse(p, w, x, nullptr, nullptr, s) != hipSuccess) return GMM_E_HIP;
+    for (int g = 0; g < w.groups; ++g) {
+        FullPass ps = pass_of(g);
+        ps.lse_in = many ? w.glse : nullptr;   // second loop: normalise with the merged LSE
+        for (int i = 0; i < sg.n; ++i) {
+            const int64_t lo = (int64_t)i * sg.len, hi = lo + sg.len < sg.tiles ? lo + sg.len : sg.tiles;
+            if (full_launch_fused(p, w, x, true, G, ps, lo, hi, i == 0, s) != hipSuccess) return GMM_E_HIP;
+            // every segment but the last is closed here; finalize adds the last one
+            if (i + 1 < sg.n && reduce_group(p, w, g, G, i > 0 ? 1 : 0, s) != hipSuccess) return GMM_E_HIP;
+        }
     }
-    if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
-    return sum_ll(p, w, G, ll_out, s);
+    return sum_ll(p, w, many ? merge_grid(p) : G, ll_out, s);
 }
 
 gmm_status full_finalize(const Plan& p, char* ws, float* pi, float* mu, float* cov,
                          hipStream_t s) {
     FullWs w = full_ws(p, ws);
     const int G = full_grid(p);
-    const int ncolp = (int)full_ncolp(p.d);
-    hipLaunchKernelGGL(k_full_reduce, dim3((ncolp + 63) / 64, p.k), dim3(256), 0, s, w.part, G,
-                       ncolp, w.colsum, full_segs(p, G).n > 1 ? 1 : 0);
+    const int add = full_segs(p, G).n > 1 ? 1 : 0;
+    for (int g = 0; g < w.groups; ++g)
+        if (reduce_group(p, w, g, G, add, s) != hipSuccess) return GMM_E_HIP;
     hipLaunchKernelGGL(k_full_mstep, dim3(p.k), dim3(256), 0, s, w.colsum, p.n, (int)p.d, p.dp,
                        w.muh, w.stats, w.pi, w.mu, w.cov, pi, mu, cov, w.flags);
     if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
@@ -568,9 +653,15 @@ gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
                        int32_t* argmax, hipStream_t s) {
     FullWs w = full_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
+    if (w.groups > 1) {
+        if (group_lse(p, w, x, lse, argmax, s) != hipSuccess) return GMM_E_HIP;
+        return sum_ll(p, w, merge_grid(p), ll_out, s);
+    }
     const int G = full_grid(p);
-    if (full_launch_fused(p, w, x, false, G, lse, argmax, 0, (p.n + kFullT - 1) / kFullT, 1,
-                          FullTopm{0, nullptr, nullptr}, s) != hipSuccess)
+    FullPass ps = pass_of(0);
+    ps.out_lse = lse;
+    ps.out_arg = argmax;
+    if (full_launch_fused(p, w, x, false, G, ps, 0, (p.n + kFullT - 1) / kFullT, 1, s) != hipSuccess)
         return GMM_E_HIP;
     return sum_ll(p, w, G, ll_out, s);
 }
@@ -580,10 +671,20 @@ gmm_status full_assign(const Plan& p, char* ws, const void* x, int m, int32_t* i
     FullWs w = full_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int G = full_grid(p);
-    if (full_launch_fused(p, w, x, false, G, nullptr, nullptr, 0, (p.n + kFullT - 1) / kFullT, 1,
-                          FullTopm{m, idx, gamma}, s) != hipSuccess)
-        return GMM_E_HIP;
-    return sum_ll(p, w, G, ll_out, s);
+    const bool many = w.groups > 1;
+    if (many && group_lse(p, w, x, nullptr, nullptr, s) != hipSuccess) return GMM_E_HIP;
+    for (int g = 0; g < w.groups; ++g) {   // the groups in order, merging into the lists
+        FullPass ps = pass_of(g);
+        ps.lse_in = many ? w.glse : nullptr;
+        ps.topm = m;
+        ps.out_idx = idx;
+        ps.out_gamma = gamma;
+        ps.tm_first = g == 0;
+        ps.tm_last = g == w.groups - 1;
+        if (full_launch_fused(p, w, x, false, G, ps, 0, (p.n + kFullT - 1) / kFullT, 1, s) != hipSuccess)
+            return GMM_E_HIP;
+    }
+    return sum_ll(p, w, many ? merge_grid(p) : G, ll_out, s);
 }
 
 }  // namespace gmm

@@ -99,6 +99,8 @@ CASES = [
     (777, 32, 300, "iso", "f16", 1),
     (3000, 32, 16, "full", "f16", 4),
     (2000, 64, 9, "full", "f16", 12),        # m > K
+    (2500, 32, 40, "full", "f16", 6),        # three groups of 16 components
+    (1200, 64, 20, "full", "f16", 3),        # two groups on the two-stage kernel
 ]
 
 

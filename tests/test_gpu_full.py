@@ -145,6 +145,12 @@ CASES = [
     (2500, 48, 12, 0, True),
     (100, 64, 16, 0, False),     # one tile: the two-stage kernel's prologue and drain only
     (700, 56, 9, 0, False),      # D < 64 on the two-stage kernel (aligned rows)
+    # K > 16: groups of 16 components, every group's LSE, the merge, then the
+    # statistics of each group normalised with the merged LSE
+    (3000, 32, 40, 0, False),    # 3 groups
+    (2500, 64, 33, 0, False),    # 3 groups on the two-stage kernel
+    (2000, 16, 100, 0, False),   # 7 groups
+    (1500, 24, 17, 3, True),     # 2 groups, element-wise loads
 ]
 
 
@@ -301,3 +307,29 @@ def test_full_size_workload(gmm_lib):
               flush=True)
         assert metrics.rel(np.sum(lse[idx], dtype=np.float64), ll_s) <= LL_TOL
         assert agree >= ARGMAX_MIN
+
+
+def test_grouped_segmented_statistics(gmm_lib, monkeypatch):
+    """K = 40 (three groups) at D = 32 with runs of one 256-point tile per
+    workgroup: every group's statistics pass takes several segments.  s0, s1
+    and s2 element by element against the oracle (allowance as in
+    test_gpu_segments), and the same step as one segment agrees to fp32
+    accumulation rounding."""
+    from tests.gpu_common import oracle_stats_chunked, stats_elementwise
+    n, d, k = 140_000, 32, 40
+    xd, xg, ldx, th0 = _make(n, d, k, 0, False, seed=77)
+    th = to_dev(*th0)
+    gm = gmm_lib.Gmm(n, d, k, "full", "f16")
+    monkeypatch.setenv("GMM_SEGMENT_TILES", "1")
+    ll, st, _ = gpu_step(gm, xg, *th)
+    monkeypatch.setenv("GMM_SEGMENT_TILES", str(1 << 40))
+    ll1, st1, _ = gpu_step(gm, xg, *th)
+    monkeypatch.delenv("GMM_SEGMENT_TILES")
+    for a, b in ((st.s0, st1.s0), (st.s1, st1.s1), (st.s2, st1.s2)):
+        assert metrics.rel_inf(a.cpu().numpy(), b.cpu().numpy()) <= 1e-5
+    ll_ref, s0, s1, s2 = oracle_stats_chunked(xd, params64("full", *th))
+    print(f"grouped full: LL rel {metrics.rel(ll, ll_ref):.2e}", flush=True)
+    assert metrics.rel(ll, ll_ref) <= LL_TOL
+    stats_elementwise(st.s0.cpu().numpy(), s0, 5e-2, 2e-3, "s0")
+    stats_elementwise(st.s1.cpu().numpy(), s1, 5e-2, 2e-3, "s1")
+    stats_elementwise(st.s2.cpu().numpy(), s2, 5e-2, 2e-3, "s2")
