@@ -128,10 +128,13 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_shift = take(sizeof(float) * (2 + 3 * kLkScanWgs) * dp);
         // panel: (features + 16 bias slots) / 16 MFMA steps x Kpad / 32 blocks x 64 lanes x 16 B
         p->off_panel = take((size_t)(((iso ? 1 : 2) * dp + 16) / 16) * (p->lk_kpad / 32) * 64 * 16);
-        p->off_chunk = take(sizeof(float) * (p->lk_kpad + 4));
-        // per-(slice, point) LSE: the two sweeps, and top-m assignment at any S
-        p->off_lse = take(sizeof(float) * (size_t)S * p->n);
-        if (S > 1) p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)S * p->n);
+        p->off_chunk = take(sizeof(float) * (2 * p->lk_kpad + 4));   // kmax, prm, c0
+        // per-(slice, point) LSE, argmax and maximum, and a row for the exactly
+        // scored components: the two sweeps, top-m assignment
+        p->off_lse = take(sizeof(float) * (size_t)(S + 1) * p->n);
+        p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)(S + 1) * p->n);
+        p->off_xc = take(sizeof(int) * (2 * p->k + 16));
+        p->off_xcpart = take(lk_xc_part_bytes(p->k, lk_ncols(p->cov, p->d)));
         p->off_part = take(sizeof(double) * (size_t)p->p_max * kLkSlice * p->ncols);
         p->off_part_ll = take((sizeof(double) + sizeof(int)) * kLkLLSlots);
         p->off_stats = take(sizeof(double) * p->k * p->ncols);

@@ -192,6 +192,10 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     const float ysc = a.prm[1];                 // |y|^2 scale 2^-g (isotropic)
     const bool want_arg = (MODE == LK_SWEEP1 && a.part_arg != nullptr) ||
                           (MODE == LK_FUSED_E && a.out_arg != nullptr);
+    // components scored exactly outside the panel (their per-point LSE, best
+    // score and its component are already in xlse / xmax / xarg)
+    constexpr bool kXc = MODE == LK_FUSED_EM || MODE == LK_FUSED_E || MODE == LK_TOPM;
+    const int nxc = (kXc && a.xc_n != nullptr) ? *a.xc_n : 0;
 
     // ---- this wave's panel: A operand, row = component, K = inner; steps
     // [KL, KS - 1) in registers, the others (the bias step, and at KL > 0 the
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                 const int64_t pg = prow + pt;
                 for (int i = 0; i < m; ++i) {
                     float2 e = make_float2(-INFINITY, __int_as_float(-1));
-                    if (slice > 0 && pg < n) {
+                    if ((slice > 0 || nxc > 0) && pg < n) {
                         const int kr = a.out_idx[pg * m + i];
                         if (kr >= 0) e = make_float2(a.out_gamma[pg * m + i], __int_as_float(kr));
                     }
@@ -568,7 +572,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                 const float2 mz = wpart[w2][pn];
                 Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
             }
-            const float lse = Ms + fast_log2(Z);
+            float lse = Ms + fast_log2(Z);
             int arg = 0;
             if (want_arg) {
                 arg = 0x7FFFFFFF;
@@ -577,6 +581,22 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
                     if (wpart[w2][pn].x == M) arg = warg[w2][pn];
             }
             const int64_t p = prow + pn;
+            if constexpr (MODE == LK_FUSED_EM || MODE == LK_FUSED_E) {
+                if (nxc > 0 && pvalid) {   // merge the exactly scored components
+                    const float xl = a.xlse[p];
+                    const float m2 = fmaxf(lse, xl);
+                    if (m2 != -INFINITY) lse = m2 + fast_log2(fast_exp2(lse - m2) + fast_exp2(xl - m2));
+                    if constexpr (MODE == LK_FUSED_E) {
+                        if (want_arg) {
+                            const float xm = a.xmax[p];
+                            const int xa = a.xarg[p];
+                            if (xm > M || (xm == M && xa < arg)) arg = xa;
+                        }
+                    } else if (w == 0 && hf == 0) {
+                        a.lse_out[p] = lse;   // their statistics pass reads it
+                    }
+                }
+            }
             if (w == 0 && hf == 0 && pvalid) {
                 if constexpr (MODE == LK_SWEEP1) {
                     a.part_lse[(int64_t)slice * n + p] = lse;

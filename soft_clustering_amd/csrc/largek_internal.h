@@ -29,15 +29,36 @@ constexpr int kLkMaxTopm = 16;
 // fp16 operand range: squares and entries are clamped / scaled below this.
 constexpr float kF16Max = 65504.0f;
 
-// A component whose estimated score rounding error near its own mean exceeds
-// this many nats is reported as ill-conditioned (flag bit 4).
-constexpr double kLkIllCondNats = 4.0;
+// A component whose estimated fp16 score rounding error near its own mean
+// exceeds this many nats is flagged (bit 4) and scored in the exact centred
+// form instead of the panel.  Score errors of e nats shift a responsibility's
+// log-odds by up to about e: at one nat a point shared by two components can
+// move a sizeable part of its weight, so the bar stays there; typical
+// well-conditioned components estimate a few tenths of a nat.
+constexpr double kLkIllCondNats = 1.0;
 
 // Tiles one workgroup accumulates in fp32 before its run is closed: the
 // statistics passes are launched in segments of at most this many tiles per
 // point chunk, and each segment adds its fp32 sums into the workgroup's fp64
 // partial slot.
 constexpr int64_t kLkSegTiles = 4096;
+
+// Exactly scored components (largek_exact.hip): workgroups of the statistics
+// kernel, and the fp64 slot area it writes (at least one slot of every
+// listed component; more slots when fewer components are listed).
+constexpr int kLkXcSlots = 256;
+constexpr size_t kLkXcSlotBytes = (size_t)32 << 20;
+inline size_t lk_xc_part_bytes(int64_t k, int64_t ncol) {
+    const size_t one = sizeof(double) * (size_t)k * ncol;
+    return one > kLkXcSlotBytes ? one : kLkXcSlotBytes;
+}
+// Slots in use for nx listed components: as many as fit, at most `grid`.
+__host__ __device__ inline int lk_xc_slots(int nx, int64_t ncol, int64_t slot_doubles, int grid) {
+    if (nx <= 0) return 0;
+    int64_t P = slot_doubles / ((int64_t)nx * ncol);
+    if (P < 1) P = 1;
+    return (int)(P < grid ? P : grid);
+}
 
 // Slots for per-workgroup LL partials and range flags (fused kernel and the
 // slice-merge kernel), and workgroups of the slice-merge kernel.
@@ -55,11 +76,16 @@ struct LkWs {
     uint4* panel;                // fp16 score panel, MFMA A-operand register layout
     float* kmax;                 // [Kpad] largest panel magnitude of each component
     float* prm;                  // [4] panel scale F = 2^f, |y|^2 scale 2^-g, 2^g, unused
-    float* part_lse;             // [S][N] base-2 LSE of each slice; row 0 is then
-                                 // overwritten with the merged LSE (two sweeps, and
-                                 // top-m assignment at any S)
-    int* part_arg;               // [S][N] argmax within each slice (two-sweep only)
-    float* part_max;             // [S][N] largest score within each slice
+    float* c0;                   // [Kpad] base-2 constant of the centred-form score
+    float* part_lse;             // [S + 1][N] base-2 LSE of each slice and (row S) of the
+                                 // exactly scored components; row 0 then holds the
+                                 // merged LSE
+    int* part_arg;               // [S + 1][N] argmax within each slice / row
+    float* part_max;             // [S + 1][N] largest score within each slice / row
+    int *xc_idx, *xc_pos, *xc_n; // exactly scored components: list [K], position of
+                                 // each component in it (-1: panel) [K], count
+    double* xc_part;             // their statistics slots
+    int64_t xc_slot_doubles;
     double *part, *part_ll;      // per-workgroup partials
     int* part_flag;              // per workgroup: X outside the fp16 operand range
     double *stats, *ll;          // reduced statistics (raw moments), LL
@@ -78,10 +104,15 @@ inline LkWs lk_ws(const Plan& p, char* ws) {
     w.panel = (uint4*)(ws + p.off_panel);
     w.kmax = (float*)(ws + p.off_chunk);
     w.prm = w.kmax + p.lk_kpad;
-    const bool two = p.lk_slices > 1;
+    w.c0 = w.prm + 4;
     w.part_lse = (float*)(ws + p.off_lse);
-    w.part_arg = two ? (int*)(ws + p.off_arg) : nullptr;
-    w.part_max = two ? (float*)(w.part_arg + (size_t)p.lk_slices * p.n) : nullptr;
+    w.part_arg = (int*)(ws + p.off_arg);
+    w.part_max = (float*)(w.part_arg + (size_t)(p.lk_slices + 1) * p.n);
+    w.xc_idx = (int*)(ws + p.off_xc);
+    w.xc_pos = w.xc_idx + p.k;
+    w.xc_n = w.xc_pos + p.k;
+    w.xc_part = (double*)(ws + p.off_xcpart);
+    w.xc_slot_doubles = (int64_t)(lk_xc_part_bytes(p.k, p.ncols) / sizeof(double));
     w.part = (double*)(ws + p.off_part);
     w.part_ll = (double*)(ws + p.off_part_ll);
     w.part_flag = (int*)(w.part_ll + kLkLLSlots);
@@ -120,6 +151,13 @@ struct LkArgs {
     int topm, topm_slice;
     int* out_idx;
     float* out_gamma;
+    // exactly scored components: count; one slice: their per-point base-2 LSE,
+    // largest score and argmax (row S of part_lse / part_max / part_arg), and
+    // where the fused kernels write the merged LSE for their statistics
+    const int* xc_n;
+    const float *xlse, *xmax;
+    const int* xarg;
+    float* lse_out;
 };
 
 // Segments of a statistics pass: tiles split into `nseg` ranges of nearly
@@ -167,6 +205,13 @@ int lk_grid(const Plan& p, int mode);
 
 // Launch the fused kernel in `mode` (largek.hip).
 hipError_t lk_launch(const Plan& p, const LkArgs& a, int mode, int grid, hipStream_t s);
+
+// The exactly scored components (largek_exact.hip).
+hipError_t lk_xc_build(const Plan& p, const LkWs& w, hipStream_t s);
+hipError_t lk_xc_lse(const Plan& p, const LkWs& w, const void* x, hipStream_t s);
+hipError_t lk_xc_stats(const Plan& p, const LkWs& w, const void* x, hipStream_t s);
+hipError_t lk_xc_topm(const Plan& p, const LkWs& w, const void* x, int m, int* idx, float* score,
+                      hipStream_t s);
 
 // Workgroup index of (slice, chunk) in a grid of G = chunks * S workgroups
 // (XCD-aware when G is a multiple of 8 * S: the slices of one chunk share

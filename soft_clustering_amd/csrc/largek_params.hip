@@ -40,7 +40,8 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 // Grid K, 128 threads.
 __global__ __launch_bounds__(128) void k_lk_load(int k_real, int d, bool iso, const float* pi,
                                                  const float* mu, const float* var, float* th_pi,
-                                                 float* th_mu, float* th_var, int* flags) {
+                                                 float* th_mu, float* th_var, int* flags, int* xc_pos,
+                                                 int* xc_n) {
     const int k = blockIdx.x;
     for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
         th_mu[(int64_t)k * d + dd] = mu[(int64_t)k * d + dd];
@@ -52,9 +53,11 @@ __global__ __launch_bounds__(128) void k_lk_load(int k_real, int d, bool iso, co
         if (iso) th_var[k] = var[k];
         flags[k] = (!(pk >= 0.0f) || !isfinite(pk)) ? 1 : 0;
         flags[k_real + k] = 0;
+        xc_pos[k] = -1;   // no exactly scored component until a pass lists them
         if (k == 0) {
             flags[2 * k_real] = 0;
             flags[2 * k_real + 1] = 0;
+            *xc_n = 0;
         }
     }
 }
@@ -171,15 +174,17 @@ template <bool WRITE>
 __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int kpad, int d, int dp, bool iso,
                                                   int nblk, const float* pi, const float* mu,
                                                   const float* var, const float2* dsc, float* kmax,
-                                                  float* prm, uint16_t* panel, int* flags) {
+                                                  float* prm, uint16_t* panel, int* flags, float* c0,
+                                                  const int* xc_pos) {
     __shared__ float red[256];
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * kKpw + (threadIdx.x >> 6);
     const int inner = (iso ? dp : 2 * dp) + 16;
     double sc = 1.0;
     if constexpr (WRITE) {
-        float mx = 0.0f;
-        for (int i = threadIdx.x; i < kpad; i += 256) mx = fmaxf(mx, kmax[i]);
+        float mx = 0.0f;   // over the components the panel scores (not the exact ones)
+        for (int i = threadIdx.x; i < kpad; i += 256)
+            if (i >= k_real || xc_pos[i] < 0) mx = fmaxf(mx, kmax[i]);
         red[threadIdx.x] = mx;
         __syncthreads();
         for (int o = 128; o > 0; o >>= 1) {
@@ -215,12 +220,15 @@ __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int kpad, int d, i
         }
         put(b + lane, v);
     };
-    if (k >= k_real) {   // padding component: zero panel, score -inf
+    // padding component, or one scored in the exact centred form instead:
+    // zero panel entries, score -inf
+    if (k >= k_real || (WRITE && xc_pos[k] >= 0)) {
         if constexpr (WRITE) {
             for (int i = lane; i < inner - 16; i += 64) put(i, 0.0);
             put_bias(-INFINITY, 0.0);
         } else if (lane == 0) {
             kmax[k] = 0.0f;
+            c0[k] = -INFINITY;
         }
         return;
     }
@@ -263,6 +271,7 @@ __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int kpad, int d, i
     if (iso) logv = (double)d * log(vi);
     const double lp = log((double)pi[k]);
     const double cst = kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logv + m2p));   // C_k (base 2)
+    const double cct = kLog2e * (lp - 0.5 * ((double)d * kLog2Pi + logv));          // centred form
     const double pg = iso ? -0.5 * kLog2e / vi * g2 : 0.0;                         // P_k 2^g
     if constexpr (!WRITE) {
         if (lane == 0) {
@@ -270,13 +279,16 @@ __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int kpad, int d, i
             if (isfinite(cst)) m = fmax(m, fabs(cst));
             m = fmax(m, fabs(pg));
             kmax[k] = isfinite(m) ? (float)m : 0.0f;
-            if (bad > 0.0) flags[k] |= 1;
+            c0[k] = (float)cct;
+            int f = flags[k] & ~16;   // the conditioning flag describes this theta only
+            if (bad > 0.0) f |= 1;
             // rounding-error estimate of the fp16 expanded score near the mean,
             // nats: two roundings of relative size <= 2^-11 per panel term
             // (random signs), the 2^-22 split of C_k and of P_k |y|^2
             const double e2 = sqrt(err2) * ldexp(1.0, -11) * (1.41421356 / 1.7320508) +
                               fabs(cst) * ldexp(1.0, -22) + fabs(pg / g2) * yt2 * ldexp(1.0, -21);
-            if (e2 * kLn2 > kLkIllCondNats) flags[k] |= 16;
+            if (e2 * kLn2 > kLkIllCondNats && bad == 0.0 && isfinite(cst)) f |= 16;
+            flags[k] = f;
         }
     } else {
         for (int h = 0; h < 2; ++h) {
@@ -295,16 +307,19 @@ __global__ __launch_bounds__(256) void k_lk_panel(int k_real, int kpad, int d, i
 // the first slice whose maximum is the overall maximum).
 __global__ __launch_bounds__(256) void k_lk_merge(int64_t n, int S, float* part_lse,
                                                   const int* part_arg, const float* part_max,
-                                                  double* part_ll, float* out_lse, int* out_arg) {
+                                                  double* part_ll, float* out_lse, int* out_arg,
+                                                  const int* xc_n) {
     __shared__ double red[256];
     double ll = 0.0;
+    // rows: the S slices, and row S when components are scored exactly
+    const int R = S + (*xc_n > 0 ? 1 : 0);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += stride) {
         float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[(int64_t)s * n + p]);
+        for (int s = 0; s < R; ++s) M = fmaxf(M, part_lse[(int64_t)s * n + p]);
         const float Ms = M == -INFINITY ? 0.0f : M;
         float Z = 0.0f;
-        for (int s = 0; s < S; ++s) Z += fast_exp2(part_lse[(int64_t)s * n + p] - Ms);
+        for (int s = 0; s < R; ++s) Z += fast_exp2(part_lse[(int64_t)s * n + p] - Ms);
         const float lse = Ms + fast_log2(Z);
         part_lse[p] = lse;
         ll += (double)lse;
@@ -312,11 +327,12 @@ __global__ __launch_bounds__(256) void k_lk_merge(int64_t n, int S, float* part_
         if (out_arg) {
             float bm = -INFINITY;
             int arg = 0x7FFFFFFF;
-            for (int s = 0; s < S; ++s) {
+            for (int s = 0; s < R; ++s) {
                 const float v = part_max[(int64_t)s * n + p];
-                if (v > bm || (arg == 0x7FFFFFFF && v == bm)) {
+                const int a = part_arg[(int64_t)s * n + p];
+                if (v > bm || (v == bm && a < arg)) {
                     bm = v;
-                    arg = part_arg[(int64_t)s * n + p];
+                    arg = a;
                 }
             }
             out_arg[p] = arg;
@@ -357,18 +373,26 @@ __global__ __launch_bounds__(256) void k_lk_reduce(
     const float2* __restrict__ dsc, double* __restrict__ stats, float* __restrict__ th_pi,
     float* __restrict__ th_mu, float* __restrict__ th_var, float* __restrict__ out_pi,
     float* __restrict__ out_mu, float* __restrict__ out_var, int* __restrict__ flags,
-    const int* __restrict__ misc) {
+    const int* __restrict__ misc, const int* __restrict__ xc_pos, const int* __restrict__ xc_n,
+    const double* __restrict__ xc_part, int64_t xc_slot_doubles) {
     extern __shared__ double colsum[];   // [ncol]
     __shared__ double red[256];
     const int k = blockIdx.x, tid = threadIdx.x;
     const int ncol = iso ? 2 + d : 1 + 2 * d;
     const int slice = k / kLkSlice, kl = k % kLkSlice;
     const int nchunks = G / S;
+    const int pos = xc_pos[k];
     for (int col = tid; col < ncol; col += 256) {
         double a0 = 0.0;
-        for (int ch = 0; ch < nchunks; ++ch) {
-            const int b = lk_wg_of(slice, ch, G, S);
-            a0 += part[((int64_t)b * kLkSlice + kl) * ncol + col];
+        if (pos < 0) {
+            for (int ch = 0; ch < nchunks; ++ch) {
+                const int b = lk_wg_of(slice, ch, G, S);
+                a0 += part[((int64_t)b * kLkSlice + kl) * ncol + col];
+            }
+        } else {   // scored exactly: its own slots (the panel gave it no responsibility)
+            const int nx = *xc_n;
+            const int P = lk_xc_slots(nx, ncol, xc_slot_doubles, kLkXcSlots);
+            for (int b = 0; b < P; ++b) a0 += xc_part[((int64_t)b * nx + pos) * ncol + col];
         }
         colsum[col] = a0;
     }
@@ -449,10 +473,12 @@ hipError_t refresh_panel(const Plan& p, const LkWs& w, const void* x, hipStream_
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_lk_panel<false>, dim3(p.lk_kpad / kKpw), dim3(256), 0, s, (int)p.k, p.lk_kpad,
                        (int)p.d, p.dp, iso, p.lk_kpad / 32, w.pi, w.mu, w.var, w.dsc, w.kmax, w.prm,
-                       (uint16_t*)w.panel, w.flags);
+                       (uint16_t*)w.panel, w.flags, w.c0, (const int*)w.xc_pos);
+    e = lk_xc_build(p, w, s);   // the components flagged above: scored exactly
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_lk_panel<true>, dim3(p.lk_kpad / kKpw), dim3(256), 0, s, (int)p.k, p.lk_kpad,
                        (int)p.d, p.dp, iso, p.lk_kpad / 32, w.pi, w.mu, w.var, w.dsc, w.kmax, w.prm,
-                       (uint16_t*)w.panel, w.flags);
+                       (uint16_t*)w.panel, w.flags, w.c0, (const int*)w.xc_pos);
     return hipGetLastError();
 }
 
@@ -476,6 +502,12 @@ LkArgs make_args(const Plan& p, const LkWs& w, const void* x) {
     a.tlo = 0;
     a.thi = (p.n + kLkT - 1) / kLkT;
     a.seg_first = 1;
+    a.xc_n = w.xc_n;
+    const size_t rS = (size_t)p.lk_slices * p.n;   // row S: the exactly scored components
+    a.xlse = w.part_lse + rS;
+    a.xmax = w.part_max + rS;
+    a.xarg = w.part_arg + rS;
+    a.lse_out = w.part_lse;
     return a;
 }
 
@@ -529,7 +561,7 @@ gmm_status lk_prepare(const Plan& p, char* ws, const float* pi, const float* mu,
                       hipStream_t s) {
     LkWs w = lk_ws(p, ws);
     hipLaunchKernelGGL(k_lk_load, dim3(p.k), dim3(128), 0, s, (int)p.k, (int)p.d,
-                       p.cov == GMM_COV_ISO, pi, mu, var, w.pi, w.mu, w.var, w.flags);
+                       p.cov == GMM_COV_ISO, pi, mu, var, w.pi, w.mu, w.var, w.flags, w.xc_pos, w.xc_n);
     return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
@@ -539,20 +571,24 @@ gmm_status lk_em_step(const Plan& p, char* ws, const void* x, double* ll_out, hi
     LkArgs a = make_args(p, w, x);
     if (p.lk_slices == 1) {
         const int G = lk_grid(p, LK_FUSED_EM);
+        if (lk_xc_lse(p, w, x, s) != hipSuccess) return GMM_E_HIP;
         if (launch_segments(p, a, LK_FUSED_EM, G, s) != hipSuccess) return GMM_E_HIP;
+        if (lk_xc_stats(p, w, x, s) != hipSuccess) return GMM_E_HIP;
         return lk_sum(p, w, G, G, ll_out, s);
     }
     const int G1 = lk_grid(p, LK_SWEEP1), G = lk_grid(p, LK_SWEEP2);
     a.part_lse = w.part_lse;
     if (lk_launch(p, a, LK_SWEEP1, G1, s) != hipSuccess) return GMM_E_HIP;
+    if (lk_xc_lse(p, w, x, s) != hipSuccess) return GMM_E_HIP;
     const int M = merge_grid(p);
     hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
                        (const int*)nullptr, (const float*)nullptr, w.part_ll, (float*)nullptr,
-                       (int*)nullptr);
+                       (int*)nullptr, (const int*)w.xc_n);
     if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
     a.part_lse = nullptr;
     a.lse_in = w.part_lse;
     if (launch_segments(p, a, LK_SWEEP2, G, s) != hipSuccess) return GMM_E_HIP;
+    if (lk_xc_stats(p, w, x, s) != hipSuccess) return GMM_E_HIP;
     // range flags: sweep 1 wrote slots [0, G1), sweep 2 rewrote [0, G)
     return lk_sum(p, w, M, G1 > G ? G1 : G, ll_out, s);
 }
@@ -563,7 +599,8 @@ gmm_status lk_finalize(const Plan& p, char* ws, float* pi, float* mu, float* var
     const size_t shm = sizeof(double) * (size_t)p.ncols;
     hipLaunchKernelGGL(k_lk_reduce, dim3(p.k), dim3(256), shm, s, w.part, G, p.lk_slices, p.n,
                        (int)p.d, p.cov == GMM_COV_ISO, p.var_floor, w.dsc, w.stats, w.pi, w.mu,
-                       w.var, pi, mu, var, w.flags, w.misc);
+                       w.var, pi, mu, var, w.flags, w.misc, (const int*)w.xc_pos, (const int*)w.xc_n,
+                       (const double*)w.xc_part, w.xc_slot_doubles);
     return hipGetLastError() == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
@@ -579,16 +616,19 @@ gmm_status lk_assign(const Plan& p, char* ws, const void* x, int m, int32_t* idx
     const int G1 = lk_grid(p, LK_SWEEP1);
     a.part_lse = w.part_lse;
     if (lk_launch(p, a, LK_SWEEP1, G1, s) != hipSuccess) return GMM_E_HIP;
+    if (lk_xc_lse(p, w, x, s) != hipSuccess) return GMM_E_HIP;
     const int M = merge_grid(p);
     hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
                        (const int*)nullptr, (const float*)nullptr, w.part_ll, (float*)nullptr,
-                       (int*)nullptr);
+                       (int*)nullptr, (const int*)w.xc_n);
     if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
     a.part_lse = nullptr;
     a.lse_in = w.part_lse;
     a.topm = m;
     a.out_idx = idx;
     a.out_gamma = gamma;
+    // the exactly scored components start every point's running list
+    if (lk_xc_topm(p, w, x, m, idx, gamma, s) != hipSuccess) return GMM_E_HIP;
     const int GT = lk_grid(p, LK_TOPM);
     for (int sl = 0; sl < p.lk_slices; ++sl) {
         a.topm_slice = sl;
@@ -607,6 +647,7 @@ gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, flo
     if (p.lk_slices == 1) {
         a.out_lse = lse;
         a.out_arg = argmax;
+        if (lk_xc_lse(p, w, x, s) != hipSuccess) return GMM_E_HIP;
         if (lk_launch(p, a, LK_FUSED_E, G, s) != hipSuccess) return GMM_E_HIP;
         return lk_sum(p, w, G, G, ll_out, s);
     }
@@ -616,9 +657,11 @@ gmm_status lk_loglik(const Plan& p, char* ws, const void* x, double* ll_out, flo
         a.part_max = w.part_max;
     }
     if (lk_launch(p, a, LK_SWEEP1, G, s) != hipSuccess) return GMM_E_HIP;
+    if (lk_xc_lse(p, w, x, s) != hipSuccess) return GMM_E_HIP;
     const int M = merge_grid(p);
     hipLaunchKernelGGL(k_lk_merge, dim3(M), dim3(256), 0, s, p.n, p.lk_slices, w.part_lse,
-                       (const int*)w.part_arg, (const float*)w.part_max, w.part_ll, lse, argmax);
+                       (const int*)w.part_arg, (const float*)w.part_max, w.part_ll, lse, argmax,
+                       (const int*)w.xc_n);
     if (hipGetLastError() != hipSuccess) return GMM_E_HIP;
     return lk_sum(p, w, M, G, ll_out, s);
 }

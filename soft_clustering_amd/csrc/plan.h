@@ -37,6 +37,7 @@ struct Plan {
     size_t off_lse, off_arg;          // large K, two sweeps: per-(slice, point) LSE,
                                       // argmax and maximum
     size_t off_ctl;                   // gmm_fit control block and the start's indices
+    size_t off_xc, off_xcpart;        // large K: exactly scored components (list, slots)
     size_t total;
     int64_t ncols;                    // statistic columns per component
     int lk_slices;                    // large K: 256-component slices

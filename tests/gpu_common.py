@@ -121,6 +121,111 @@ def ill_conditioned(theta, x, cov_type):
     return np.nonzero(fp16_score_error_nats(theta, x, cov_type) > ILL_COND_NATS)[0].tolist()
 
 
+def point_score_error_nats(theta, x, cov_type):
+    """The error model of fp16_score_error_nats at every (point, component):
+    the terms A y_d^2 and B y_d of the point's own y = x - c, two fp16
+    roundings each with random signs.  Returns an [N, K] array in nats."""
+    pi, mu, cov = (np.asarray(t, np.float64) for t in theta)
+    x = np.asarray(x, np.float64)
+    c = x.mean(axis=0)
+    y2 = (x - c) ** 2
+    var = cov[:, None] * np.ones_like(mu) if cov_type == "iso" else cov
+    a = 0.5 * LOG2E / var
+    b = LOG2E * (mu - c) / var
+    s = (y2 * y2) @ (a * a).T + y2 @ (b * b).T
+    return np.sqrt(np.maximum(s, 0.0)) * FP16_U * np.sqrt(2.0 / 3.0) * np.log(2.0)
+
+
+def gamma_error_bound(x, p, theta32, cov_type, margin=3.0, exact_nats=2.0):
+    """Bound on |gamma_gpu - gamma| per (point, component) from the fp16
+    score errors: E_nk = margin x point_score_error_nats (a component whose
+    fp16_score_error_nats exceeds exact_nats is taken as scored exactly in
+    fp32, E = 1e-4).  With every score of point n off by at most E_nj,
+    gamma'_nk = gamma_nk e^d_k / sum_j gamma_nj e^d_j lies between
+    gamma e^-E_k / (gamma e^-E_k + sum_{j != k} gamma_nj e^E_j) and
+    gamma e^E_k / (gamma e^E_k + sum_{j != k} gamma_nj e^-E_j): the bound is
+    the larger distance of the two from gamma_nk.  gamma from the oracle.
+    Returns (bound, gamma)."""
+    exact = fp16_score_error_nats(theta32, x, cov_type) > exact_nats
+    e = np.minimum(margin * point_score_error_nats(theta32, x, cov_type), 60.0)   # e^60: still finite
+    e[:, exact] = 1e-4
+    a = oracle.log_joint(x, p, oracle.prepare(p))
+    lse = np.logaddexp.reduce(a, axis=1)
+    g = np.exp(a - lse[:, None])
+    gu = g * np.exp(e)
+    gd = g * np.exp(-e)
+    rest_up = gu.sum(axis=1, keepdims=True) - gu   # sum_{j != k} gamma_nj e^E_nj
+    rest_dn = gd.sum(axis=1, keepdims=True) - gd
+    with np.errstate(invalid="ignore", divide="ignore"):
+        hi = np.where(gu > 0, gu / (gu + rest_dn), 0.0)
+        lo = np.where(gd > 0, gd / (gd + rest_up), 0.0)
+    return np.maximum(hi - g, g - lo), g
+
+
+def check_params_bounded(ref, st, theta, x, B, g, cov_type, stat_u=FP16_U, what=""):
+    """s0, mu and the variances of every component against the oracle's,
+    element by element, within the error that the responsibility bound B
+    (gamma_error_bound) propagates: s0 by sum_n B_nk, and to first order mu
+    by sum_n B_nk |x_n - mu_k| / s0_k, the variance by sum_n B_nk |(x_n -
+    mu_k)^2 - var_k| / s0_k (isotropic: the mean over dimensions).  Plus the
+    rounding of the statistics operands, relative stat_u each, worst case:
+    y = x - c (c the data centre) staged in fp16 moves mu by
+    stat_u sum_n gamma_nk |y_n| / s0_k and, through the mean subtracted in
+    the variance, the variance by 2 |mu_k - c| times that; y^2 staged in
+    fp16 moves the variance by stat_u sum_n gamma_nk y_n^2 / s0_k.  And a
+    floor for the fp32 arithmetic (1e-3 relative, 1e-4 of the largest).
+    The first-order propagation to mu and the variance holds while the mass
+    bound is small against the mass: components with sum_n B_nk > s0_k / 4
+    (their weight is not determined at this precision) have s0 checked and
+    their mean and variance reported, not compared."""
+    x = np.asarray(x, np.float64)
+    n, d = x.shape
+    c = x.mean(axis=0)
+    s0 = np.asarray(ref.nk, np.float64)
+    mu, var = ref.params.mu, ref.params.cov
+    bs0 = B.sum(axis=0)
+    bmu = np.zeros_like(mu)
+    bvar = np.zeros_like(var)
+    for k in np.nonzero((bs0 > 0) | (s0 > 0))[0]:
+        live = (B[:, k] > 0) | (g[:, k] > 0)
+        dx = x[live] - mu[k]
+        yc = np.abs(x[live] - c)
+        w = B[live, k] / max(s0[k], 1e-300)
+        wg = stat_u * g[live, k] / max(s0[k], 1e-300)
+        rmu = wg @ yc                             # per dimension
+        bmu[k] = w @ np.abs(dx) + rmu
+        mc = np.abs(mu[k] - c)
+        if cov_type == "iso":
+            bvar[k] = (w @ np.abs((dx * dx).mean(axis=1) - var[k]) + wg @ (yc * yc).mean(axis=1) +
+                       np.mean(2.0 * mc * rmu))
+        else:
+            bvar[k] = w @ np.abs(dx * dx - var[k]) + wg @ (yc * yc) + 2.0 * mc * rmu
+    heavy = s0 >= 1e-3 * n / max(len(s0), 1)   # empty components keep theta: not compared
+    loose = heavy & (bs0 > 0.25 * s0)
+    if loose.any():
+        print(f"   {what}: {int(loose.sum())} components with mass bound above s0 / 4 "
+              f"(first {np.nonzero(loose)[0][:8].tolist()}): mean and variance not compared", flush=True)
+    heavy &= ~loose
+    out = {}
+    for name, got, want, bnd in (("s0", st.s0.cpu().numpy(), s0, bs0),
+                                 ("mu", theta[1].cpu().numpy(), mu, bmu),
+                                 ("var", theta[2].cpu().numpy(), var, bvar)):
+        got = np.asarray(got, np.float64).reshape(np.shape(want))
+        err = np.abs(got - want)
+        allow = bnd + 1e-3 * np.abs(want) + 1e-4 * np.max(np.abs(want))
+        ratio = err / allow
+        if name != "s0":
+            ratio[~heavy] = 0.0
+        worst = float(np.max(ratio)) if ratio.size else 0.0
+        i = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else ()
+        out[name] = worst
+        print(f"   {what} {name}: worst err/bound {worst:.3f} at {i} (err {err[i] if ratio.size else 0:.3e}, "
+              f"bound {allow[i] if ratio.size else 0:.3e})", flush=True)
+    bad = {k: v for k, v in out.items() if not v <= 1.0}
+    assert not bad, (what, bad)
+    return out
+
+
 def oracle_stats_chunked(x, p, chunk=8192, workers=8, **kw):
     """The oracle's em_step over consecutive chunks of points in a thread
     pool; returns (LL, s0, s1, s2) summed over the chunks in chunk order (the

@@ -79,10 +79,10 @@ def test_workspace_has_no_nk_term():
 ])
 def test_workspace_far_below_nk(cov, x_dtype, n, d, k):
     """The benchmark workloads' workspaces: the full path does not grow with N
-    (per-workgroup partial slots are capped); the large-K paths keep one fp32
-    LSE per point and 256-component slice (top-m assignment and the two
-    sweeps), plus an argmax and a maximum when there are several slices: 4 or
-    12 bytes per point and slice, a small fraction of the fp32 N x K matrix."""
+    (per-workgroup partial slots are capped); the large-K paths keep an fp32
+    LSE, an argmax and a maximum per point for every 256-component slice and
+    for the exactly scored components: 12 bytes per point and row, S + 1
+    rows for S slices, a small fraction of the fp32 N x K matrix."""
     ws = gmm.workspace_bytes(gmm.make_desc(n, d, k, cov, x_dtype))
     if cov == "full":   # O(P K D^2): 256 partial slots of 16 x (1 + D + D(D+1)/2) fp64
         assert ws <= 256 * 16 * (1 + d + d * (d + 1) // 2) * 8 + (8 << 20), ws
@@ -92,9 +92,8 @@ def test_workspace_far_below_nk(cov, x_dtype, n, d, k):
     if cov == "full":
         assert ws10 == ws
     else:
-        slices = (k + 255) // 256
-        per = 4 if slices == 1 else 12
-        assert ws10 - ws == 9 * n * per * slices + (ws10 - ws) % 256   # linear in N
+        rows = (k + 255) // 256 + 1
+        assert ws10 - ws == 9 * n * 12 * rows + (ws10 - ws) % 256   # linear in N
 
 
 def test_null_arguments_rejected_before_launch():
