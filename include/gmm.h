@@ -74,7 +74,12 @@ typedef struct {
                            ([LP-GMM] 4.1); 1e-3 */
 } gmm_desc;
 
-/* Device-side health report, filled by gmm_diagnostics. */
+/* Device-side health report, filled by gmm_diagnostics: the flags that
+ * [LP-GMM] 3.3 asks the preprocessing to raise (an indefinite covariance is
+ * detected and marked there, never branched on in the hot loop), the
+ * failure modes of 4.1 (not positive definite) and 4.2 (underflow to 0/0 =
+ * NaN), and the checks of the debugging order in 5.1 (weights, non-finite
+ * values, small variances that make the fp16 score swing). */
 typedef struct {
     int32_t bad_params;      /* components whose prepared variance/covariance
                                 was non-positive or non-finite */
@@ -84,15 +89,23 @@ typedef struct {
     int32_t ridge_retries;   /* full covariance: largest escalation count */
     int32_t empty;           /* components with s0 < 1e-6 at the last finalize */
     int32_t nonfinite;       /* 1 if the last LL or statistics were NaN/Inf */
-    int32_t x_range;         /* fp16-operand diagonal kernels: 1 if the last
+    int32_t x_range;         /* large-K (fp16 operand) plans: 1 if the last
                                 pass met a value of X whose scaled square
-                                exceeded the fp16 range (it was clamped); NaN
-                                in X shows up as a non-finite LL */
-    int32_t ill_cond;        /* fp16-operand kernels: components whose expanded
-                                score [x^2, x] . panel is estimated to carry
-                                more than 4 nats of rounding error near their
-                                own mean (e.g. a variance collapsed to the
-                                floor); their responsibilities are unreliable */
+                                exceeded the fp16 range (the centre and scale
+                                come from a sample of X).  The pass then fails
+                                visibly: its LL is NaN, nonfinite is set and
+                                gmm_finalize keeps theta.  NaN in X shows up as
+                                a non-finite LL */
+    int32_t ill_cond;        /* large-K plans: components whose fp16 expanded
+                                score [y^2, y, 1] . panel is estimated to carry
+                                more than 1 nat of rounding error near their
+                                own mean (a variance small against the
+                                component's distance from the data centre,
+                                [LP-GMM] 5.1 fourth step).  They are taken out
+                                of the panel and scored in the exact centred
+                                form in fp32 ([LP-GMM] 1.2, 1.3); the count is
+                                informational.  0 on the other paths, whose
+                                scores are centred or split into fp16 pairs */
     int32_t reserved;
     double  ll;              /* LL of the last gmm_em_step / gmm_loglik */
 } gmm_diag;
@@ -202,9 +215,14 @@ gmm_status gmm_fit(const gmm_desc* desc, void* ws, size_t ws_bytes, const void* 
 
 /* Copy the sufficient statistics of the last EM iteration into device fp64
  * buffers (each nullable): s0 [K]; s1 [K*D]; s2 [K*D] (diag: sum gamma x^2),
- * [K] (iso: sum gamma |x|^2) or [K*D*D] (full: sum gamma x x^T).  The
- * per-workgroup partials of gmm_em_step are reduced by gmm_finalize, so call
- * this after gmm_finalize; the values are those of the em_step it finished. */
+ * [K] (iso: sum gamma |x|^2) or [K*D*D] (full: sum gamma x x^T) - the
+ * zeroth, first and second moments of [Flash-GMM] Method (statistics
+ * accumulated on chip tile by tile), in raw units of x.  The per-workgroup
+ * partials of gmm_em_step are reduced by gmm_finalize ([LP-GMM] 3.1, M-step:
+ * partial reductions per block, then a global one), so call this after
+ * gmm_finalize; the values are those of the em_step it finished.  Errors:
+ * GMM_E_ARG for a null descriptor or workspace, GMM_E_WORKSPACE,
+ * GMM_E_HIP if a copy fails. */
 gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes,
                          double* s0, double* s1, double* s2, hipStream_t stream);
 

@@ -129,8 +129,10 @@ __device__ __forceinline__ uint2 tr16(const uint16_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int COV, int DP, int MODE, bool BF16, bool VEC>
-__global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void k_lk(const LkArgs a) {
+template <int COV, int DP, int MODE_ARG, bool BF16, bool VEC>
+__global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) void k_lk(const LkArgs a) {
+    constexpr int MODE = MODE_ARG & (kLkArg - 1);
+    constexpr bool want_arg = (MODE_ARG & kLkArg) != 0 && (MODE == LK_SWEEP1 || MODE == LK_FUSED_E);
     constexpr int WV = lk_waves(MODE, COV);     // waves per workgroup
     constexpr int KW = kLkSlice / WV;           // components per wave
     constexpr int CB = KW / 32;                 // 32-component blocks per wave
@@ -190,8 +192,6 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
     const int d = a.d;
     const float F = a.prm[0];                   // panel scale 2^f
     const float ysc = a.prm[1];                 // |y|^2 scale 2^-g (isotropic)
-    const bool want_arg = (MODE == LK_SWEEP1 && a.part_arg != nullptr) ||
-                          (MODE == LK_FUSED_E && a.out_arg != nullptr);
     // components scored exactly outside the panel (their per-point LSE, best
     // score and its component are already in xlse / xmax / xarg)
     constexpr bool kXc = MODE == LK_FUSED_EM || MODE == LK_FUSED_E || MODE == LK_TOPM;
@@ -373,7 +373,9 @@ __global__ __launch_bounds__(64 * lk_waves(MODE, COV), lk_wg_per_cu(MODE)) void 
         if constexpr (!kIso) {
             const float v0 = yp[0] * yp[0], v1 = yp[1] * yp[1];
             rng = fmaxf(rng, fmaxf(v0, v1));
-            hq[pr] = pack_h2(fminf(v0, kF16Max), fminf(v1, kF16Max));
+            // beyond the fp16 range the square converts to inf: the pass is
+            // flagged below (rng) and its results are discarded
+            hq[pr] = pack_h2(v0, v1);
         }
         if (pr == 3) {
             const int off_y = kIso ? 0 : DP;
@@ -770,8 +772,10 @@ hipError_t launch1(const Plan& p, const LkArgs& a, int mode, int grid, hipStream
     switch (mode) {
         case LK_FUSED_EM: return launch2<COV, LK_FUSED_EM>(p, a, grid, s);
         case LK_SWEEP1: return launch2<COV, LK_SWEEP1>(p, a, grid, s);
+        case LK_SWEEP1 | kLkArg: return launch2<COV, LK_SWEEP1 | kLkArg>(p, a, grid, s);
         case LK_SWEEP2: return launch2<COV, LK_SWEEP2>(p, a, grid, s);
         case LK_FUSED_E: return launch2<COV, LK_FUSED_E>(p, a, grid, s);
+        case LK_FUSED_E | kLkArg: return launch2<COV, LK_FUSED_E | kLkArg>(p, a, grid, s);
         case LK_TOPM: return launch2<COV, LK_TOPM>(p, a, grid, s);
     }
     return hipErrorInvalidValue;
@@ -780,6 +784,9 @@ hipError_t launch1(const Plan& p, const LkArgs& a, int mode, int grid, hipStream
 }  // namespace
 
 hipError_t lk_launch(const Plan& p, const LkArgs& a, int mode, int grid, hipStream_t s) {
+    // the argmax variants when the caller asked for it
+    if ((mode == LK_SWEEP1 && a.part_arg != nullptr) || (mode == LK_FUSED_E && a.out_arg != nullptr))
+        mode |= kLkArg;
     if (p.cov == GMM_COV_ISO) return launch1<GMM_COV_ISO>(p, a, mode, grid, s);
     return launch1<GMM_COV_DIAG>(p, a, mode, grid, s);
 }

@@ -22,6 +22,9 @@ enum LkMode : int {
     LK_TOPM = 4,       // one slice per launch: the m largest responsibilities per
                        // point, merged with those of the slices before it
 };
+// Added to LK_SWEEP1 / LK_FUSED_E when the per-point argmax is wanted: the
+// comparisons it needs are compiled only into those variants.
+constexpr int kLkArg = 8;
 
 // Largest m of gmm_assign.
 constexpr int kLkMaxTopm = 16;
@@ -188,6 +191,7 @@ inline int64_t lk_ncols(int cov, int64_t d) { return cov == GMM_COV_ISO ? 2 + d 
 // the tile twice as often: sweep 2 of 2e8 x 128 x 1024 went 253 -> 272 ms).
 // The modes without statistics run 4 waves and two workgroups per CU.
 __host__ __device__ constexpr int lk_waves(int mode, int cov) {
+    mode &= kLkArg - 1;
     return ((mode == LK_FUSED_EM || mode == LK_SWEEP2) && cov == GMM_COV_ISO) ? 8 : 4;
 }
 
@@ -196,6 +200,7 @@ __host__ __device__ constexpr int lk_waves(int mode, int cov) {
 // overlap the other's vector work and latencies); the statistics modes need
 // up to 512 registers per lane and run one.
 __host__ __device__ constexpr int lk_wg_per_cu(int mode) {
+    mode &= kLkArg - 1;
     return (mode == LK_SWEEP1 || mode == LK_FUSED_E) ? 2 : 1;
 }
 
