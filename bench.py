@@ -57,22 +57,22 @@ DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="5103003437b3811e", fetch_kib=125182.2, write_kib=4144.3,
-        copy_bytes=2.56e+08, copy_fetch_kib=125018.1875, copy_write_kib=250000.0),
+        sources="be8e56b42ee450f8", fetch_kib=125175.4, write_kib=4144.3,
+        copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="134550805c3d2c7f", fetch_kib=1251280.2, write_kib=68095.5,
-        copy_bytes=2.56e+09, copy_fetch_kib=1250037.75, copy_write_kib=2500000.0),
+        sources="e42fadc9e4dd3d7d", fetch_kib=1251316.7, write_kib=69170.8,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250037.5, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="134550805c3d2c7f", fetch_kib=100045778.3, write_kib=7364216.2,
-        copy_bytes=5.12e+10, copy_fetch_kib=25000259.0625, copy_write_kib=50000000.0),
+        sources="e42fadc9e4dd3d7d", fetch_kib=87983610.3, write_kib=7363628.1,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000252.9375, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="70217c6d857fc3dd", fetch_kib=63934.1, write_kib=35516.4,
+        sources="e4a222026d575f44", fetch_kib=63933.3, write_kib=35532.7,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
 FAMILY_SOURCES = {
     "diag_f32": ("diag_split.hip", "diag_params.hip", "diag_internal.h") + _SHARED_SOURCES,
-    "largek": ("largek.hip", "largek_params.hip", "largek_internal.h") + _SHARED_SOURCES,
+    "largek": ("largek.hip", "largek_params.hip", "largek_exact.hip", "largek_internal.h") + _SHARED_SOURCES,
     "full": ("full_fused.hip", "full_params.hip", "full_internal.h") + _SHARED_SOURCES,
 }
 
