@@ -234,7 +234,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
         for (int b = 0; b < KW / 16; ++b) aux[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     double ll2 = 0.0;
-    float rng = 0.0f;   // diag: largest (y')^2 staged; iso: largest |y|^2 2^-g (clamped above fp16 max)
+    float rng = 0.0f;   // iso: largest |y|^2 2^-g staged (clamped above the fp16 maximum)
+    half2v rq = {(_Float16)0.0f, (_Float16)0.0f};   // diag: largest fp16 (y')^2 staged (inf: out of range)
 
     // ---- staging: item (row, 8-column block); the kCB items of a row sit in
     // consecutive lanes and every item of a thread has the same column block.
@@ -371,11 +372,14 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
         }
         hy[pr] = pack_h2(yp[0], yp[1]);
         if constexpr (!kIso) {
-            const float v0 = yp[0] * yp[0], v1 = yp[1] * yp[1];
-            rng = fmaxf(rng, fmaxf(v0, v1));
-            // beyond the fp16 range the square converts to inf: the pass is
-            // flagged below (rng) and its results are discarded
-            hq[pr] = pack_h2(v0, v1);
+            // the square of the staged fp16 y' (one packed multiply), so the
+            // score is the expanded form at the rounded point; beyond the fp16
+            // range it is inf: the pass is flagged below and its results
+            // are discarded
+            const half2v h = __builtin_bit_cast(half2v, hy[pr]);
+            const half2v q = h * h;
+            rq = __builtin_elementwise_max(rq, q);
+            hq[pr] = __builtin_bit_cast(uint32_t, q);
         }
         if (pr == 3) {
             const int off_y = kIso ? 0 : DP;
@@ -696,6 +700,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
     }
 
     // ---- epilogue: per-workgroup partials, one writer per value
+    if constexpr (!kIso) rng = fmaxf((float)rq[0], (float)rq[1]);
     const int flag = __syncthreads_or(rng > kF16Max ? 1 : 0);
     const bool first = a.seg_first != 0;
     if (tid == 0) a.part_flag[blockIdx.x] = first ? flag : (a.part_flag[blockIdx.x] | flag);
