@@ -157,8 +157,13 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
     __shared__ __attribute__((aligned(16))) uint16_t yh_t[2][kT];   // iso: |y|^2 2^-g, fp16
     __shared__ uint4 plds[WV][CB][KL + 1][64];   // LDS-resident steps of each wave's panel
     __shared__ float2 dsc_l[DP];       // [e][8-column block], column 8 block + e: iso (c, s), diag (s, -c s)
-    __shared__ float2 wpart[WV][kT];   // per-wave (max, sum) of each point, base-2 score units
-    __shared__ int warg[WV][kT];
+    // E-step modes without statistics: one barrier per tile (the exchange's);
+    // the exchange buffers alternate between tiles so that a wave writing the
+    // next tile's values cannot overwrite values another wave still reads
+    constexpr bool kOneBarrier = kExchange && !kStats;
+    constexpr int NXB = kOneBarrier ? 2 : 1;
+    __shared__ float2 wpart_b[NXB][WV][kT];   // per-wave (max, sum) of each point, base-2 score units
+    __shared__ int warg_b[NXB][WV][kT];
     __shared__ double llred[NT];
     // top-m mode: the slice's base-2 scores of the tile, each point's partial
     // lists (8 threads per point, 32 components each) and the running list
@@ -551,6 +556,8 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
         }
 
         if constexpr (kExchange) {
+            float2(*wpart)[kT] = wpart_b[kOneBarrier ? cur : 0];
+            int(*warg)[kT] = warg_b[kOneBarrier ? cur : 0];
             // this wave's (max, sum) per point, base-2 score units
             float m = mcb[0];
 #pragma unroll
@@ -696,7 +703,9 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
             }
         }
 
-        __syncthreads();
+        // the next tile was staged by every wave before the exchange barrier
+        // (one-barrier modes), and nothing reads this tile after it
+        if constexpr (!kOneBarrier) __syncthreads();
     }
 
     // ---- epilogue: per-workgroup partials, one writer per value
