@@ -130,13 +130,16 @@ __device__ __forceinline__ uint2 tr16(const uint16_t* p) {
 }
 
 template <int COV, int DP, int MODE_ARG, bool BF16, bool VEC>
-__global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) void k_lk(const LkArgs a) {
+__global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) void k_lk(const LkArgs a) {
     constexpr int MODE = MODE_ARG & (kLkArg - 1);
     constexpr bool want_arg = (MODE_ARG & kLkArg) != 0 && (MODE == LK_SWEEP1 || MODE == LK_FUSED_E);
-    constexpr int WV = lk_waves(MODE, COV);     // waves per workgroup
+    constexpr int SPW = lk_slices_per_wg(MODE_ARG);   // slices per workgroup (2: sweep 1 only)
+    static_assert(SPW == 1 || MODE == LK_SWEEP1, "paired slices: sweep 1 only");
+    constexpr int WV = lk_waves(MODE, COV);     // waves per slice
+    constexpr int WT = WV * SPW;                // waves per workgroup
     constexpr int KW = kLkSlice / WV;           // components per wave
     constexpr int CB = KW / 32;                 // 32-component blocks per wave
-    constexpr int NT = 64 * WV;                 // threads per workgroup
+    constexpr int NT = 64 * WT;                 // threads per workgroup
     using Sh = LkShape<COV, DP>;
     constexpr bool kIso = Sh::kIso;
     constexpr int KS = Sh::kKS, NFB = Sh::kNFB, RY = Sh::kRowY;
@@ -155,15 +158,15 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
     __shared__ __attribute__((aligned(16))) uint16_t ybuf[2][kT * RY];
     __shared__ __attribute__((aligned(16))) uint16_t gbuf[kStats ? WV : 1][kStats ? kT * RG : 8];
     __shared__ __attribute__((aligned(16))) uint16_t yh_t[2][kT];   // iso: |y|^2 2^-g, fp16
-    __shared__ uint4 plds[WV][CB][KL + 1][64];   // LDS-resident steps of each wave's panel
+    __shared__ uint4 plds[WT][CB][KL + 1][64];   // LDS-resident steps of each wave's panel
     __shared__ float2 dsc_l[DP];       // [e][8-column block], column 8 block + e: iso (c, s), diag (s, -c s)
     // E-step modes without statistics: one barrier per tile (the exchange's);
     // the exchange buffers alternate between tiles so that a wave writing the
     // next tile's values cannot overwrite values another wave still reads
     constexpr bool kOneBarrier = kExchange && !kStats;
     constexpr int NXB = kOneBarrier ? 2 : 1;
-    __shared__ float2 wpart_b[NXB][WV][kT];   // per-wave (max, sum) of each point, base-2 score units
-    __shared__ int warg_b[NXB][WV][kT];
+    __shared__ float2 wpart_b[NXB][WT][kT];   // per-wave (max, sum) of each point, base-2 score units
+    __shared__ int warg_b[NXB][WT][kT];
     __shared__ double llred[NT];
     // top-m mode: the slice's base-2 scores of the tile, each point's partial
     // lists (8 threads per point, 32 components each) and the running list
@@ -173,6 +176,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
     __shared__ int8_t chead[kTopm ? kT : 1][kTopm ? 9 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wl = w % WV, w0 = w - wl;                 // wave within its slice, the slice's first wave
     const int pn = lane & 31, hf = lane >> 5;           // point column, wave half
     const int gq = lane >> 4, gi = lane & 15;           // 16-lane group, lane in group
     const int G = gridDim.x, S = a.S;
@@ -181,18 +185,21 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
         slice = a.topm_slice;
         chunk = blockIdx.x;
     } else {
-        const int b = blockIdx.x;
-        if (G % (8 * S) == 0) {
+        // workgroup b -> (slice group, chunk); the groups of one chunk share an XCD
+        const int b = blockIdx.x, Sg = S / SPW;
+        int sg;
+        if (G % (8 * Sg) == 0) {
             const int r = b >> 3;
-            slice = r % S;
-            chunk = (r / S) * 8 + (b & 7);
+            sg = r % Sg;
+            chunk = (r / Sg) * 8 + (b & 7);
         } else {
-            slice = b % S;
-            chunk = b / S;
+            sg = b % Sg;
+            chunk = b / Sg;
         }
+        slice = sg * SPW + w / WV;
     }
-    const int nchunks = kTopm ? G : G / S;
-    const int kbase = slice * kLkSlice + w * KW;
+    const int nchunks = kTopm ? G : G / (S / SPW);
+    const int kbase = slice * kLkSlice + wl * KW;
     const int64_t n = a.n;
     const int d = a.d;
     const float F = a.prm[0];                   // panel scale 2^f
@@ -575,14 +582,15 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
                 if (want_arg) warg[w][pn] = bi;
             }
             __syncthreads();
-            float M = wpart[0][pn].x;
+            // the waves of this wave's slice: w0 .. w0 + WV - 1
+            float M = wpart[w0][pn].x;
 #pragma unroll
-            for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w2][pn].x);
+            for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w0 + w2][pn].x);
             const float Ms = M == -INFINITY ? 0.0f : M;
             float Z = 0.0f;
 #pragma unroll
             for (int w2 = 0; w2 < WV; ++w2) {
-                const float2 mz = wpart[w2][pn];
+                const float2 mz = wpart[w0 + w2][pn];
                 Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
             }
             float lse = Ms + fast_log2(Z);
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
                 arg = 0x7FFFFFFF;
 #pragma unroll
                 for (int w2 = WV - 1; w2 >= 0; --w2)
-                    if (wpart[w2][pn].x == M) arg = warg[w2][pn];
+                    if (wpart[w0 + w2][pn].x == M) arg = warg[w0 + w2][pn];
             }
             const int64_t p = prow + pn;
             if constexpr (MODE == LK_FUSED_EM || MODE == LK_FUSED_E) {
@@ -605,12 +613,12 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
                             const int xa = a.xarg[p];
                             if (xm > M || (xm == M && xa < arg)) arg = xa;
                         }
-                    } else if (w == 0 && hf == 0) {
+                    } else if (wl == 0 && hf == 0) {
                         a.lse_out[p] = lse;   // their statistics pass reads it
                     }
                 }
             }
-            if (w == 0 && hf == 0 && pvalid) {
+            if (wl == 0 && hf == 0 && pvalid) {
                 if constexpr (MODE == LK_SWEEP1) {
                     a.part_lse[(int64_t)slice * n + p] = lse;
                     if (want_arg) {
@@ -760,9 +768,9 @@ __global__ __launch_bounds__(64 * lk_waves(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG
 template <int COV, int DP, int MODE, bool VEC>
 hipError_t launch4(const Plan& p, const LkArgs& a, int grid, hipStream_t s) {
     if (p.xdt == GMM_BF16)
-        hipLaunchKernelGGL((k_lk<COV, DP, MODE, true, VEC>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
+        hipLaunchKernelGGL((k_lk<COV, DP, MODE, true, VEC>), dim3(grid), dim3(lk_threads(MODE, COV)), 0, s, a);
     else
-        hipLaunchKernelGGL((k_lk<COV, DP, MODE, false, VEC>), dim3(grid), dim3(64 * lk_waves(MODE, COV)), 0, s, a);
+        hipLaunchKernelGGL((k_lk<COV, DP, MODE, false, VEC>), dim3(grid), dim3(lk_threads(MODE, COV)), 0, s, a);
     return hipGetLastError();
 }
 
@@ -787,6 +795,8 @@ hipError_t launch1(const Plan& p, const LkArgs& a, int mode, int grid, hipStream
         case LK_FUSED_EM: return launch2<COV, LK_FUSED_EM>(p, a, grid, s);
         case LK_SWEEP1: return launch2<COV, LK_SWEEP1>(p, a, grid, s);
         case LK_SWEEP1 | kLkArg: return launch2<COV, LK_SWEEP1 | kLkArg>(p, a, grid, s);
+        case LK_SWEEP1 | kLkPair: return launch2<COV, LK_SWEEP1 | kLkPair>(p, a, grid, s);
+        case LK_SWEEP1 | kLkArg | kLkPair: return launch2<COV, LK_SWEEP1 | kLkArg | kLkPair>(p, a, grid, s);
         case LK_SWEEP2: return launch2<COV, LK_SWEEP2>(p, a, grid, s);
         case LK_FUSED_E: return launch2<COV, LK_FUSED_E>(p, a, grid, s);
         case LK_FUSED_E | kLkArg: return launch2<COV, LK_FUSED_E | kLkArg>(p, a, grid, s);
@@ -799,8 +809,9 @@ hipError_t launch1(const Plan& p, const LkArgs& a, int mode, int grid, hipStream
 
 hipError_t lk_launch(const Plan& p, const LkArgs& a, int mode, int grid, hipStream_t s) {
     // the argmax variants when the caller asked for it
-    if ((mode == LK_SWEEP1 && a.part_arg != nullptr) || (mode == LK_FUSED_E && a.out_arg != nullptr))
-        mode |= kLkArg;
+    const bool arg = (mode == LK_SWEEP1 && a.part_arg != nullptr) || (mode == LK_FUSED_E && a.out_arg != nullptr);
+    mode = lk_plan_mode(p, mode);
+    if (arg) mode |= kLkArg;
     if (p.cov == GMM_COV_ISO) return launch1<GMM_COV_ISO>(p, a, mode, grid, s);
     return launch1<GMM_COV_DIAG>(p, a, mode, grid, s);
 }

@@ -25,6 +25,9 @@ enum LkMode : int {
 // Added to LK_SWEEP1 / LK_FUSED_E when the per-point argmax is wanted: the
 // comparisons it needs are compiled only into those variants.
 constexpr int kLkArg = 8;
+// Added to LK_SWEEP1 when the number of slices is even: one workgroup of
+// eight waves scores two slices, so each tile is staged once for both.
+constexpr int kLkPair = 16;
 
 // Largest m of gmm_assign.
 constexpr int kLkMaxTopm = 16;
@@ -200,8 +203,20 @@ __host__ __device__ constexpr int lk_waves(int mode, int cov) {
 // overlap the other's vector work and latencies); the statistics modes need
 // up to 512 registers per lane and run one.
 __host__ __device__ constexpr int lk_wg_per_cu(int mode) {
+    if (mode & kLkPair) return 1;   // eight waves: two per SIMD already
     mode &= kLkArg - 1;
     return (mode == LK_SWEEP1 || mode == LK_FUSED_E) ? 2 : 1;
+}
+
+// Slices per workgroup and threads per workgroup of a mode (with its bits).
+__host__ __device__ constexpr int lk_slices_per_wg(int mode) { return (mode & kLkPair) ? 2 : 1; }
+__host__ __device__ constexpr int lk_threads(int mode, int cov) {
+    return 64 * lk_waves(mode, cov) * lk_slices_per_wg(mode);
+}
+
+// The variant bits that depend on the plan only (not on the call's outputs).
+inline int lk_plan_mode(const Plan& p, int mode) {
+    return (mode == LK_SWEEP1 && p.lk_slices % 2 == 0) ? (mode | kLkPair) : mode;
 }
 
 // Workgroups of the fused kernel in `mode` (chunks x slices), a function of

@@ -545,9 +545,11 @@ gmm_status lk_sum(const Plan& p, const LkWs& w, int P, int Pf, double* ll_out, h
 // each chunk's slices share an XCD; never more chunks than tiles, partial
 // slots (statistics modes) or LL / flag slots.
 int lk_grid(const Plan& p, int mode) {
-    const int S = mode == LK_TOPM ? 1 : p.lk_slices;   // top-m: one slice per launch
+    const int mb = lk_plan_mode(p, mode);
+    // workgroups per point chunk (top-m: one slice per launch)
+    const int S = mode == LK_TOPM ? 1 : p.lk_slices / lk_slices_per_wg(mb);
     const int64_t tiles = (p.n + kLkT - 1) / kLkT;
-    int64_t chunks = (int64_t)lk_wg_per_cu(mode) * device_cu_count() / S;
+    int64_t chunks = (int64_t)lk_wg_per_cu(mb) * device_cu_count() / S;
     if (chunks >= 8) chunks = chunks / 8 * 8;
     if (chunks < 1) chunks = 1;
     if (chunks > tiles) chunks = tiles < 1 ? 1 : tiles;
