@@ -155,15 +155,20 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
     constexpr int KL = kTight ? DP / 16 : 0;   // panel steps [0, KL) and the bias step in LDS
     constexpr int KR = KS - 1 - KL;            // panel steps in registers: [KL, KS - 1)
 
-    __shared__ __attribute__((aligned(16))) uint16_t ybuf[2][kT * RY];
+    // tiles of X in LDS: double buffered; the fused E+M mode keeps three, so
+    // that the tile being staged is never one a slower wave still reads for
+    // its statistics and the exchange barrier is the only one per tile
+    constexpr int NYB = (kExchange && kStats) ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) uint16_t ybuf[NYB][kT * RY];
     __shared__ __attribute__((aligned(16))) uint16_t gbuf[kStats ? WV : 1][kStats ? kT * RG : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t yh_t[2][kT];   // iso: |y|^2 2^-g, fp16
+    __shared__ __attribute__((aligned(16))) uint16_t yh_t[NYB][kT];   // iso: |y|^2 2^-g, fp16
     __shared__ uint4 plds[WT][CB][KL + 1][64];   // LDS-resident steps of each wave's panel
     __shared__ float2 dsc_l[DP];       // [e][8-column block], column 8 block + e: iso (c, s), diag (s, -c s)
-    // E-step modes without statistics: one barrier per tile (the exchange's);
-    // the exchange buffers alternate between tiles so that a wave writing the
-    // next tile's values cannot overwrite values another wave still reads
-    constexpr bool kOneBarrier = kExchange && !kStats;
+    // the modes that exchange per-point values between waves: one barrier per
+    // tile (the exchange's); the exchange buffers alternate between tiles so
+    // that a wave writing the next tile's values cannot overwrite values
+    // another wave still reads
+    constexpr bool kOneBarrier = kExchange;
     constexpr int NXB = kOneBarrier ? 2 : 1;
     __shared__ float2 wpart_b[NXB][WT][kT];   // per-wave (max, sum) of each point, base-2 score units
     __shared__ int warg_b[NXB][WT][kT];
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
 
     // diagonal bias slots: constant [1, 1, 0...] in both tile buffers
     if constexpr (!kIso) {
-        for (int i = tid; i < 2 * kT; i += NT) {
+        for (int i = tid; i < NYB * kT; i += NT) {
             uint4* bias = reinterpret_cast<uint4*>(ybuf[i / kT] + Sh::ych(i % kT, Sh::kFCh));
             bias[0] = make_uint4(0x3C003C00u, 0u, 0u, 0u);
             bias[1] = make_uint4(0u, 0u, 0u, 0u);
@@ -456,7 +461,8 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
     __syncthreads();
 
     for (int64_t t = t0; t < t1; ++t) {
-        const int cur = (int)((t - t0) & 1);
+        const int cur = (int)((t - t0) % NYB), nxt = cur + 1 == NYB ? 0 : cur + 1;
+        const int par = (int)((t - t0) & 1);
         const uint16_t* yb = ybuf[cur];
         const int64_t prow = t * kT;
         const bool pvalid = prow + pn < n;
@@ -505,11 +511,11 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
                     const half8 pa = in_lds(ks) ? pq[cb][ks] : pnl[cb][in_lds(ks) ? 0 : ks - KL];
                     scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
                 }
-                if (ks < kPairs) stage_pair(cur ^ 1, ks);
+                if (ks < kPairs) stage_pair(nxt, ks);
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int sp = KS; sp < kPairs; ++sp) stage_pair(cur ^ 1, sp);
+            for (int sp = KS; sp < kPairs; ++sp) stage_pair(nxt, sp);
             // the loads of the tile after next
             load_tile(t + 2 < t1 ? t + 2 : t1 - 1);
         }
@@ -563,8 +569,8 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
         }
 
         if constexpr (kExchange) {
-            float2(*wpart)[kT] = wpart_b[kOneBarrier ? cur : 0];
-            int(*warg)[kT] = warg_b[kOneBarrier ? cur : 0];
+            float2(*wpart)[kT] = wpart_b[kOneBarrier ? par : 0];
+            int(*warg)[kT] = warg_b[kOneBarrier ? par : 0];
             // this wave's (max, sum) per point, base-2 score units
             float m = mcb[0];
 #pragma unroll
@@ -711,8 +717,9 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
             }
         }
 
-        // the next tile was staged by every wave before the exchange barrier
-        // (one-barrier modes), and nothing reads this tile after it
+        // one-barrier modes: the next tile was staged by every wave before the
+        // exchange barrier, and the tile staged during the next one is not
+        // this one (three buffers when the statistics read this tile after it)
         if constexpr (!kOneBarrier) __syncthreads();
     }
 
