@@ -189,16 +189,20 @@ def test_workload_shapes_subset(gmm_lib, name, n):
 
 
 XC_CASES = [
-    # n, d, k, cov: one slice (fused kernel) and several (two sweeps)
-    (4000, 32, 100, "iso"),
-    (4000, 32, 100, "diag"),
-    (3000, 48, 300, "diag"),
-    (3000, 24, 520, "iso"),
+    # n, d, k, cov, x_dtype, ldx_pad, misalign: one slice (fused kernel) and
+    # several (two sweeps); vector and element-wise row loads
+    (4000, 32, 100, "iso", "bf16", 0, False),
+    (4000, 32, 100, "diag", "bf16", 0, False),
+    (3000, 48, 300, "diag", "bf16", 0, False),
+    (3000, 24, 520, "iso", "bf16", 0, False),
+    (2000, 17, 300, "diag", "f16", 3, True),
+    (2500, 40, 100, "iso", "f16", 0, False),
 ]
 
 
-@pytest.mark.parametrize("n,d,k,cov", XC_CASES, ids=[f"n{a}-d{b}-k{c}-{e}" for a, b, c, e in XC_CASES])
-def test_exact_components(gmm_lib, n, d, k, cov):
+@pytest.mark.parametrize("n,d,k,cov,x_dtype,ldx_pad,misalign", XC_CASES,
+                         ids=[f"n{a}-d{b}-k{c}-{e}-{f}-pad{g}-mis{int(h)}" for a, b, c, e, f, g, h in XC_CASES])
+def test_exact_components(gmm_lib, n, d, k, cov, x_dtype, ldx_pad, misalign):
     """Components collapsed onto single points far from the data mean
     (variance 1e-4 at a stored point): their fp16 expanded-form score is off
     by thousands of nats, so the library takes them out of the panel and
@@ -207,7 +211,7 @@ def test_exact_components(gmm_lib, n, d, k, cov):
     E-step's per-point log-normaliser, the reduced-precision gate of the
     step, the collapsed components' s0 / s1 / s2 element by element, the
     top-m lists, and a second step from the GPU's own parameters."""
-    xd, xg, ldx, (pi0, mu0, cov0) = _make(n, d, k, cov, "bf16", 0, False, seed=7 * k + d)
+    xd, xg, ldx, (pi0, mu0, cov0) = _make(n, d, k, cov, x_dtype, ldx_pad, misalign, seed=7 * k + d)
     rng = np.random.default_rng(k + 1)
     pick = np.sort(rng.choice(k, size=6, replace=False))
     far = np.argsort(-np.abs(xd - xd.mean(0)).sum(1))[:6]   # the points furthest out
@@ -215,10 +219,10 @@ def test_exact_components(gmm_lib, n, d, k, cov):
     cov0[pick] = 1e-4
     ill = ill_conditioned((pi0, mu0, cov0), xd, cov)
     assert set(pick.tolist()) <= set(ill), (pick, ill[:16])
-    gm = gmm_lib.Gmm(n, d, k, cov, "bf16", ldx=ldx)
+    gm = gmm_lib.Gmm(n, d, k, cov, x_dtype, ldx=ldx)
     th = to_dev(pi0, mu0, cov0)
     p = params64(cov, *th)
-    what = f"n{n} d{d} k{k} {cov}"
+    what = f"n{n} d{d} k{k} {cov} {x_dtype}"
     # E-step alone
     ll_e, lse, arg = gpu_loglik(gm, xg, th)
     assert gm.diagnostics().ill_cond >= len(pick)
