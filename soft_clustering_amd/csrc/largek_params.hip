@@ -385,10 +385,24 @@ __global__ __launch_bounds__(256) void k_lk_reduce(
     for (int col = tid; col < ncol; col += 256) {
         double a0 = 0.0;
         if (pos < 0) {
-            for (int ch = 0; ch < nchunks; ++ch) {
-                const int b = lk_wg_of(slice, ch, G, S);
-                a0 += part[((int64_t)b * kLkSlice + kl) * ncol + col];
+            // eight running sums (chunk ch into sum ch % 8), so that eight
+            // loads are in flight; combined in a fixed tree
+            double a8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a8[u] = 0.0;
+            int ch = 0;
+            for (; ch + 8 <= nchunks; ch += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int b = lk_wg_of(slice, ch + u, G, S);
+                    a8[u] += part[((int64_t)b * kLkSlice + kl) * ncol + col];
+                }
             }
+            for (; ch < nchunks; ++ch) {
+                const int b = lk_wg_of(slice, ch, G, S);
+                a8[ch % 8] += part[((int64_t)b * kLkSlice + kl) * ncol + col];
+            }
+            a0 = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
         } else {   // scored exactly: its own slots (the panel gave it no responsibility)
             const int nx = *xc_n;
             const int P = lk_xc_slots(nx, ncol, xc_slot_doubles, kLkXcSlots);
