@@ -315,11 +315,21 @@ __global__ __launch_bounds__(256) void k_lk_merge(int64_t n, int S, float* part_
     const int R = S + (*xc_n > 0 ? 1 : 0);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += stride) {
+        // every row's value first (all loads in flight), then the combine
+        constexpr int kMaxRows = 4096 / kLkSlice + 1;
+        float v[kMaxRows];
         float M = -INFINITY;
-        for (int s = 0; s < R; ++s) M = fmaxf(M, part_lse[(int64_t)s * n + p]);
+#pragma unroll
+        for (int s = 0; s < kMaxRows; ++s)
+            if (s < R) v[s] = part_lse[(int64_t)s * n + p];
+#pragma unroll
+        for (int s = 0; s < kMaxRows; ++s)
+            if (s < R) M = fmaxf(M, v[s]);
         const float Ms = M == -INFINITY ? 0.0f : M;
         float Z = 0.0f;
-        for (int s = 0; s < R; ++s) Z += fast_exp2(part_lse[(int64_t)s * n + p] - Ms);
+#pragma unroll
+        for (int s = 0; s < kMaxRows; ++s)
+            if (s < R) Z += fast_exp2(v[s] - Ms);
         const float lse = Ms + fast_log2(Z);
         part_lse[p] = lse;
         ll += (double)lse;
