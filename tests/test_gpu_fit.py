@@ -101,7 +101,10 @@ def test_one_step_parity_every_iteration(gmm_lib, tiny):
 
 
 @pytest.mark.parametrize("cov,x_dtype,n,d,k", [("diag", "f32", 4096, 16, 8), ("full", "f16", 3000, 16, 4),
-                                                ("iso", "bf16", 3000, 32, 40)])
+                                                ("iso", "bf16", 3000, 32, 40),
+                                                # two sweeps, segmented passes and, as components
+                                                # shrink, exactly scored ones inside the graph
+                                                ("diag", "bf16", 4000, 32, 300)])
 def test_graph_and_batch_invariance(gmm_lib, cov, x_dtype, n, d, k):
     rng = np.random.default_rng(5)
     mu_t = rng.uniform(-5, 5, size=(k, d))
@@ -118,7 +121,8 @@ def test_graph_and_batch_invariance(gmm_lib, cov, x_dtype, n, d, k):
                                batch=batch, use_graph=use_graph, stream=stream)
         torch.cuda.synchronize()
         out.append((nit, hist.cpu(), pi.cpu(), mu.cpu(), cv.cpu()))
-        print(f"{cov}: graph {use_graph} batch {batch}: {nit} iterations, LL {hist[nit - 1].item():.6e}", flush=True)
+        print(f"{cov}: graph {use_graph} batch {batch}: {nit} iterations, LL {hist[nit - 1].item():.6e}, "
+              f"exactly scored components at the end {gm.diagnostics().ill_cond}", flush=True)
     for o in out[1:]:
         assert o[0] == out[0][0]
         for a, b in zip(o[1:], out[0][1:]):
@@ -135,3 +139,44 @@ def test_graph_and_batch_invariance(gmm_lib, cov, x_dtype, n, d, k):
         gm.finalize()
         torch.cuda.synchronize()
         assert metrics.rel(ll.item(), hist[t]) <= 1e-6, (t, ll.item(), hist[t])
+
+
+def test_fit_with_exact_components(gmm_lib):
+    """A given start with components collapsed onto single far points (the
+    large-K family scores them exactly, outside the fp16 panel): the captured
+    iteration replays the exact-component launches too.  Graph replay and
+    direct launches agree bit for bit, and the LL history equals that of the
+    plain em_step + finalize sequence from the same start."""
+    from tests.test_gpu_largek import _make
+    n, d, k = 3000, 24, 300
+    xd, xg, ldx, (pi0, mu0, cov0) = _make(n, d, k, "diag", "bf16", 0, False, seed=77)
+    rng = np.random.default_rng(78)
+    pick = rng.choice(k, size=5, replace=False)
+    far = np.argsort(-np.abs(xd - xd.mean(0)).sum(1))[:5]
+    mu0[pick] = xd[far].astype(np.float32)
+    cov0[pick] = 1e-4
+    gm = gmm_lib.Gmm(n, d, k, "diag", "bf16", ldx=ldx)
+    th0 = to_dev(pi0, mu0, cov0)
+    gm.prepare(*th0)
+    ll = torch.zeros(1, dtype=torch.float64, device="cuda")
+    gm.loglik(xg, ll)
+    torch.cuda.synchronize()
+    assert gm.diagnostics().ill_cond >= len(pick)
+    out = []
+    for use_graph, batch in ((True, 3), (False, 1)):
+        pi, mu, cv = (t.clone() for t in th0)
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            nit, hist = gm.fit(xg, pi, mu, cv, max_iter=6, tol=0.0, init="given",
+                               batch=batch, use_graph=use_graph, stream=stream)
+        torch.cuda.synchronize()
+        out.append((nit, hist.cpu(), pi.cpu(), mu.cpu(), cv.cpu()))
+    assert out[0][0] == out[1][0] == 6
+    for a, b in zip(out[0][1:], out[1][1:]):
+        assert torch.equal(a, b)
+    gm.prepare(*th0)
+    for t in range(6):
+        gm.em_step(xg, ll)
+        gm.finalize()
+        torch.cuda.synchronize()
+        assert ll.item() == out[0][1][t].item(), (t, ll.item(), out[0][1][t].item())
