@@ -255,7 +255,7 @@ def main(argv=None):
                          "whose HBM counters calibrate FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the fused EM "
+        print(f"bench.py: the benchmark runs on exactly one GPU (asked for {a.gpus}); the fused EM "
               "iteration is single-GPU and multi-GPU sharding is not built.", file=sys.stderr)
         return 2
 

@@ -30,7 +30,7 @@ Generators (published definitions, implemented here from them):
   "A sample of brilliance", CACM 1987): for j = N-K .. N-1 draw t uniform in
   [0, j]; take t, or j when t is already taken.
 
-Readings (listed in the design doc): ties in the top-m order go to the lower
+Readings of points the pages leave open: ties in the top-m order go to the lower
 component index; the random draw in [0, j] is the generator's output modulo
 j + 1; the start is K distinct points in increasing index order as means,
 unit (co)variances and equal weights; the loop stops after iteration t >= 1

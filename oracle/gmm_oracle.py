@@ -29,7 +29,7 @@ What it computes is the textbook EM iteration, slowly and directly:
 Precision: every operation is IEEE fp64 (numpy float64).  X is whatever the
 caller stored (fp32 / fp16 / bf16 values), upcast exactly to fp64.
 
-Readings of points the pages leave open (each one listed in the design doc):
+Readings of points the pages leave open:
   * LL is the total sum_n lse_n under the parameters the E-step used.
   * Variances are the maximum-likelihood ones (divide by N_k), clamped below
     at var_floor (a clamp keeps EM monotone; an additive floor would not).
