@@ -149,6 +149,8 @@ CASES = [
     # statistics of each group normalised with the merged LSE
     (3000, 32, 40, 0, False),    # 3 groups
     (2500, 64, 33, 0, False),    # 3 groups on the two-stage kernel
+    (1500, 1, 3, 0, False),      # D = 1
+    (800, 2, 20, 1, True),       # D = 2, two groups, element-wise loads
     (2000, 16, 100, 0, False),   # 7 groups
     (1500, 24, 17, 3, True),     # 2 groups, element-wise loads
 ]

@@ -135,6 +135,8 @@ CASES = [
     (999, 17, 200, "diag", "bf16", 3, True),
     (5003, 128, 1024, "diag", "bf16", 0, False),
     (2000, 64, 777, "diag", "f16", 16, False),
+    (500, 1, 100, "diag", "bf16", 0, False),      # D = 1
+    (777, 2, 300, "iso", "f16", 1, True),         # D = 2, two slices, element-wise loads
 ]
 
 
@@ -257,6 +259,38 @@ def test_exact_components(gmm_lib, n, d, k, cov, x_dtype, ldx_pad, misalign):
     ll2, st2, th2 = gpu_step(gm, xg, *th1)
     ref2 = oracle.em_step(xd, params64(cov, *th1))
     check_later_step(ref2, ll2, st2, th2, th1, xd, cov, what=f"  second step {what}")
+
+
+def test_largest_k(gmm_lib):
+    """K = 4096, the largest the large-K family takes (16 slices, the merge of
+    17 rows with an exactly scored component among them): 4096 separated
+    isotropic clusters of three points each in D = 8, the components started
+    near them; the E-step argmax, one step and a second step against the
+    oracle."""
+    rng = np.random.default_rng(4096)
+    n, d, k = 3 * 4096, 8, 4096
+    mu_t = rng.uniform(-60.0, 60.0, size=(k, d))
+    z = np.repeat(np.arange(k), 3)
+    xf = (mu_t[z] + 0.5 * rng.standard_normal((n, d))).astype(np.float32)
+    xs = torch.from_numpy(xf).to(torch.bfloat16)
+    xd = xs.double().numpy()
+    mu0 = (mu_t + 0.1 * rng.standard_normal((k, d))).astype(np.float32)
+    cov0 = rng.uniform(0.2, 0.4, size=k).astype(np.float32)
+    mu0[7], cov0[7] = xd[3 * 7], 1e-4   # one component collapsed onto a point: scored exactly
+    pi0 = np.full(k, 1.0 / k, np.float32)
+    gm = gmm_lib.Gmm(n, d, k, "iso", "bf16")
+    xg = xs.cuda()
+    th = to_dev(pi0, mu0, cov0)
+    p = params64("iso", *th)
+    _, lse, arg = gpu_loglik(gm, xg, th)
+    assert gm.diagnostics().ill_cond >= 1
+    check_argmax(xd, p, arg, what="k4096 loglik")
+    ll, st, th1 = gpu_step(gm, xg, *th)
+    ref = oracle.em_step(xd, p)
+    check_reduced(ref, ll, st, th1, what="  k4096 em step")
+    ll2, st2, th2 = gpu_step(gm, xg, *th1, prepare=False)
+    ref2 = oracle.em_step(xd, params64("iso", *th1))
+    check_later_step(ref2, ll2, st2, th2, th1, xd, "iso", what="  k4096 second step")
 
 
 def test_determinism_bitwise(gmm_lib):
