@@ -73,7 +73,7 @@ constexpr int kLkMergeWgs = 1024;
 
 // Rows of X sampled for the centre / scale, and workgroups scanning them.
 constexpr int kLkScanRows = 4096;
-constexpr int kLkScanWgs = 32;
+constexpr int kLkScanWgs = 256;   // 16 sample rows per workgroup: the scattered row reads all in flight
 
 struct LkWs {
     float *pi, *mu, *var;        // fp32 parameters theta (var: [K] iso, [K*D] diag)

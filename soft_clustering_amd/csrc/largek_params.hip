@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void k_lk_scan(const uint16_t* __restrict__ x,
     const int per = kLkScanRows / kLkScanWgs;
     float sum = 0.0f, lo = INFINITY, hi = -INFINITY;
     if (dd < d) {
+#pragma unroll 8
         for (int i = blockIdx.x * per + ph; i < (blockIdx.x + 1) * per && i < ns; i += nph) {
             const int64_t row = (int64_t)i * n / ns;
             const uint32_t b = x[row * ldx + dd];
@@ -112,21 +113,42 @@ __global__ __launch_bounds__(256) void k_lk_scan(const uint16_t* __restrict__ x,
 // |x_d - c_d|, so the sampled y' lie in [-16, 16] and y'^2 stays below the
 // fp16 maximum for |y'| < 255.  Isotropic: 2^-g with the sampled bound of
 // |x - c|^2 times 2^-g below 2^14, so |y|^2 2^-g stays in fp16 range for
-// points within twice the sampled spread.  One workgroup of 128 threads.
-__global__ __launch_bounds__(128) void k_lk_centre(int64_t n, int d, int dp, bool bf16, bool iso,
-                                                   const float* scan, float2* dsc, float* prm) {
-    __shared__ double red[128];
-    const int dd = threadIdx.x;
-    double r2 = 0.0;
+// points within twice the sampled spread.  One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_lk_centre(int64_t n, int d, int dp, bool bf16, bool iso,
+                                                    const float* scan, float2* dsc, float* prm) {
+    // thread (part, dd): dimension dd = tid % 128 over the scan workgroups
+    // b = part (mod 8); the eight parts combined in a fixed tree through LDS
+    constexpr int kParts = 8;
+    static_assert(kLkScanWgs % kParts == 0, "scan workgroups in groups of eight");
+    __shared__ double red[1024];
+    __shared__ double ps[kParts][128];
+    __shared__ float plo[kParts][128], phi[kParts][128];
+    const int dd = threadIdx.x % 128, part = threadIdx.x / 128;
     if (dd < d) {
-        const int64_t ns = n < kLkScanRows ? n : kLkScanRows;
         double s = 0.0;
         float lo = INFINITY, hi = -INFINITY;
-        for (int b = 0; b < kLkScanWgs; ++b) {
+#pragma unroll 8
+        for (int b = part; b < kLkScanWgs; b += kParts) {
             const float* o = scan + ((int64_t)b * dp + dd) * 3;
             s += (double)o[0];
             lo = fminf(lo, o[1]);
             hi = fmaxf(hi, o[2]);
+        }
+        ps[part][dd] = s;
+        plo[part][dd] = lo;
+        phi[part][dd] = hi;
+    }
+    __syncthreads();
+    double r2 = 0.0;
+    if (part == 0 && dd < d) {
+        const int64_t ns = n < kLkScanRows ? n : kLkScanRows;
+        const double s = ((ps[0][dd] + ps[1][dd]) + (ps[2][dd] + ps[3][dd])) +
+                         ((ps[4][dd] + ps[5][dd]) + (ps[6][dd] + ps[7][dd]));
+        float lo = plo[0][dd], hi = phi[0][dd];
+#pragma unroll
+        for (int q = 1; q < kParts; ++q) {
+            lo = fminf(lo, plo[q][dd]);
+            hi = fmaxf(hi, phi[q][dd]);
         }
         // c is rounded to X's storage type, so x - c is exact in fp32 and, for
         // data within ~2^11 storage ulps of c, exact in fp16 too: no rounding
@@ -142,11 +164,11 @@ __global__ __launch_bounds__(128) void k_lk_centre(int64_t n, int d, int dp, boo
             r2 = r * r;
         }
         dsc[dd] = make_float2((float)c, (float)ldexp(1.0, -e));
-    } else if (dd < dp) {
+    } else if (part == 0 && dd < dp) {
         dsc[dd] = make_float2(0.0f, 0.0f);
     }
     r2 = block_sum_f64(r2, red);
-    if (dd == 0) {
+    if (threadIdx.x == 0) {
         int g = 0;
         if (iso && r2 > 0.0 && isfinite(r2)) {
             g = ilogb(r2) - 13;
@@ -491,7 +513,7 @@ hipError_t refresh_panel(const Plan& p, const LkWs& w, const void* x, hipStream_
     else
         hipLaunchKernelGGL(k_lk_scan<false>, dim3(kLkScanWgs), dim3(256), 0, s, (const uint16_t*)x,
                            p.n, p.ldx, (int)p.d, p.dp, w.scan);
-    hipLaunchKernelGGL(k_lk_centre, dim3(1), dim3(128), 0, s, p.n, (int)p.d, p.dp,
+    hipLaunchKernelGGL(k_lk_centre, dim3(1), dim3(1024), 0, s, p.n, (int)p.d, p.dp,
                        p.xdt == GMM_BF16, iso, w.scan, w.dsc, w.prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
