@@ -60,11 +60,11 @@ TRAFFIC = {
         sources="be8e56b42ee450f8", fetch_kib=125175.4, write_kib=4144.3,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="e66d40fd3b9a4f07", fetch_kib=1251328.3, write_kib=75823.9,
-        copy_bytes=2.56e+09, copy_fetch_kib=1250036.75, copy_write_kib=2500000.0),
+        sources="f06237dc1256a653", fetch_kib=1251546.0, write_kib=76509.9,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250035.8125, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="e66d40fd3b9a4f07", fetch_kib=69072610.8, write_kib=7354770.2,
-        copy_bytes=5.12e+10, copy_fetch_kib=25000258.6875, copy_write_kib=50000000.0),
+        sources="f06237dc1256a653", fetch_kib=68083652.2, write_kib=7375739.1,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000246.0625, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
         sources="e4a222026d575f44", fetch_kib=63933.3, write_kib=35532.7,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
