@@ -96,16 +96,21 @@ typedef struct {
                                 visibly: its LL is NaN, nonfinite is set and
                                 gmm_finalize keeps theta.  NaN in X shows up as
                                 a non-finite LL */
-    int32_t ill_cond;        /* large-K plans: components whose fp16 expanded
-                                score [y^2, y, 1] . panel is estimated to carry
-                                more than 1 nat of rounding error near their
-                                own mean (a variance small against the
-                                component's distance from the data centre,
-                                [LP-GMM] 5.1 fourth step).  They are taken out
+    int32_t ill_cond;        /* components whose expanded score [y^2, y, 1] .
+                                panel is estimated to carry more than 1 nat of
+                                rounding error near their own mean (a variance
+                                small against the component's distance from
+                                the data centre, [LP-GMM] 5.1 fourth step).
+                                Large-K plans (fp16 panel): they are taken out
                                 of the panel and scored in the exact centred
-                                form in fp32 ([LP-GMM] 1.2, 1.3); the count is
-                                informational.  0 on the other paths, whose
-                                scores are centred or split into fp16 pairs */
+                                form in fp32 ([LP-GMM] 1.2, 1.3), so the count
+                                is informational.  Diagonal fp32 plans (split
+                                fp16 panel, about 22 bits): counted from the
+                                prepared theta; only components near the
+                                variance floor far from the centre get there,
+                                and their LL contribution then carries that
+                                error (their statistics do not).  0 for full
+                                covariance, whose score is centred */
     int32_t reserved;
     double  ll;              /* LL of the last gmm_em_step / gmm_loglik */
 } gmm_diag;

@@ -288,6 +288,49 @@ gmm_status gmm_get_stats(const gmm_desc* desc, const void* ws, size_t ws_bytes, 
     return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }
 
+// Diagonal fp32 path: components whose split-fp16 expanded score [y^2 | y] .
+// panel (about 22 significant bits per term) is estimated to carry more than
+// one nat of rounding error near their own mean: the terms A y^2 and B y at
+// |mu - c| + 3 sigma from the centre c, relative error 2^-22 each, random
+// signs ([LP-GMM] 5.1 fourth step: a small variance makes the score swing).
+// A component at the variance floor far from the centre reaches tens of nats
+// (the LL then misses the fp32 bar; the statistics keep it, since such a
+// component owns its points whatever the error).  Host arithmetic on theta
+// and the centre, read in fixed-size pieces.
+static hipError_t diag_ill_cond(const Plan& p, const char* base, int32_t* count) {
+    constexpr int kCompPiece = 16, kMaxD = 128;
+    float cen[kMaxD], mu[kCompPiece * kMaxD], var[kCompPiece * kMaxD];
+    const int d = (int)p.d;
+    hipError_t e = hipMemcpy(cen, base + p.off_shift, sizeof(float) * d, hipMemcpyDeviceToHost);
+    int cnt = 0;
+    for (int64_t k0 = 0; k0 < p.k && e == hipSuccess; k0 += kCompPiece) {
+        const int m = (int)(p.k - k0 < kCompPiece ? p.k - k0 : kCompPiece);
+        e = hipMemcpy(mu, base + p.off_mu + sizeof(float) * k0 * d, sizeof(float) * m * d,
+                      hipMemcpyDeviceToHost);
+        if (e == hipSuccess)
+            e = hipMemcpy(var, base + p.off_cov + sizeof(float) * k0 * d, sizeof(float) * m * d,
+                          hipMemcpyDeviceToHost);
+        for (int i = 0; i < m && e == hipSuccess; ++i) {
+            double err2 = 0.0;
+            bool ok = true;
+            for (int dd = 0; dd < d; ++dd) {
+                const double v = var[i * d + dd], mc = fabs((double)mu[i * d + dd] - (double)cen[dd]);
+                if (!(v > 0.0) || !isfinite(v) || !isfinite(mc)) {
+                    ok = false;
+                    break;
+                }
+                const double yt = mc + 3.0 * sqrt(v);
+                const double ta = 0.5 * kLog2e * yt * yt / v, tb = kLog2e * mc * yt / v;
+                err2 += ta * ta + tb * tb;
+            }
+            const double nats = sqrt(err2) * ldexp(1.0, -22) * 0.81649658 * 0.69314718;
+            if (ok && nats > 1.0) ++cnt;
+        }
+    }
+    *count = cnt;
+    return e;
+}
+
 gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes, gmm_diag* out,
                            hipStream_t stream) {
     Plan p;
@@ -339,6 +382,7 @@ gmm_status gmm_diagnostics(const gmm_desc* desc, const void* ws, size_t ws_bytes
     }
     if (misc[0]) out->nonfinite = 1;
     if (p.path == PATH_LARGEK) out->x_range = misc[1];
+    if (dg && e == hipSuccess) e = diag_ill_cond(p, base, &out->ill_cond);
     out->ll = ll;
     return e == hipSuccess ? GMM_OK : GMM_E_HIP;
 }

@@ -259,3 +259,67 @@ def test_full_size_diag_workload(gmm_lib):
     idx = np.random.default_rng(0).choice(w.n, 4096, replace=False)
     _, lse_ref, _ = oracle.loglik(x[idx].double().numpy(), params64("diag", pi, mu, cov))
     np.testing.assert_allclose(lse.cpu().numpy()[idx], lse_ref, rtol=2e-5, atol=5e-3)
+
+
+def _split_score_error_nats(mu, var, c):
+    """The error model of the split-fp16 expanded score (about 22 bits per
+    term): A y^2 and B y at |mu - c| + 3 sigma, relative 2^-22 each, random
+    signs; nats per component."""
+    mc = np.abs(mu - c)
+    yt = mc + 3.0 * np.sqrt(var)
+    ta = 0.5 * 1.4426950408889634 * yt * yt / var
+    tb = 1.4426950408889634 * mc * yt / var
+    return np.sqrt(np.sum(ta * ta + tb * tb, axis=1)) * 2.0 ** -22 * np.sqrt(2.0 / 3.0) * np.log(2.0)
+
+
+@pytest.mark.parametrize("var_c", [1e-4, 1e-6])
+def test_collapsed_components(gmm_lib, var_c):
+    """Three components collapsed onto single far points.  At variance 1e-4
+    the split-fp16 score still resolves them: the whole fp32 step gate holds.
+    At the default variance floor (1e-6) their expanded-form scores carry
+    tens of nats of rounding error near their points ([LP-GMM] 5.1, fourth
+    step): the library reports them (gmm_diag.ill_cond), the statistics and
+    parameters still hold the fp32 bar (each owns its point whatever the
+    error), and the LL error stays within the estimated score error of
+    those components times their mass."""
+    rng = np.random.default_rng(11)
+    n, d, k = 4000, 32, 16
+    mu_t = rng.uniform(-6, 6, size=(k, d))
+    xf = (mu_t[rng.integers(0, k, n)] + rng.standard_normal((n, d))).astype(np.float32)
+    far = np.argsort(-np.abs(xf - xf.mean(0)).sum(1))[:3]
+    xd = xf.astype(np.float64)
+    mu0 = xf[rng.choice(n, k, replace=False)].copy()
+    cov0 = np.ones((k, d), np.float32)
+    pi0 = np.full(k, 1.0 / k, np.float32)
+    pick = [1, 4, 7]
+    mu0[pick] = xf[far]
+    cov0[pick] = var_c
+    gm = gmm_lib.Gmm(n, d, k, "diag", "f32")
+    th = to_dev(pi0, mu0, cov0)
+    ll, st, th1 = gpu_step(gm, torch.from_numpy(xf).cuda(), *th)
+    ref = oracle.em_step(xd, params64("diag", *th))
+    c = mu0[int(np.argmax(pi0))].astype(np.float64)   # the centre: the heaviest component's mean
+    est = _split_score_error_nats(mu0.astype(np.float64), cov0.astype(np.float64), c)
+    flagged = np.nonzero(est > 1.0)[0]
+    gm.prepare(*th)
+    dg = gm.diagnostics()
+    print(f"var {var_c}: estimated nats of the collapsed components {est[pick]}, "
+          f"library ill_cond {dg.ill_cond}, LL rel err {metrics.rel(ll, ref.ll):.2e}", flush=True)
+    assert dg.ill_cond == len(flagged)
+    if var_c >= 1e-4:
+        assert len(flagged) == 0
+        check_step(ref, ll, st, th1, what=f"collapsed var {var_c}", xd=xd)
+        return
+    assert set(pick) <= set(flagged.tolist())
+    errs = {
+        "s0": metrics.rel_inf(st.s0.cpu().numpy(), ref.nk),
+        "s1": metrics.rel_inf(st.s1.cpu().numpy(), ref.s1),
+        "s2": metrics.rel_inf(st.s2.cpu().numpy(), ref.s2),
+        "pi": metrics.rel_inf(th1[0].cpu().numpy(), ref.params.pi),
+        "mu": metrics.rel_inf(th1[1].cpu().numpy(), ref.params.mu),
+        "cov": metrics.rel_inf(th1[2].cpu().numpy(), ref.params.cov),
+    }
+    print("   ", " ".join(f"{kk}={v:.2e}" for kk, v in errs.items()), flush=True)
+    assert all(v <= FP32_TOL for v in errs.values()), errs
+    bound = 3.0 * float(np.sum(est[flagged] * np.asarray(ref.nk)[flagged])) + FP32_TOL * abs(ref.ll)
+    assert abs(ll - ref.ll) <= bound, (ll, ref.ll, bound)
