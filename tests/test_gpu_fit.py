@@ -104,7 +104,9 @@ def test_one_step_parity_every_iteration(gmm_lib, tiny):
                                                 ("iso", "bf16", 3000, 32, 40),
                                                 # two sweeps, segmented passes and, as components
                                                 # shrink, exactly scored ones inside the graph
-                                                ("diag", "bf16", 4000, 32, 300)])
+                                                ("diag", "bf16", 4000, 32, 300),
+                                                # full covariance in two groups of components
+                                                ("full", "f16", 3000, 8, 20)])
 def test_graph_and_batch_invariance(gmm_lib, cov, x_dtype, n, d, k):
     rng = np.random.default_rng(5)
     mu_t = rng.uniform(-5, 5, size=(k, d))
