@@ -58,6 +58,28 @@ __device__ __forceinline__ int row16_min_i(int v) {
 }
 
 // Hardware base-2 transcendental instructions (v_exp_f32, v_log_f32).
+// The values of v in lanes l and l ^ 32 (the two halves of a wave of 64)
+// from one v_permlane32_swap, a VALU exchange (a shuffle is an LDS round
+// trip, which also waits for every LDS access issued before it).  In every
+// lane .x is the lower half's value and .y the upper half's, so combining
+// the two gives bitwise the same result in both lanes.
+__device__ __forceinline__ uint2 wave_halves(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return make_uint2(r[0], r[1]);
+}
+__device__ __forceinline__ float halves_max(float v) {
+    const uint2 h = wave_halves(__float_as_uint(v));
+    return fmaxf(__uint_as_float(h.x), __uint_as_float(h.y));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const uint2 h = wave_halves(__float_as_uint(v));
+    return __uint_as_float(h.x) + __uint_as_float(h.y);
+}
+__device__ __forceinline__ int halves_min(int v) {
+    const uint2 h = wave_halves((uint32_t)v);
+    return min((int)h.x, (int)h.y);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

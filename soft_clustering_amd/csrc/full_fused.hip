@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
                         q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
                     }
                 float q = q0 + q1;
-                q += __shfl_xor(q, 32);
+                q = halves_sum(q);
                 if (lane < 32) g_s[k][32 * st + lane] = cvk - hqk * q;
             }
         }

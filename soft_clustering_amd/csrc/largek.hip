@@ -358,7 +358,13 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
     constexpr int kPairs = 4 * IPT;       // staging steps: two columns of one item each
     uint32_t hy[4], hq[4];                // packed y' and y'^2 of the current item
     float ss = 0.0f;                      // isotropic: partial |y|^2 of the current item
-    float2 dq[8];                         // this thread's 8 (centre, scale) pairs, read once per tile
+    // this thread's 8 (centre, scale) pairs: read once per kernel and kept in
+    // registers where the registers allow (otherwise once per tile).  Read
+    // per tile, the compiler places the reads where the staging uses them,
+    // after the operand reads issued ahead, and each wait for them drains
+    // that queue.
+    constexpr bool kDqReg = !kTight && !(want_arg && !kIso && DP == 128);
+    float2 dq[8];
     auto dsc_fetch = [&]() {
 #pragma unroll
         for (int e = 0; e < 8; ++e) dq[e] = dsc_l[e * Sh::kCB + cbk];
@@ -460,267 +466,329 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int64_t t = t0; t < t1; ++t) {
-        const int cur = (int)((t - t0) % NYB), nxt = cur + 1 == NYB ? 0 : cur + 1;
-        const int par = (int)((t - t0) & 1);
-        const uint16_t* yb = ybuf[cur];
+    // per-block values of the tile whose softmax is being formed
+    float mcb[CB], zcb[CB];                 // per block: max (acc units), sum of exp2(F (acc - max))
+    int acb[CB];                            // per block: lowest component at the max
+    half2v eh[MODE == LK_FUSED_EM ? CB : 1][8];   // fused E+M: exp2(F (acc - max)), fp16 pairs
+
+    // ---- scores of tile t from the LDS tile yb (acc units; S = F acc), one
+    // 32-component block at a time: lane (pn, hf), register r of block cb
+    // holds point pn and component kbase + 32 cb + 8 (r / 4) + 4 hf + r % 4;
+    // tile t + 1 is staged into buffer nxt between the MFMAs and the loads of
+    // tile t + 2 are issued after them
+    auto score_tile = [&](int64_t t, const uint16_t* yb, int nxt, f32x16 (&scb)[CB]) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) scb[cb][r] = 0.0f;
+        // operands read kPF steps ahead of their MFMAs: the tile (B, K = inner)
+        // and the LDS-resident panel steps (A)
+        constexpr int kPF = kTight ? 2 : 4;
+        constexpr auto in_lds = [](int ks) { return ks < KL || ks == KS - 1; };
+        half8 yq[KS];
+        half8 pq[CB][KS];
+        auto issue = [&](int ks) {
+            yq[ks] = *reinterpret_cast<const half8*>(yb + Sh::ych(pn, 2 * ks + hf));
+            if (in_lds(ks))
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    pq[cb][ks] = __builtin_bit_cast(half8, plds[w][cb][ks < KL ? ks : KL][lane]);
+        };
+        if constexpr (!kDqReg) dsc_fetch();
+#pragma unroll
+        for (int ks = 0; ks < kPF && ks < KS; ++ks) issue(ks);
+        // step ks: the MFMAs of step ks, then one staging step of the next tile
+        // (the other buffer) while they run; the order is pinned per step
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + kPF < KS) issue(ks + kPF);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const half8 pa = in_lds(ks) ? pq[cb][ks] : pnl[cb][in_lds(ks) ? 0 : ks - KL];
+                scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
+            }
+            if (ks < kPairs) stage_pair(nxt, ks);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int sp = KS; sp < kPairs; ++sp) stage_pair(nxt, sp);
+        // the loads of the tile after next
+        load_tile(t + 2 < t1 ? t + 2 : t1 - 1);
+    };
+    // ---- per block: the softmax values (modes that exchange), the slice's
+    // base-2 scores (top-m) or gamma = exp2(S - lse) into LDS (sweep 2)
+    auto block_phase = [&](f32x16 (&scb)[CB], uint16_t* gw, float lse_cur) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        f32x16& sc = scb[cb];
+        if constexpr (kExchange) {
+            float m = sc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
+            m = halves_max(m);
+            const float nmf = m == -INFINITY ? 0.0f : -F * m;
+            float z = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = fast_exp2(fmaf(sc[r], F, nmf));
+                if constexpr (MODE == LK_FUSED_EM) {
+                    if (r & 1) eh[cb][r >> 1] = half2v{(_Float16)sc[r - 1], (_Float16)e};
+                    else sc[r] = e;
+                }
+                z += e;
+            }
+            mcb[cb] = m;
+            zcb[cb] = halves_sum(z);
+            acb[cb] = 0x7FFFFFFF;
+            if constexpr (!kStats) {
+                if (want_arg) {
+                    int bi = 0x7FFFFFFF;
+#pragma unroll
+                    for (int r = 15; r >= 0; --r)
+                        if (sc[r] == m) bi = kbase + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    acb[cb] = halves_min(bi);
+                }
+            }
+        } else if constexpr (kTopm) {
+            // base-2 scores of the slice's components -> LDS [point][component]
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                stile[pn][w * KW + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)] = F * sc[r];
+        } else {
+            // sweep 2: gamma = exp2(S - lse) (lse = +inf beyond N) -> LDS [point][component]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float gv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gv[e] = fast_exp2(fmaf(sc[4 * q + e], F, -lse_cur));
+                *reinterpret_cast<uint2*>(gw + gch<KW>(pn, 8 * cb + 2 * q + hf)) =
+                    make_uint2(pack_h2(gv[0], gv[1]), pack_h2(gv[2], gv[3]));
+            }
+        }
+    }
+    };
+    // ---- this wave's (max, sum) per point into exchange buffer par
+    auto wave_part = [&](int par) {
+        float2(*wpart)[kT] = wpart_b[kOneBarrier ? par : 0];
+        int(*warg)[kT] = warg_b[kOneBarrier ? par : 0];
+        // this wave's (max, sum) per point, base-2 score units
+        float m = mcb[0];
+#pragma unroll
+        for (int cb = 1; cb < CB; ++cb) m = fmaxf(m, mcb[cb]);
+        const float Fm = m == -INFINITY ? -INFINITY : F * m;
+        float z = 0.0f;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int cb = CB - 1; cb >= 0; --cb) {
+            if (mcb[cb] != -INFINITY) z = fmaf(zcb[cb], fast_exp2(F * (mcb[cb] - m)), z);
+            if (mcb[cb] == m) bi = acb[cb];
+        }
+        if (hf == 0) {
+            wpart[w][pn] = make_float2(Fm, z);
+            if (want_arg) warg[w][pn] = bi;
+        }
+    };
+    // ---- after the exchange barrier: the LSE (and argmax) over the slice of
+    // the points of tile t from exchange buffer par, and what the mode writes
+    // (lanes of the lower half of wave `owner` write the per-point values)
+    auto combine = [&](int64_t t, int par, uint16_t* gw, bool owner) {
+        float2(*wpart)[kT] = wpart_b[kOneBarrier ? par : 0];
+        int(*warg)[kT] = warg_b[kOneBarrier ? par : 0];
         const int64_t prow = t * kT;
         const bool pvalid = prow + pn < n;
-        float lse_cur = 0.0f;
-        if constexpr (MODE == LK_SWEEP2) {
-            lse_cur = lse_nx;
-            lse_nx = load_lse(t + 1 < t1 ? t + 1 : t);
+        // the waves of this wave's slice: w0 .. w0 + WV - 1
+        float M = wpart[w0][pn].x;
+#pragma unroll
+        for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w0 + w2][pn].x);
+        const float Ms = M == -INFINITY ? 0.0f : M;
+        float Z = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < WV; ++w2) {
+            const float2 mz = wpart[w0 + w2][pn];
+            Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
         }
-
-        // ---- scores (acc units; S = F acc), one 32-component block at a time:
-        // lane (pn, hf), register r of block cb holds point pn and component
-        // kbase + 32 cb + 8 (r / 4) + 4 hf + r % 4
-        uint16_t* gw = gbuf[kStats ? w : 0];
-        float mcb[CB], zcb[CB];                 // per block: max (acc units), sum of exp2(F (acc - max))
-        int acb[CB];                            // per block: lowest component at the max
-        half2v eh[MODE == LK_FUSED_EM ? CB : 1][8];   // fused E+M: exp2(F (acc - max)), fp16 pairs
-        f32x16 scb[CB];
-        {
+        float lse = Ms + fast_log2(Z);
+        int arg = 0;
+        if (want_arg) {
+            arg = 0x7FFFFFFF;
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) scb[cb][r] = 0.0f;
-            // operands read kPF steps ahead of their MFMAs: the tile (B, K = inner)
-            // and the LDS-resident panel steps (A)
-            constexpr int kPF = kTight ? 2 : 4;
-            constexpr auto in_lds = [](int ks) { return ks < KL || ks == KS - 1; };
-            half8 yq[KS];
-            half8 pq[CB][KS];
-            auto issue = [&](int ks) {
-                yq[ks] = *reinterpret_cast<const half8*>(yb + Sh::ych(pn, 2 * ks + hf));
-                if (in_lds(ks))
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-                        pq[cb][ks] = __builtin_bit_cast(half8, plds[w][cb][ks < KL ? ks : KL][lane]);
-            };
-            dsc_fetch();
-#pragma unroll
-            for (int ks = 0; ks < kPF && ks < KS; ++ks) issue(ks);
-            // step ks: the MFMAs of step ks, then one staging step of the next tile
-            // (the other buffer) while they run; the order is pinned per step
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ks + kPF < KS) issue(ks + kPF);
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const half8 pa = in_lds(ks) ? pq[cb][ks] : pnl[cb][in_lds(ks) ? 0 : ks - KL];
-                    scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
-                }
-                if (ks < kPairs) stage_pair(nxt, ks);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int sp = KS; sp < kPairs; ++sp) stage_pair(nxt, sp);
-            // the loads of the tile after next
-            load_tile(t + 2 < t1 ? t + 2 : t1 - 1);
+            for (int w2 = WV - 1; w2 >= 0; --w2)
+                if (wpart[w0 + w2][pn].x == M) arg = warg[w0 + w2][pn];
         }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            f32x16& sc = scb[cb];
-            if constexpr (kExchange) {
-                float m = sc[0];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
-                m = fmaxf(m, __shfl_xor(m, 32, 64));
-                const float nmf = m == -INFINITY ? 0.0f : -F * m;
-                float z = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(fmaf(sc[r], F, nmf));
-                    if constexpr (MODE == LK_FUSED_EM) {
-                        if (r & 1) eh[cb][r >> 1] = half2v{(_Float16)sc[r - 1], (_Float16)e};
-                        else sc[r] = e;
-                    }
-                    z += e;
-                }
-                mcb[cb] = m;
-                zcb[cb] = z + __shfl_xor(z, 32, 64);
-                acb[cb] = 0x7FFFFFFF;
-                if constexpr (!kStats) {
+        const int64_t p = prow + pn;
+        if constexpr (MODE == LK_FUSED_EM || MODE == LK_FUSED_E) {
+            if (nxc > 0 && pvalid) {   // merge the exactly scored components
+                const float xl = a.xlse[p];
+                const float m2 = fmaxf(lse, xl);
+                if (m2 != -INFINITY) lse = m2 + fast_log2(fast_exp2(lse - m2) + fast_exp2(xl - m2));
+                if constexpr (MODE == LK_FUSED_E) {
                     if (want_arg) {
-                        int bi = 0x7FFFFFFF;
-#pragma unroll
-                        for (int r = 15; r >= 0; --r)
-                            if (sc[r] == m) bi = kbase + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        acb[cb] = min(bi, __shfl_xor(bi, 32, 64));
+                        const float xm = a.xmax[p];
+                        const int xa = a.xarg[p];
+                        if (xm > M || (xm == M && xa < arg)) arg = xa;
                     }
+                } else if (owner && hf == 0) {
+                    a.lse_out[p] = lse;   // their statistics pass reads it
                 }
-            } else if constexpr (kTopm) {
-                // base-2 scores of the slice's components -> LDS [point][component]
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stile[pn][w * KW + 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)] = F * sc[r];
+            }
+        }
+        if (owner && hf == 0 && pvalid) {
+            if constexpr (MODE == LK_SWEEP1) {
+                a.part_lse[(int64_t)slice * n + p] = lse;
+                if (want_arg) {
+                    a.part_arg[(int64_t)slice * n + p] = arg;
+                    a.part_max[(int64_t)slice * n + p] = M;
+                }
             } else {
-                // sweep 2: gamma = exp2(S - lse) (lse = +inf beyond N) -> LDS [point][component]
+                ll2 += (double)lse;
+                if constexpr (MODE == LK_FUSED_E) {
+                    if (a.out_lse) a.out_lse[p] = lse * kLn2f;
+                    if (want_arg) a.out_arg[p] = arg;
+                }
+            }
+        }
+        if constexpr (MODE == LK_FUSED_EM) {
+            // gamma = exp2(F (acc - m_cb)) exp2(F m_cb - lse), zero beyond N -> LDS
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const float f = (pvalid && mcb[cb] != -INFINITY) ? fast_exp2(F * mcb[cb] - lse) : 0.0f;
+                const half2v f2 = {(_Float16)f, (_Float16)f};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    float gv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) gv[e] = fast_exp2(fmaf(sc[4 * q + e], F, -lse_cur));
+                    const half2v g0 = eh[cb][2 * q] * f2, g1 = eh[cb][2 * q + 1] * f2;
                     *reinterpret_cast<uint2*>(gw + gch<KW>(pn, 8 * cb + 2 * q + hf)) =
-                        make_uint2(pack_h2(gv[0], gv[1]), pack_h2(gv[2], gv[3]));
+                        make_uint2(__builtin_bit_cast(uint32_t, g0), __builtin_bit_cast(uint32_t, g1));
                 }
             }
         }
+    };
 
-        if constexpr (kExchange) {
-            float2(*wpart)[kT] = wpart_b[kOneBarrier ? par : 0];
-            int(*warg)[kT] = warg_b[kOneBarrier ? par : 0];
-            // this wave's (max, sum) per point, base-2 score units
-            float m = mcb[0];
-#pragma unroll
-            for (int cb = 1; cb < CB; ++cb) m = fmaxf(m, mcb[cb]);
-            const float Fm = m == -INFINITY ? -INFINITY : F * m;
-            float z = 0.0f;
-            int bi = 0x7FFFFFFF;
-#pragma unroll
-            for (int cb = CB - 1; cb >= 0; --cb) {
-                if (mcb[cb] != -INFINITY) z = fmaf(zcb[cb], fast_exp2(F * (mcb[cb] - m)), z);
-                if (mcb[cb] == m) bi = acb[cb];
-            }
-            if (hf == 0) {
-                wpart[w][pn] = make_float2(Fm, z);
-                if (want_arg) warg[w][pn] = bi;
+    if constexpr (SPW == 2 && !want_arg) {
+        // Two slices per workgroup, one wave of each on every SIMD: the
+        // second slice's waves run half a tile behind the first's.  Between
+        // two barriers the first slice scores tile t and forms its softmax;
+        // the second forms the softmax of tile t - 1 (its scores kept in
+        // registers across the barrier) and then scores tile t.  Each slice
+        // combines the exchange of its previous tile after the barrier.  On
+        // a 2e8 x 128 x 1024 step this measured about 1% faster than both
+        // slices in step.  (Not in the argmax variants, whose registers it
+        // would overflow at D = 128.)
+        const bool lag = w >= WV;
+        f32x16 scb[CB];
+        for (int64_t t = t0; t < t1; ++t) {
+            const int cur = (int)((t - t0) & 1), par = cur;
+            if (t > t0 && (!lag || t - 1 > t0)) combine(lag ? t - 2 : t - 1, par ^ 1, nullptr, wl == 0);
+            if (!lag) {
+                score_tile(t, ybuf[cur], cur ^ 1, scb);
+                block_phase(scb, nullptr, 0.0f);
+                wave_part(par);
+            } else {
+                if (t > t0) {
+                    block_phase(scb, nullptr, 0.0f);
+                    wave_part(par);
+                }
+                score_tile(t, ybuf[cur], cur ^ 1, scb);
             }
             __syncthreads();
-            // the waves of this wave's slice: w0 .. w0 + WV - 1
-            float M = wpart[w0][pn].x;
-#pragma unroll
-            for (int w2 = 1; w2 < WV; ++w2) M = fmaxf(M, wpart[w0 + w2][pn].x);
-            const float Ms = M == -INFINITY ? 0.0f : M;
-            float Z = 0.0f;
-#pragma unroll
-            for (int w2 = 0; w2 < WV; ++w2) {
-                const float2 mz = wpart[w0 + w2][pn];
-                Z = fmaf(mz.y, fast_exp2(mz.x - Ms), Z);
+        }
+        if (t0 < t1) {
+            const int par = (int)((t1 - t0) & 1);
+            if (!lag || t1 - 1 > t0) combine(lag ? t1 - 2 : t1 - 1, par ^ 1, nullptr, wl == 0);
+            if (lag) {
+                block_phase(scb, nullptr, 0.0f);
+                wave_part(par);
             }
-            float lse = Ms + fast_log2(Z);
-            int arg = 0;
-            if (want_arg) {
-                arg = 0x7FFFFFFF;
-#pragma unroll
-                for (int w2 = WV - 1; w2 >= 0; --w2)
-                    if (wpart[w0 + w2][pn].x == M) arg = warg[w0 + w2][pn];
+            __syncthreads();
+            if (lag) combine(t1 - 1, par, nullptr, wl == 0);
+        }
+    } else {
+        for (int64_t t = t0; t < t1; ++t) {
+            const int cur = (int)((t - t0) % NYB), nxt = cur + 1 == NYB ? 0 : cur + 1;
+            const int par = (int)((t - t0) & 1);
+            const uint16_t* yb = ybuf[cur];
+            const int64_t prow = t * kT;
+            float lse_cur = 0.0f;
+            if constexpr (MODE == LK_SWEEP2) {
+                lse_cur = lse_nx;
+                lse_nx = load_lse(t + 1 < t1 ? t + 1 : t);
             }
-            const int64_t p = prow + pn;
-            if constexpr (MODE == LK_FUSED_EM || MODE == LK_FUSED_E) {
-                if (nxc > 0 && pvalid) {   // merge the exactly scored components
-                    const float xl = a.xlse[p];
-                    const float m2 = fmaxf(lse, xl);
-                    if (m2 != -INFINITY) lse = m2 + fast_log2(fast_exp2(lse - m2) + fast_exp2(xl - m2));
-                    if constexpr (MODE == LK_FUSED_E) {
-                        if (want_arg) {
-                            const float xm = a.xmax[p];
-                            const int xa = a.xarg[p];
-                            if (xm > M || (xm == M && xa < arg)) arg = xa;
-                        }
-                    } else if (wl == 0 && hf == 0) {
-                        a.lse_out[p] = lse;   // their statistics pass reads it
-                    }
+            uint16_t* gw = gbuf[kStats ? w : 0];
+            f32x16 scb[CB];
+            score_tile(t, yb, nxt, scb);
+            block_phase(scb, gw, lse_cur);
+            if constexpr (kExchange) {
+                wave_part(par);
+                __syncthreads();
+                combine(t, par, gw, wl == 0);
+            }
+
+            if constexpr (kTopm) {
+                __syncthreads();   // the tile's scores are in stile
+                topm_tile(prow);
+            }
+
+            // ---- statistics MFMAs from the responsibility tile (wave-private)
+            if constexpr (kStats) {
+                // A operands: gamma^T (row = component, K = 16 points per step);
+                // B operands: the tile of X (K = points, column = feature), read
+                // two feature blocks ahead of their MFMAs
+                constexpr int kSteps = 2 * NFB;                 // (kp, fb)
+                constexpr int kPFB = kTight ? 1 : 2;
+                half8 bzq[kSteps];
+                half8 ag[2][CB];
+                // transposed reads: lane i of 16-lane group q takes row 16 kp + 8 (q / 2) + i / 4 (+ 4)
+                const int trow = 8 * (gq >> 1) + (gi >> 2);
+                auto bz_read = [&](int i) {
+                    const int kp = i / NFB, fb = i % NFB;
+                    const int r = 16 * kp + trow, c = 4 * fb + 2 * (gq & 1) + ((gi & 3) >> 1), o = 4 * (gi & 1);
+                    const uint2 lo = tr16(yb + Sh::ych(r, c) + o), hi = tr16(yb + Sh::ych(r + 4, c) + o);
+                    return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                };
+                auto g_read = [&](int r, int u) {
+                    const uint2 lo = tr16(gw + gch<KW>(r, u)), hi = tr16(gw + gch<KW>(r + 4, u));
+                    return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                };
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        ag[kp][cb] = g_read(16 * kp + trow, 8 * cb + 4 * (gq & 1) + (gi & 3));
+#pragma unroll
+                for (int i = 0; i < kPFB; ++i) bzq[i] = bz_read(i);
+#pragma unroll
+                for (int i = 0; i < kSteps; ++i) {
+                    if (i + kPFB < kSteps) bzq[i + kPFB] = bz_read(i + kPFB);
+                    const int kp = i / NFB, fb = i % NFB;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[cb][fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag[kp][cb], bzq[i], acc[cb][fb], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (2 * CB + kPFB), 1);
+#pragma unroll
+                for (int i = 0; i < kSteps; ++i) {
+                    if (i + kPFB < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x008, CB, 1);
+                }
+                // s0 (and iso sum gamma |y|^2): 16 components x 32 points against [1, yh]
+                half8 bx;
+                {
+                    const uint4 hv = *reinterpret_cast<const uint4*>(&yh_t[cur][8 * gq]);
+                    const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+                    const uint4 z4 = make_uint4(0, 0, 0, 0);
+                    bx = __builtin_bit_cast(half8, gi == 0 ? ones : ((kIso && gi == 1) ? hv : z4));
+                }
+#pragma unroll
+                for (int b = 0; b < KW / 16; ++b) {
+                    const half8 ax = g_read(8 * gq + (gi >> 2), 4 * b + (gi & 3));
+                    aux[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bx, aux[b], 0, 0, 0);
                 }
             }
-            if (wl == 0 && hf == 0 && pvalid) {
-                if constexpr (MODE == LK_SWEEP1) {
-                    a.part_lse[(int64_t)slice * n + p] = lse;
-                    if (want_arg) {
-                        a.part_arg[(int64_t)slice * n + p] = arg;
-                        a.part_max[(int64_t)slice * n + p] = M;
-                    }
-                } else {
-                    ll2 += (double)lse;
-                    if constexpr (MODE == LK_FUSED_E) {
-                        if (a.out_lse) a.out_lse[p] = lse * kLn2f;
-                        if (want_arg) a.out_arg[p] = arg;
-                    }
-                }
-            }
-            if constexpr (MODE == LK_FUSED_EM) {
-                // gamma = exp2(F (acc - m_cb)) exp2(F m_cb - lse), zero beyond N -> LDS
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const float f = (pvalid && mcb[cb] != -INFINITY) ? fast_exp2(F * mcb[cb] - lse) : 0.0f;
-                    const half2v f2 = {(_Float16)f, (_Float16)f};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const half2v g0 = eh[cb][2 * q] * f2, g1 = eh[cb][2 * q + 1] * f2;
-                        *reinterpret_cast<uint2*>(gw + gch<KW>(pn, 8 * cb + 2 * q + hf)) =
-                            make_uint2(__builtin_bit_cast(uint32_t, g0), __builtin_bit_cast(uint32_t, g1));
-                    }
-                }
-            }
-        }
 
-        if constexpr (kTopm) {
-            __syncthreads();   // the tile's scores are in stile
-            topm_tile(prow);
+            // one-barrier modes: the next tile was staged by every wave before the
+            // exchange barrier, and the tile staged during the next one is not
+            // this one (three buffers when the statistics read this tile after it)
+            if constexpr (!kOneBarrier) __syncthreads();
         }
-
-        // ---- statistics MFMAs from the responsibility tile (wave-private)
-        if constexpr (kStats) {
-            // A operands: gamma^T (row = component, K = 16 points per step);
-            // B operands: the tile of X (K = points, column = feature), read
-            // two feature blocks ahead of their MFMAs
-            constexpr int kSteps = 2 * NFB;                 // (kp, fb)
-            constexpr int kPFB = kTight ? 1 : 2;
-            half8 bzq[kSteps];
-            half8 ag[2][CB];
-            // transposed reads: lane i of 16-lane group q takes row 16 kp + 8 (q / 2) + i / 4 (+ 4)
-            const int trow = 8 * (gq >> 1) + (gi >> 2);
-            auto bz_read = [&](int i) {
-                const int kp = i / NFB, fb = i % NFB;
-                const int r = 16 * kp + trow, c = 4 * fb + 2 * (gq & 1) + ((gi & 3) >> 1), o = 4 * (gi & 1);
-                const uint2 lo = tr16(yb + Sh::ych(r, c) + o), hi = tr16(yb + Sh::ych(r + 4, c) + o);
-                return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            };
-            auto g_read = [&](int r, int u) {
-                const uint2 lo = tr16(gw + gch<KW>(r, u)), hi = tr16(gw + gch<KW>(r + 4, u));
-                return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            };
-#pragma unroll
-            for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    ag[kp][cb] = g_read(16 * kp + trow, 8 * cb + 4 * (gq & 1) + (gi & 3));
-#pragma unroll
-            for (int i = 0; i < kPFB; ++i) bzq[i] = bz_read(i);
-#pragma unroll
-            for (int i = 0; i < kSteps; ++i) {
-                if (i + kPFB < kSteps) bzq[i + kPFB] = bz_read(i + kPFB);
-                const int kp = i / NFB, fb = i % NFB;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    acc[cb][fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag[kp][cb], bzq[i], acc[cb][fb], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (2 * CB + kPFB), 1);
-#pragma unroll
-            for (int i = 0; i < kSteps; ++i) {
-                if (i + kPFB < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-                __builtin_amdgcn_sched_group_barrier(0x008, CB, 1);
-            }
-            // s0 (and iso sum gamma |y|^2): 16 components x 32 points against [1, yh]
-            half8 bx;
-            {
-                const uint4 hv = *reinterpret_cast<const uint4*>(&yh_t[cur][8 * gq]);
-                const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-                const uint4 z4 = make_uint4(0, 0, 0, 0);
-                bx = __builtin_bit_cast(half8, gi == 0 ? ones : ((kIso && gi == 1) ? hv : z4));
-            }
-#pragma unroll
-            for (int b = 0; b < KW / 16; ++b) {
-                const half8 ax = g_read(8 * gq + (gi >> 2), 4 * b + (gi & 3));
-                aux[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bx, aux[b], 0, 0, 0);
-            }
-        }
-
-        // one-barrier modes: the next tile was staged by every wave before the
-        // exchange barrier, and the tile staged during the next one is not
-        // this one (three buffers when the statistics read this tile after it)
-        if constexpr (!kOneBarrier) __syncthreads();
     }
 
     // ---- epilogue: per-workgroup partials, one writer per value
