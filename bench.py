@@ -57,16 +57,16 @@ DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="67f222d03e530a20", fetch_kib=125176.3, write_kib=4144.3,
+        sources="13892434a1997e62", fetch_kib=125176.5, write_kib=4144.3,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="afe3c24832354895", fetch_kib=1251546.1, write_kib=76547.9,
-        copy_bytes=2.56e+09, copy_fetch_kib=1250035.9375, copy_write_kib=2500000.0),
+        sources="53cb83c8cf4ec040", fetch_kib=1251543.2, write_kib=78581.5,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250037.0, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="afe3c24832354895", fetch_kib=69332261.9, write_kib=7377041.8,
-        copy_bytes=5.12e+10, copy_fetch_kib=25000259.75, copy_write_kib=50000000.0),
+        sources="53cb83c8cf4ec040", fetch_kib=53696969.6, write_kib=7378128.0,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000259.875, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="03e19ff49c43ca07", fetch_kib=63930.7, write_kib=35527.9,
+        sources="fed76dcfa986ffb6", fetch_kib=63930.5, write_kib=35529.8,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
