@@ -96,6 +96,34 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// MFMAs with their accumulators in VGPRs, for the statistics kernels that run
+// one wave per SIMD.  There the compiler gives every MFMA an AGPR accumulator,
+// and the scores (32 registers) and s0 (16) then share the 256 AGPRs with the
+// 256 statistics accumulators: it copies scores out for the softmax and swaps
+// statistics in and out around their MFMAs, 128 register moves per tile.  In
+// inline asm the accumulator is a VGPR operand.  The compiler does not see the
+// MFMA inside the asm, so the wait states it would insert are written out: a
+// few before each (a VALU write of an operand just before an MFMA needs them)
+// and `mfma_v_settle` (24) after the last one, before any other instruction
+// touches the results (a 32x32x16 result needs 11 before a VALU reads it).
+// The "+v" operands of the settle make every later use depend on it.
+// (first: the accumulator starts at zero; a constant once the loop unrolls)
+__device__ __forceinline__ void mfma32_v(f32x16& d, const half8& a, const half8& b, bool first) {
+    if (first)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    else
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_v(f32x4& d, const half8& a, const half8& b) {
+    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_settle(f32x16& x, f32x16& y) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void mfma_v_settle(f32x4& x, f32x4& y, f32x4& z, f32x4& u) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y), "+v"(z), "+v"(u));
+}
+
 template <bool BF16>
 __device__ __forceinline__ float h16_to_f32(uint32_t bits16) {
     if constexpr (BF16) return __uint_as_float(bits16 << 16);
@@ -154,6 +182,8 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
     constexpr bool kTight = kStats && !kIso && DP == 128;
     constexpr int KL = kTight ? DP / 16 : 0;   // panel steps [0, KL) and the bias step in LDS
     constexpr int KR = KS - 1 - KL;            // panel steps in registers: [KL, KS - 1)
+    // one wave per SIMD there: scores and s0 accumulate in VGPRs (mfma32_v)
+    constexpr bool kAsmAcc = kTight;
 
     // tiles of X in LDS: double buffered; the fused E+M mode keeps three, so
     // that the tile being staged is never one a slower wave still reads for
@@ -505,13 +535,18 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const half8 pa = in_lds(ks) ? pq[cb][ks] : pnl[cb][in_lds(ks) ? 0 : ks - KL];
-                scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
+                if constexpr (kAsmAcc) mfma32_v(scb[cb], pa, yq[ks], ks == 0);
+                else scb[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, yq[ks], scb[cb], 0, 0, 0);
             }
             if (ks < kPairs) stage_pair(nxt, ks);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int sp = KS; sp < kPairs; ++sp) stage_pair(nxt, sp);
+        if constexpr (kAsmAcc) {
+            static_assert(CB == 2, "settle both score blocks");
+            mfma_v_settle(scb[0], scb[1]);
+        }
         // the loads of the tile after next
         load_tile(t + 2 < t1 ? t + 2 : t1 - 1);
     };
@@ -780,7 +815,8 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
 #pragma unroll
                 for (int b = 0; b < KW / 16; ++b) {
                     const half8 ax = g_read(8 * gq + (gi >> 2), 4 * b + (gi & 3));
-                    aux[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bx, aux[b], 0, 0, 0);
+                    if constexpr (kAsmAcc) mfma16_v(aux[b], ax, bx);
+                    else aux[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bx, aux[b], 0, 0, 0);
                 }
             }
 
@@ -791,6 +827,10 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
         }
     }
 
+    if constexpr (kAsmAcc) {
+        static_assert(KW / 16 == 4, "settle the s0 accumulators");
+        mfma_v_settle(aux[0], aux[1], aux[2], aux[3]);
+    }
     // ---- epilogue: per-workgroup partials, one writer per value
     if constexpr (!kIso) rng = fmaxf((float)rq[0], (float)rq[1]);
     const int flag = __syncthreads_or(rng > kF16Max ? 1 : 0);
