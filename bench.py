@@ -60,11 +60,11 @@ TRAFFIC = {
         sources="13892434a1997e62", fetch_kib=125176.5, write_kib=4144.3,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="53cb83c8cf4ec040", fetch_kib=1251543.2, write_kib=78581.5,
-        copy_bytes=2.56e+09, copy_fetch_kib=1250037.0, copy_write_kib=2500000.0),
+        sources="3a13e1f2e8ef07d1", fetch_kib=1251543.4, write_kib=78178.5,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250035.6875, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="53cb83c8cf4ec040", fetch_kib=53696969.6, write_kib=7378128.0,
-        copy_bytes=5.12e+10, copy_fetch_kib=25000259.875, copy_write_kib=50000000.0),
+        sources="3a13e1f2e8ef07d1", fetch_kib=53724488.1, write_kib=7429791.0,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000257.9375, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
         sources="fed76dcfa986ffb6", fetch_kib=63930.5, write_kib=35529.8,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
