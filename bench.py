@@ -66,7 +66,7 @@ TRAFFIC = {
         sources="3a13e1f2e8ef07d1", fetch_kib=53724488.1, write_kib=7429791.0,
         copy_bytes=5.12e+10, copy_fetch_kib=25000257.9375, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="fed76dcfa986ffb6", fetch_kib=63930.5, write_kib=35529.8,
+        sources="2484ae2e4834f396", fetch_kib=65749.8, write_kib=39105.4,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")

@@ -502,40 +502,74 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
                         wp[vv] = __builtin_bit_cast(half8, wpk[((int64_t)k * NV + vv) * 64 + lane]);
                     }
                     const float cvk = cv_s[k], hqk = hq_s[k];
-#pragma unroll 2
-                    for (int st = 0; st < T / 32; ++st) {
-                        __asm__ volatile("" ::: "memory");   // -W mu re-read per block
-                        f32x16 acc[NOB];
+                    // Point blocks st = 0 .. 7 of 32 points, software-pipelined.  Per
+                    // block the 4 MFMAs of output block 0 (inputs 0..31) come first,
+                    // then the 8 of output block 1; the squares of output block 0
+                    // are summed between the MFMAs of output block 1 and those of
+                    // output block 1 between the first 4 MFMAs of the next point
+                    // block, so the matrix core is not idle while the wave forms
+                    // |z|^2.  Each group of FMAs is pinned to its MFMA step: its
+                    // operands pass through an empty asm statement there (the
+                    // compiler would otherwise place them all after the MFMAs) and
+                    // the step ends in a scheduling barrier.
+                    f32x16 a0, a1, p1;   // output blocks 0 and 1 of this point block, 1 of the last
+                    float q[2][4];       // partial |z|^2 of the last / this point block
+                    auto sq = [&](const f32x16& acc, float (&qq)[4], int r0, int r1) __attribute__((always_inline)) {
 #pragma unroll
-                        for (int ob = 0; ob < NOB; ++ob)
-                            acc[ob] = *reinterpret_cast<const f32x16*>(&wb_s[k][ob][lane >> 5][0]);
-                        const int row = 32 * st + (lane & 31);
-#pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) {
-                            const half8 xb = __builtin_bit_cast(
-                                half8, *reinterpret_cast<const uint4*>(&xt[xoff(row, 2 * ks + (lane >> 5))]));
-#pragma unroll
-                            for (int ob = 0; ob < NOB; ++ob) {
-                                if (ks > 2 * ob + 1) continue;
-                                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wp[ob * NKS + ks], xb, acc[ob], 0, 0, 0);
-                                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wp[(NOB + ob) * NKS + ks], xb, acc[ob], 0, 0, 0);
-                            }
+                        for (int r = r0; r < r1; ++r) {
+                            float e = acc[r];
+                            __asm__ volatile("" : "+v"(e));
+                            qq[r % 4] = fmaf(e, e, qq[r % 4]);
                         }
-                        float q0 = 0.0f, q1 = 0.0f;
-#pragma unroll
-                        for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-                            for (int r = 0; r < 16; r += 2) {
-                                q0 = fmaf(acc[ob][r], acc[ob][r], q0);
-                                q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
-                            }
-                        float q = q0 + q1;
+                    };
+                    auto finish = [&](float (&qq)[4], int st) __attribute__((always_inline)) {
+                        float t = (qq[0] + qq[1]) + (qq[2] + qq[3]);
                         {   // lanes l < 32 add lane l + 32's half (a cross-half swap, no LDS trip)
-                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q),
+                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
                                                                              false, false);
-                            q += __uint_as_float(sw[1]);
+                            t += __uint_as_float(sw[1]);
                         }
-                        if (lane < 32) gs[k][32 * st + lane] = cvk - hqk * q;
+                        if (lane < 32) gs[k][32 * st + lane] = cvk - hqk * t;
+                    };
+#pragma unroll
+                    for (int st = 0; st <= T / 32; ++st) {
+                        float (&qc)[4] = q[st & 1];
+                        float (&qp)[4] = q[(st & 1) ^ 1];
+                        if (st == T / 32) {   // drain: output block 1 of the last point block
+                            sq(p1, qp, 0, 16);
+                            finish(qp, st - 1);
+                            break;
+                        }
+                        qc[0] = qc[1] = qc[2] = qc[3] = 0.0f;
+                        __asm__ volatile("" ::: "memory");   // -W mu re-read per block
+                        a0 = *reinterpret_cast<const f32x16*>(&wb_s[k][0][lane >> 5][0]);
+                        a1 = *reinterpret_cast<const f32x16*>(&wb_s[k][1][lane >> 5][0]);
+                        const int row = 32 * st + (lane & 31);
+                        half8 xb[NKS];
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks)
+                            xb[ks] = __builtin_bit_cast(
+                                half8, *reinterpret_cast<const uint4*>(&xt[xoff(row, 2 * ks + (lane >> 5))]));
+                        // output block 0: inputs 0..31 (2 steps, hi and lo); squares of the
+                        // last point block's output block 1, four per MFMA
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const int ks = m >> 1, hl = m & 1;
+                            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(wp[(hl * NOB + 0) * NKS + ks], xb[ks], a0, 0, 0, 0);
+                            if (st > 0) sq(p1, qp, 4 * m, 4 * m + 4);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        if (st > 0) finish(qp, st - 1);
+                        // output block 1: inputs 0..63 (4 steps, hi and lo); squares of
+                        // output block 0 once its chain has completed (from the third MFMA)
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            const int ks = m >> 1, hl = m & 1;
+                            a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(wp[(hl * NOB + 1) * NKS + ks], xb[ks], a1, 0, 0, 0);
+                            if (m >= 2) sq(a0, qc, (16 * (m - 2)) / 6, (16 * (m - 1)) / 6);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        p1 = a1;
                     }
                 }
             }
