@@ -313,7 +313,11 @@ __global__ __launch_bounds__(lk_threads(MODE_ARG, COV), lk_wg_per_cu(MODE_ARG)) 
         }
     };
     // sweep 2: merged LSE of point pn of tile t (+inf beyond N: gamma = 0)
-    auto load_lse = [&](int64_t t) { const int64_t p = t * kT + pn; return p < n ? a.lse_in[p] : INFINITY; };
+    auto load_lse = [&](int64_t t) {   // clamped index and a select: no branch around the load
+        const int64_t p = t * kT + pn;
+        const float v = a.lse_in[p < n ? p : n - 1];
+        return p < n ? v : INFINITY;
+    };
 
     // Top-m of the tile's points over this slice, merged with the running
     // list of the slices before it (the outputs).  An entry is better when its
