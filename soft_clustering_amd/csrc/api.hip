@@ -146,7 +146,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
     }
     if (p->cov == GMM_COV_FULL && p->xdt == GMM_F16) {
         // full covariance: fp16 X, split fp16 whitening panel, fp16 MFMA whitening and moments
-        if (p->d > 64 || p->k > kFullMaxK) return GMM_E_UNSUPPORTED;
+        if (p->d > 128 || p->k > kFullMaxK) return GMM_E_UNSUPPORTED;
         int dp = pad_dim(p->d);
         const int64_t tiles = (p->n + kFullT - 1) / kFullT;
         const int G = full_groups(p->k);          // groups of 16 components
@@ -162,7 +162,7 @@ gmm_status make_plan(const gmm_desc* desc, Plan* p) {
         p->off_cov = take(sizeof(float) * p->k * p->d * p->d);
         p->off_panel = take(sizeof(uint4) * full_w_vecs(dp) * G);
         p->off_shift = take(sizeof(float) * (kpad * full_dpo(dp) + kpad * dp + 2 * kpad));
-        if (G > 1) {   // per-(group, point) LSE, argmax and maximum
+        if (full_lse_pass(p->k, dp)) {   // per-(group, point) LSE, argmax and maximum
             p->off_lse = take(sizeof(float) * (size_t)G * p->n);
             p->off_arg = take((sizeof(int) + sizeof(float)) * (size_t)G * p->n);
         }

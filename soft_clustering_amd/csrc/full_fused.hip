@@ -741,6 +741,355 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 64 < D <= 128 (padded to 128).  The whitening panel of one component (the
+// 20 lower-triangle 32 x 32 blocks of W, hi and lo: 160 registers per lane)
+// and its lower-triangle second moments (36 blocks of 16 x 16: 144 registers)
+// fill most of the 512 registers a lane has at one wave per SIMD, so a wave
+// holds one component at a time, and the point work of every EM iteration
+// takes the two loops over the components ([LP-GMM] 3.2): an E-step launch per
+// group of 16 writes the group's log-sum-exp per point (merged over the groups
+// afterwards), then one E+M launch per quad of components normalises with the
+// merged LSE and accumulates the statistics (the whitening is done twice).
+//   E-step launch (EM = false): wave w whitens the tile against components
+//   4w..4w+3 of the group in turn, each panel loaded when its turn comes;
+//   every thread then forms its point's log-sum-exp and the other per-point
+//   outputs exactly as k_full_fused does.
+//   E+M launch: components 4 quad .. 4 quad + 3 of the group, one per wave,
+//   the panel loaded once; after the whitening every thread turns the four
+//   scores of its point into responsibilities, then wave w accumulates the
+//   second moments of its component and the first moments of dimension blocks
+//   2w, 2w + 1 of all four.
+namespace wide {
+constexpr int DP = 128, NB = 8, NBLK = 36, NOB = 4, NKS = 8;
+constexpr int NPR = 20;          // lower-triangle (out block, K step) pairs: K step <= 2 ob + 1
+constexpr int kXR = DP + 8;      // halves per row of the row-major tile
+constexpr int kGS = T + 4;
+constexpr int NVL = 2 * NOB * NKS;   // panel vectors per lane and component in memory
+__host__ __device__ constexpr int pair_of(int ob, int ks) { return ob * (ob + 1) + ks; }
+}  // namespace wide
+
+template <bool EM, bool VEC>
+__global__ __launch_bounds__(256, 1) void k_full_wide(
+    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
+    const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
+    const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
+    double* __restrict__ part_ll, const FullPass ps, int64_t tlo, int64_t thi, int seg_first) {
+    using namespace wide;
+    constexpr int KC = EM ? 4 : KP;   // components of this launch
+    const int kq = EM ? 4 * ps.quad : 0;   // the first of them within the group
+    __shared__ __attribute__((aligned(16))) uint32_t nm_s[EM ? 4 : 1][DP];   // (-mu, -mu) fp16 pairs
+    __shared__ __attribute__((aligned(16))) float wb_s[KC][DP];              // -W mu
+    __shared__ float cv_s[KC], hq_s[KC];
+    __shared__ __attribute__((aligned(16))) float g_s[KC][kGS];              // scores, then gamma
+    // the tile, row-major; E+M: two buffers, the next tile's registers are
+    // written out between the whitening and the moments of this one
+    constexpr int NBUF = EM ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t xr_s[NBUF][T][kXR];
+    __shared__ double red[256];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+
+    if constexpr (EM) {
+        for (int i = tid; i < 4 * DP; i += 256) {
+            const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-muh[(kq + i / DP) * DP + i % DP]));
+            nm_s[i / DP][i % DP] = h | (h << 16);
+        }
+    }
+    for (int i = tid; i < KC * DP; i += 256) wb_s[i / DP][i % DP] = -wbias[(kq + i / DP) * DP + i % DP];
+    if (tid < KC) {
+        const float rs = rscale[kq + tid];
+        cv_s[tid] = cvec[kq + tid];
+        hq_s[tid] = kHalfLog2e * rs * rs;   // |z|^2 = 2^-2e |W x - W mu|^2
+    }
+
+    const int G = gridDim.x;
+    const int64_t tiles = thi - tlo;
+    const int64_t tb = tiles / G, tr = tiles % G;
+    const int b = blockIdx.x;
+    const int64_t t0 = tlo + b * tb + (b < tr ? b : tr);
+    const int64_t t1 = t0 + tb + (b < tr ? 1 : 0);
+
+    // dimensions 8c..8c+7 of this thread's point of tile t, zero outside
+    // [0, N) x [0, D); every load from an in-bounds address, masked afterwards
+    auto load_col = [&](int64_t t, int c) __attribute__((always_inline)) {
+        const int64_t p = t * T + tid;
+        const bool valid = p < n;
+        const _Float16* row = x + (valid ? p : 0) * ldx;
+        if constexpr (VEC) {
+            const int cmax = d / 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
+            const uint32_t m = (valid && c < cmax) ? ~0u : 0u;
+            return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+        } else {
+            const uint16_t* rb = reinterpret_cast<const uint16_t*>(row);
+            uint32_t wv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i0 = 8 * c + 2 * q;
+                const uint32_t lo = rb[i0 < d ? i0 : 0], hi = rb[i0 + 1 < d ? i0 + 1 : 0];
+                wv[q] = (valid && i0 < d ? lo : 0u) | ((valid && i0 + 1 < d ? hi : 0u) << 16);
+            }
+            return make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    };
+    auto load_point = [&](int64_t t, uint4 (&xv)[DP / 8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < DP / 8; ++c) xv[c] = load_col(t, c);
+    };
+    // the lower-triangle blocks of component kg's panel (group-local index)
+    auto load_panel = [&](int kg, half8 (&wv)[2][NPR]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int ks = 0; ks <= 2 * ob + 1; ++ks)
+                    wv[hl][pair_of(ob, ks)] = __builtin_bit_cast(
+                        half8, wpk[((int64_t)kg * NVL + (hl * NOB + ob) * NKS + ks) * 64 + lane]);
+    };
+    // base-2 scores of launch component kl for points 32 st .. 32 st + 31 of
+    // the tile into g_s[kl]: lane l holds point l % 32 and out dimensions
+    // 32 ob + 8 (r / 4) + 4 (l / 32) + r % 4; the accumulators start from -W mu
+    auto whiten_step = [&](int kl, const half8 (&wv)[2][NPR], int cur, int st, float cvk,
+                           float hqk) __attribute__((always_inline)) {
+        {
+            f32x16 acc[NOB];
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[ob][r] = wb_s[kl][32 * ob + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const half8 xb = __builtin_bit_cast(
+                    half8, *reinterpret_cast<const uint4*>(&xr_s[cur][32 * st + (lane & 31)][16 * ks + 8 * (lane >> 5)]));
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob) {
+                    if (ks > 2 * ob + 1) continue;   // above the diagonal: W is lower triangular
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[0][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[1][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
+                }
+            }
+            float q0 = 0.0f, q1 = 0.0f;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    q0 = fmaf(acc[ob][r], acc[ob][r], q0);
+                    q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
+                }
+            const float q = halves_sum(q0 + q1);
+            if (lane < 32) g_s[kl][32 * st + lane] = cvk - hqk * q;
+        }
+    };
+
+    float s0acc[EM ? 4 : 1] = {};
+    f32x4 acc2[EM ? NBLK : 1];
+    f32x4 acc1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (EM) {
+#pragma unroll
+        for (int q = 0; q < NBLK; ++q) acc2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    double ll = 0.0;
+
+    half8 wv[2][NPR];
+    uint4 xv[EM ? 1 : DP / 8];   // E-step: the next tile's point, loaded behind this one
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[buf][tid][8 * c]) = xv[c];
+    };
+    if constexpr (EM) {
+        load_panel(kq + w, wv);
+        if (t0 < t1) {
+#pragma unroll
+            for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[0][tid][8 * c]) = load_col(t0, c);
+        }
+    } else {
+        if (t0 < t1) load_point(t0, xv);
+    }
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t p = t * T + tid;
+        const bool valid = p < n;
+        const int cur = EM ? (int)((t - t0) & 1) : 0;
+        __syncthreads();   // the previous tile is done with g_s (and its own buffer)
+        if constexpr (EM) {
+            // the next tile goes to the other buffer (it held tile t - 1) two
+            // 16-byte columns per whitening step, each stored three steps after
+            // its loads were issued: 32 registers in flight instead of 64
+            const bool more = t + 1 < t1;
+            const float cvk = cv_s[w], hqk = hq_s[w];
+            uint4 nx[4][2];
+#pragma unroll
+            for (int st = 0; st < T / 32; ++st) {
+                if (more) {
+                    nx[st % 4][0] = load_col(t + 1, 2 * st);
+                    nx[st % 4][1] = load_col(t + 1, 2 * st + 1);
+                    if (st >= 3) {
+                        const int c = 2 * (st - 3);
+                        *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = nx[(st - 3) % 4][0];
+                        *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = nx[(st - 3) % 4][1];
+                    }
+                }
+                whiten_step(w, wv, cur, st, cvk, hqk);
+            }
+            if (more) {
+#pragma unroll
+                for (int st = T / 32; st < T / 32 + 3; ++st) {
+                    const int c = 2 * (st - 3);
+                    *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = nx[(st - 3) % 4][0];
+                    *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = nx[(st - 3) % 4][1];
+                }
+            }
+        } else {
+            store_tile(0);
+            __syncthreads();
+            if (t + 1 < t1) load_point(t + 1, xv);   // the next tile, behind this one's work
+#pragma unroll 1
+            for (int kk = 0; kk < 4; ++kk) {
+                const int kl = 4 * w + kk;
+                load_panel(kl, wv);
+                const float cvk = cv_s[kl], hqk = hq_s[kl];
+#pragma unroll 1
+                for (int st = 0; st < T / 32; ++st) whiten_step(kl, wv, 0, st, cvk, hqk);
+            }
+        }
+        __syncthreads();
+
+        if constexpr (EM) {
+            // responsibilities from the merged LSE of all groups
+            const float lse2 = valid ? ps.lse_in[p] * kLog2ef : 0.0f;
+            const float lsafe = lse2 == -INFINITY ? INFINITY : lse2;   // no live component
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float gk = valid ? fast_exp2(g_s[k][tid] - lsafe) : 0.0f;
+                s0acc[k] += gk;
+                g_s[k][tid] = gk;
+            }
+        } else {
+            // base-2 log-sum-exp of the group, per-point outputs (as k_full_fused)
+            float sv[KP];
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                sv[k] = g_s[k][tid];
+                M = fmaxf(M, sv[k]);
+            }
+            const float Ms = M == -INFINITY ? 0.0f : M;
+            float Z = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) Z += fast_exp2(sv[k] - Ms);
+            const float own = Ms + fast_log2(Z);
+            const float lse2 = ps.lse_in != nullptr ? (valid ? ps.lse_in[p] * kLog2ef : 0.0f) : own;
+            if (valid) {
+                ll += (double)own;
+                if (ps.out_lse) ps.out_lse[p] = lse2 * kLn2f;
+                if (ps.out_arg) {
+                    int a = 0;
+#pragma unroll
+                    for (int k = KP - 1; k >= 0; --k)
+                        if (sv[k] == M) a = k;
+                    ps.out_arg[p] = KP * ps.group + a;
+                }
+                if (ps.out_max) ps.out_max[p] = M;
+                if (ps.topm > 0) write_topm(sv, lse2, ps, p);
+            }
+        }
+
+        if constexpr (EM) {
+            __syncthreads();
+#pragma unroll 1
+            for (int ks = 0; ks < T / 32; ++ks) {
+                const int pc = 32 * ks + 8 * g;   // this lane's 8 points of the K step
+                // x of points pc..pc+7, dimension 16 bb + j: two transposed reads of the tile
+                uint4 xb[NB];
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) {
+                    const uint16_t* src = &xr_s[cur][32 * ks + 8 * g + (j >> 2)][16 * bb + 4 * (j & 3)];
+                    const uint2 lo = tr16(src), hi = tr16(src + 4 * kXR);
+                    xb[bb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+                {   // s1 += gamma^T x: rows 0..3 the four components, dims 16 bb + j (bb = 2w, 2w + 1)
+                    half8 ga = {};
+                    if (j < 4) {
+                        const float4 g0 = *reinterpret_cast<const float4*>(&g_s[j][pc]);
+                        const float4 g1 = *reinterpret_cast<const float4*>(&g_s[j][pc + 4]);
+                        ga = half8{(_Float16)g0.x, (_Float16)g0.y, (_Float16)g0.z, (_Float16)g0.w,
+                                   (_Float16)g1.x, (_Float16)g1.y, (_Float16)g1.z, (_Float16)g1.w};
+                    }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {   // read again: xb is not indexed by the wave
+                        const uint16_t* src = &xr_s[cur][32 * ks + 8 * g + (j >> 2)][16 * (2 * w + h) + 4 * (j & 3)];
+                        const uint2 lo = tr16(src), hi = tr16(src + 4 * kXR);
+                        acc1[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            ga, __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y)), acc1[h], 0, 0, 0);
+                    }
+                }
+                const float4 g0 = *reinterpret_cast<const float4*>(&g_s[w][pc]);
+                const float4 g1 = *reinterpret_cast<const float4*>(&g_s[w][pc + 4]);
+                const half8 gh = {(_Float16)g0.x, (_Float16)g0.y, (_Float16)g0.z, (_Float16)g0.w,
+                                  (_Float16)g1.x, (_Float16)g1.y, (_Float16)g1.z, (_Float16)g1.w};
+                half8 yc[NB];
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) {
+                    const half2v nm = __builtin_bit_cast(half2v, nm_s[w][16 * bb + j]);
+                    yc[bb] = __builtin_bit_cast(half8, xb[bb]) + __builtin_shufflevector(nm, nm, 0, 1, 0, 1, 0, 1, 0, 1);
+                }
+#pragma unroll
+                for (int ab = 0; ab < NB; ++ab) {
+                    const half8 ya = yc[ab] * gh;   // gamma (x - mu_k)
+#pragma unroll
+                    for (int bb = 0; bb <= ab; ++bb)
+                        acc2[blk_index(ab, bb)] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(ya, yc[bb], acc2[blk_index(ab, bb)], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    __syncthreads();
+    if constexpr (EM) {
+        // rows kq..kq+3 of this workgroup's partial slot [KP][1 + D + D(D+1)/2]
+        const int ncolp = 1 + d + d * (d + 1) / 2;
+        float* dst = part + (int64_t)b * KP * ncolp;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) g_s[k][tid] = s0acc[k];
+        __syncthreads();
+        if (tid < 4) {
+            double s = 0.0;
+            for (int i = 0; i < T; ++i) s += (double)g_s[tid][i];
+            dst[(int64_t)(kq + tid) * ncolp] = (float)s;
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int dd = 16 * (2 * w + h) + j;
+                    if (dd < d) dst[(int64_t)(kq + r) * ncolp + 1 + dd] = acc1[h][r];
+                }
+        }
+#pragma unroll
+        for (int ab = 0; ab < NB; ++ab)
+#pragma unroll
+            for (int bb = 0; bb <= ab; ++bb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ab + 4 * g + r, col = 16 * bb + j;
+                    if (row >= col && row < d)
+                        dst[(int64_t)(kq + w) * ncolp + 1 + d + tri_idx(row, col)] = acc2[blk_index(ab, bb)][r];
+                }
+    } else {
+        red[tid] = ll;
+        __syncthreads();
+        for (int s2 = 128; s2 > 0; s2 >>= 1) {
+            if (tid < s2) red[tid] += red[tid + s2];
+            __syncthreads();
+        }
+        if (tid == 0 && part_ll != nullptr) part_ll[b] = seg_first ? red[0] * kLn2 : part_ll[b] + red[0] * kLn2;
+    }
+}
+
 // Group g's slice of the per-component arrays and partial slots.
 struct FullGroupPtrs {
     const uint4* wpk;
@@ -781,7 +1130,7 @@ hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int
                      const FullPass& ps, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
     const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
     // LL partials only from a group that is the only one (several: the merge sums the LL)
-    double* pll = w.groups == 1 ? w.part_ll : nullptr;
+    double* pll = w.lse_pass ? nullptr : w.part_ll;
     if (DP == 64 && vec) {   // the pipelined kernel
         const FullGroupPtrs q = group_ptrs<64>(p, w, ps.group);
 #define FULL_PIPE(EM_, EXT_)                                                                     \
@@ -798,6 +1147,26 @@ hipError_t launch_dp(const Plan& p, const FullWs& w, const void* x, bool em, int
     }
     return vec ? launch_dv<DP, true>(p, w, x, em, grid, ps, pll, tlo, thi, seg_first, s)
                : launch_dv<DP, false>(p, w, x, em, grid, ps, pll, tlo, thi, seg_first, s);
+}
+
+// D <= 128: E-step launches over a group of 16, E+M launches over quad ps.quad
+// of it (normalised with ps.lse_in, the merged LSE; the LL comes from the merge)
+hipError_t launch_wide(const Plan& p, const FullWs& w, const void* x, bool em, int grid,
+                       const FullPass& ps, int64_t tlo, int64_t thi, int seg_first, hipStream_t s) {
+    if (em && ps.lse_in == nullptr) return hipErrorInvalidValue;
+    const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
+    const FullGroupPtrs q = group_ptrs<wide::DP>(p, w, ps.group);
+    double* pll = (!em && !w.lse_pass) ? w.part_ll : nullptr;
+#define FULL_WIDE(EM_, VEC_)                                                                     \
+    hipLaunchKernelGGL((k_full_wide<EM_, VEC_>), dim3(grid), dim3(256), 0, s,                    \
+                       (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, q.wpk, q.wbias, q.muh, \
+                       q.cvec, q.rscale, q.part, pll, ps, tlo, thi, seg_first)
+    if (em && vec) FULL_WIDE(true, true);
+    else if (em) FULL_WIDE(true, false);
+    else if (vec) FULL_WIDE(false, true);
+    else FULL_WIDE(false, false);
+#undef FULL_WIDE
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -817,6 +1186,7 @@ hipError_t full_launch_fused(const Plan& p, const FullWs& w, const void* x, bool
         case 16: return launch_dp<16>(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
         case 32: return launch_dp<32>(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
         case 64: return launch_dp<64>(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
+        case 128: return launch_wide(p, w, x, em, grid, ps, tlo, thi, seg_first, s);
     }
     return hipErrorInvalidValue;
 }

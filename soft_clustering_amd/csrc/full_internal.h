@@ -48,12 +48,18 @@ struct FullWs {
     int* garg;                 // several groups: [G][N] argmax within each group (global index)
     float* gmax;               // several groups: [G][N] largest base-2 score within each group
     int groups;
+    bool lse_pass;             // the LSE comes from a pass of its own and the merge: several
+                               // groups, or D > 64 (statistics launches per quad of components)
     int64_t slots;             // partial slots per group
 };
 
 inline int64_t full_ncolp(int64_t d) { return 1 + d + d * (d + 1) / 2; }
 
 inline int full_groups(int64_t k) { return (int)((k + kFullKP - 1) / kFullKP); }
+
+// Whether the statistics pass normalises with a merged LSE written beforehand
+// (several groups; or D > 64, where a statistics launch covers four components)
+inline bool full_lse_pass(int64_t k, int dp) { return full_groups(k) > 1 || dp > 64; }
 
 inline FullWs full_ws(const Plan& p, char* ws) {
     FullWs w;
@@ -75,16 +81,18 @@ inline FullWs full_ws(const Plan& p, char* ws) {
     w.flags = (int*)(ws + p.off_diag);
     w.groups = full_groups(p.k);
     w.slots = p.p_max;
-    const bool many = w.groups > 1;
-    w.glse = many ? (float*)(ws + p.off_lse) : nullptr;
-    w.garg = many ? (int*)(ws + p.off_arg) : nullptr;
-    w.gmax = many ? (float*)(w.garg + (size_t)w.groups * p.n) : nullptr;
+    w.lse_pass = full_lse_pass(p.k, p.dp);
+    w.glse = w.lse_pass ? (float*)(ws + p.off_lse) : nullptr;
+    w.garg = w.lse_pass ? (int*)(ws + p.off_arg) : nullptr;
+    w.gmax = w.lse_pass ? (float*)(w.garg + (size_t)w.groups * p.n) : nullptr;
     return w;
 }
 
 // Kernel arguments that vary by group and pass (see full_launch_fused).
 struct FullPass {
     int group;               // components 16 group .. 16 group + 15
+    int quad;                // D > 64, statistics launches: components 4 quad .. 4 quad + 3
+                             // of the group
     const float* lse_in;     // natural-log LSE per point to normalise with (nullable:
                              // the group's own, when it is the only one)
     float* out_lse;          // E-step: natural-log LSE per point (the group's own)

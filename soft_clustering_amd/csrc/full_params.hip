@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     constexpr int NOB = full_nob(DP), NKS = full_nks(DP), DPO = full_dpo(DP);
     constexpr int NV = 2 * NOB * NKS * 64;   // panel vectors per component
     constexpr int RT = DP / 16;   // rows (and columns) of the matrix per thread
-    __shared__ double A[DP][DP + 1];
-    __shared__ double W[DP][DP + 1];
+    __shared__ double A[DP][DP + 1];   // C~, then its factor; at the end W = (L s)^{-1}
+    double(*W)[DP + 1] = A;           // (one matrix of LDS: 132 KB at D = 128)
     __shared__ double pinv[DP], mus[DP];
     __shared__ double pan[2][4][DP];   // four broadcast columns (factorisation), double-buffered
     __shared__ double rpan[2][4][DP];  // four broadcast rows (inverse), double-buffered
@@ -318,6 +318,10 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         }
     }
     __syncthreads();
+    // log|C~| = 2 sum log L_ii from the fp64 factor, before W takes its place
+    double ld = 0.0;
+    for (int i = tid; i < d; i += 256) ld += 0.5 * log(A[i][i]);   // log L_ii
+    ld = block_sum_f64(ld, red);
     // W = (L s)^{-1}; where its largest entry would leave the range the fp16
     // panel holds comfortably (above 2^14: a covariance far wider in one
     // direction than its mean variance suggests), s grows by the power of two
@@ -368,19 +372,14 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         Wk[v] = make_uint4(hw[0], hw[1], hw[2], hw[3]);              // hi half of the panel
         Wk[NV / 2 + v] = make_uint4(lw[0], lw[1], lw[2], lw[3]);     // lo half
     }
-    // bias W mu (fp64), the fp16 centre of the moments, log|C~| from the fp64 factor
+    // bias W mu (fp64), the fp16 centre of the moments
     for (int o = tid; o < DPO; o += 256) {
         double bsum = 0.0;
         if (o < d)
             for (int ic = 0; ic <= o; ++ic) bsum += W[o][ic] * mus[ic];
         wbias[k * DPO + o] = (float)bsum;
     }
-    double ld = 0.0;
-    for (int i = tid; i < DP; i += 256) {
-        if (i < d) ld += 0.5 * log(A[i][i]);   // log L_ii
-        muh[k * DP + i] = (float)(_Float16)(float)mus[i];
-    }
-    ld = block_sum_f64(ld, red);
+    for (int i = tid; i < DP; i += 256) muh[k * DP + i] = (float)(_Float16)(float)mus[i];
     if (tid == 0) {
         const double logdet = 2.0 * ld;
         const double lp = log((double)pi[k]);
@@ -434,7 +433,7 @@ __global__ __launch_bounds__(256) void k_full_mstep(const double* __restrict__ c
                                                     float* __restrict__ th_cov, float* out_pi,
                                                     float* out_mu, float* out_cov, int* flags) {
     __shared__ double red[256];
-    __shared__ double cen[64], s1v[64], dlt[64];   // centre, s1, mu' - centre (d <= 64)
+    __shared__ double cen[128], s1v[128], dlt[128];   // centre, s1, mu' - centre (d <= 128)
     const int k = blockIdx.x, tid = threadIdx.x;
     const int ncolp = 1 + d + d * (d + 1) / 2;
     const double* cs = colsum + (int64_t)k * ncolp;
@@ -457,7 +456,7 @@ __global__ __launch_bounds__(256) void k_full_mstep(const double* __restrict__ c
         if (out_mu) out_mu[(int64_t)k * d + i] = mf;
     }
     __syncthreads();
-    // row i = q / d from a float estimate (exact here: q < 64^2 and the quotient's
+    // row i = q / d from a float estimate (exact here: q < 128^2 and the quotient's
     // distance to the next integer is at least 1 / (2 d))
     const float inv_d = 1.0f / (float)d;
 #pragma unroll 4
@@ -582,6 +581,7 @@ hipError_t chol(const Plan& p, const FullWs& w, hipStream_t s) {
         case 16: FULL_CHOL(16); break;
         case 32: FULL_CHOL(32); break;
         case 64: FULL_CHOL(64); break;
+        case 128: FULL_CHOL(128); break;
         default: return hipErrorInvalidValue;
     }
 #undef FULL_CHOL
@@ -621,14 +621,20 @@ gmm_status full_em_step(const Plan& p, char* ws, const void* x, double* ll_out, 
     FullWs w = full_ws(p, ws);
     const int G = full_grid(p);
     const FullSegs sg = full_segs(p, G);
-    const bool many = w.groups > 1;
+    const bool many = w.lse_pass;
     if (many && group_lse(p, w, x, nullptr, nullptr, s) != hipSuccess) return GMM_E_HIP;
     for (int g = 0; g < w.groups; ++g) {
         FullPass ps = pass_of(g);
         ps.lse_in = many ? w.glse : nullptr;   // second loop: normalise with the merged LSE
+        // D > 64: one statistics launch per quad of live components
+        const int64_t kc = p.k - (int64_t)kFullKP * g < kFullKP ? p.k - (int64_t)kFullKP * g : kFullKP;
+        const int nq = p.dp > 64 ? (int)((kc + 3) / 4) : 1;
         for (int i = 0; i < sg.n; ++i) {
             const int64_t lo = (int64_t)i * sg.len, hi = lo + sg.len < sg.tiles ? lo + sg.len : sg.tiles;
-            if (full_launch_fused(p, w, x, true, G, ps, lo, hi, i == 0, s) != hipSuccess) return GMM_E_HIP;
+            for (int q = 0; q < nq; ++q) {
+                ps.quad = q;
+                if (full_launch_fused(p, w, x, true, G, ps, lo, hi, i == 0, s) != hipSuccess) return GMM_E_HIP;
+            }
             // every segment but the last is closed here; finalize adds the last one
             if (i + 1 < sg.n && reduce_group(p, w, g, G, i > 0 ? 1 : 0, s) != hipSuccess) return GMM_E_HIP;
         }
@@ -653,7 +659,7 @@ gmm_status full_loglik(const Plan& p, char* ws, const void* x, double* ll_out, f
                        int32_t* argmax, hipStream_t s) {
     FullWs w = full_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
-    if (w.groups > 1) {
+    if (w.lse_pass) {
         if (group_lse(p, w, x, lse, argmax, s) != hipSuccess) return GMM_E_HIP;
         return sum_ll(p, w, merge_grid(p), ll_out, s);
     }
@@ -671,7 +677,7 @@ gmm_status full_assign(const Plan& p, char* ws, const void* x, int m, int32_t* i
     FullWs w = full_ws(p, ws);
     if (p.n == 0) return sum_ll(p, w, 0, ll_out, s);
     const int G = full_grid(p);
-    const bool many = w.groups > 1;
+    const bool many = w.lse_pass;
     if (many && group_lse(p, w, x, nullptr, nullptr, s) != hipSuccess) return GMM_E_HIP;
     for (int g = 0; g < w.groups; ++g) {   // the groups in order, merging into the lists
         FullPass ps = pass_of(g);

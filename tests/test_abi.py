@@ -52,7 +52,7 @@ def test_bad_descriptors(kw):
     dict(n=10, d=64, k=65),                                   # diagonal K > 64 with fp32 storage
     dict(n=10, d=64, k=8, cov="iso"),                         # isotropic with fp32 storage
     dict(n=10, d=64, k=4097, cov="diag", x_dtype="bf16"),     # K above the large-K limit
-    dict(n=10, d=65, k=8, cov="full", x_dtype="f16"),         # full covariance, D > 64
+    dict(n=10, d=129, k=8, cov="full", x_dtype="f16"),        # full covariance, D > 128
     dict(n=10, d=64, k=257, cov="full", x_dtype="f16"),       # full covariance, K > 256
     dict(n=10, d=16, k=4, cov="full", x_dtype="f32"),         # full covariance, fp32 storage
 ])

@@ -101,6 +101,7 @@ CASES = [
     (2000, 64, 9, "full", "f16", 12),        # m > K
     (2500, 32, 40, "full", "f16", 6),        # three groups of 16 components
     (1200, 64, 20, "full", "f16", 3),        # two groups on the two-stage kernel
+    (1500, 128, 20, "full", "f16", 5),       # D = 128, two groups
 ]
 
 

@@ -106,7 +106,9 @@ def test_one_step_parity_every_iteration(gmm_lib, tiny):
                                                 # shrink, exactly scored ones inside the graph
                                                 ("diag", "bf16", 4000, 32, 300),
                                                 # full covariance in two groups of components
-                                                ("full", "f16", 3000, 8, 20)])
+                                                ("full", "f16", 3000, 8, 20),
+                                                # D = 96: statistics launches per quad of components
+                                                ("full", "f16", 3000, 96, 6)])
 def test_graph_and_batch_invariance(gmm_lib, cov, x_dtype, n, d, k):
     rng = np.random.default_rng(5)
     mu_t = rng.uniform(-5, 5, size=(k, d))

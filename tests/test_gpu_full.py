@@ -153,6 +153,12 @@ CASES = [
     (800, 2, 20, 1, True),       # D = 2, two groups, element-wise loads
     (2000, 16, 100, 0, False),   # 7 groups
     (1500, 24, 17, 3, True),     # 2 groups, element-wise loads
+    # 64 < D <= 128: an E-step launch per group of 16 writes its LSE, the merge,
+    # then one statistics launch per quad of components (one per wave)
+    (3000, 128, 16, 0, False),   # D = 128, four quads
+    (2000, 100, 5, 4, True),     # D = 100 padded to 128, element-wise loads, two quads
+    (2500, 128, 20, 0, False),   # two groups at D = 128
+    (200, 72, 3, 0, False),      # one tile, D = 72
 ]
 
 
@@ -311,14 +317,15 @@ def test_full_size_workload(gmm_lib):
         assert agree >= ARGMAX_MIN
 
 
-def test_grouped_segmented_statistics(gmm_lib, monkeypatch):
-    """K = 40 (three groups) at D = 32 with runs of one 256-point tile per
-    workgroup: every group's statistics pass takes several segments.  s0, s1
-    and s2 element by element against the oracle (allowance as in
+@pytest.mark.parametrize("n,d,k", [(140_000, 32, 40), (70_000, 128, 20)], ids=["d32-k40", "d128-k20"])
+def test_grouped_segmented_statistics(gmm_lib, monkeypatch, n, d, k):
+    """K = 40 (three groups) at D = 32, and K = 20 (two groups, statistics
+    launches per quad of components) at D = 128, with runs of one 256-point
+    tile per workgroup: every group's statistics pass takes several segments.
+    s0, s1 and s2 element by element against the oracle (allowance as in
     test_gpu_segments), and the same step as one segment agrees to fp32
     accumulation rounding."""
     from tests.gpu_common import oracle_stats_chunked, stats_elementwise
-    n, d, k = 140_000, 32, 40
     xd, xg, ldx, th0 = _make(n, d, k, 0, False, seed=77)
     th = to_dev(*th0)
     gm = gmm_lib.Gmm(n, d, k, "full", "f16")
