@@ -332,7 +332,9 @@ def main(argv=None):
     if fp32_path:
         kname = "k_diag_split (the LL sum in its last workgroup)"
     elif full_path:
-        kname = ("k_full_pipe (+ k_full_sum_ll)" if w.d > 32 else "k_full_fused (+ k_full_sum_ll)")
+        kname = ("k_full_wide<E-step> + k_full_merge + one k_full_wide<statistics> per quad of components "
+                 "(+ k_full_sum_ll)" if w.d > 64 else
+                 "k_full_pipe (+ k_full_sum_ll)" if w.d > 32 else "k_full_fused (+ k_full_sum_ll)")
     elif w.k <= 256:
         kname = "k_lk<fused E+M> (+ k_lk_scan, k_lk_centre, k_lk_panel, k_lk_sum)"
     else:

@@ -49,7 +49,11 @@ extern "C" {
 typedef enum {
     GMM_OK = 0,
     GMM_E_ARG = 1,          /* null pointer, bad size, bad enum, bad alignment */
-    GMM_E_UNSUPPORTED = 2,  /* (cov, dtype, D, K) combination not provided */
+    GMM_E_UNSUPPORTED = 2,  /* (cov, dtype, D, K) combination not provided.
+                               Provided: D <= 128 throughout; diagonal with
+                               K <= 64 (any storage type); diagonal or
+                               isotropic with bf16 / fp16 storage, K <= 4096;
+                               full covariance with fp16 storage, K <= 256 */
     GMM_E_WORKSPACE = 3,    /* ws_bytes smaller than gmm_workspace_bytes() */
     GMM_E_HIP = 4,          /* a HIP runtime call or kernel launch failed */
     GMM_E_NOT_PD = 5,       /* reported by gmm_diagnostics only */

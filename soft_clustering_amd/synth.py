@@ -71,6 +71,10 @@ WORKLOADS = {
         Workload("full-f16-n1e6-d64-k16", 1_000_000, 64, 16, "full", "f16",
                  ("normal", 5.0), ("eig_log10", -1.5, 1.5), iters=1,
                  data_seed=1005, init_seed=2005),
+        # the full-covariance mixture at D = 128 (the widest D the library takes)
+        Workload("full-f16-n1e6-d128-k16", 1_000_000, 128, 16, "full", "f16",
+                 ("normal", 5.0), ("eig_log10", -1.5, 1.5), iters=1,
+                 data_seed=1006, init_seed=2006),
     ]
 }
 
