@@ -56,32 +56,34 @@ __global__ __launch_bounds__(256) void k_full_load(int k_real, int d, const floa
     }
 }
 
-// One workgroup per padded component (256 threads).  The factorisation is
-// right-looking on the lower triangle of C~ (fp64), one column per step: each
-// thread holds its elements (ti + 16 a, tc + 16 b) in registers and the column
-// of each step is broadcast through LDS.
-template <int DP>
-__global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridge_rel,
+// One workgroup per padded component (TG x TG threads: 16 x 16, or 32 x 32 at
+// D = 128).  The factorisation is right-looking on the lower triangle of C~
+// (fp64), one column per step: each thread holds its elements
+// (ti + TG a, tc + TG b) in registers and the column of each step is
+// broadcast through LDS.
+template <int DP, int TG>
+__global__ __launch_bounds__(TG * TG) void k_full_chol(int k_real, int d, float ridge_rel,
                                                    const float* pi, const float* mu,
                                                    const float* cov, uint4* wpk, float* wbias,
                                                    float* muh, float* cvec, float* rscale,
                                                    int* flags) {
     constexpr int NOB = full_nob(DP), NKS = full_nks(DP), DPO = full_dpo(DP);
     constexpr int NV = 2 * NOB * NKS * 64;   // panel vectors per component
-    constexpr int RT = DP / 16;   // rows (and columns) of the matrix per thread
+    constexpr int NT = TG * TG;
+    constexpr int RT = DP / TG;   // rows (and columns) of the matrix per thread
     __shared__ double A[DP][DP + 1];   // C~, then its factor; at the end W = (L s)^{-1}
     double(*W)[DP + 1] = A;           // (one matrix of LDS: 132 KB at D = 128)
     __shared__ double pinv[DP], mus[DP];
     __shared__ double pan[2][4][DP];   // four broadcast columns (factorisation), double-buffered
     __shared__ double rpan[2][4][DP];  // four broadcast rows (inverse), double-buffered
-    __shared__ double red[256];
+    __shared__ double red[NT];
     const int k = blockIdx.x, tid = threadIdx.x;
-    const int ti = tid / 16, tc = tid % 16;   // this thread's elements: (ti + 16 a, tc + 16 b)
+    const int ti = tid / TG, tc = tid % TG;   // this thread's elements: (ti + TG a, tc + TG b)
     uint4* Wk = wpk + (int64_t)k * NV;
     auto put_identity = [&]() {   // a zero panel: the component is never scored (c_k = -inf)
-        for (int i = tid; i < NV; i += 256) Wk[i] = make_uint4(0, 0, 0, 0);
-        for (int i = tid; i < DPO; i += 256) wbias[k * DPO + i] = 0.0f;
-        for (int i = tid; i < DP; i += 256) muh[k * DP + i] = 0.0f;
+        for (int i = tid; i < NV; i += NT) Wk[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < DPO; i += NT) wbias[k * DPO + i] = 0.0f;
+        for (int i = tid; i < DP; i += NT) muh[k * DP + i] = 0.0f;
         if (tid == 0) {
             cvec[k] = -INFINITY;
             rscale[k] = 1.0f;
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     for (int a = 0; a < RT; ++a)
 #pragma unroll
         for (int b2 = 0; b2 < RT; ++b2) {
-            const int r = ti + 16 * a, c = tc + 16 * b2;
+            const int r = ti + TG * a, c = tc + TG * b2;
             const bool in = c <= r && r < d;
             Cr[a][b2] = in ? C[(int64_t)r * d + c] : 0.0f;
             if (in && !isfinite(Cr[a][b2])) bad = 1.0;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         for (int a = 0; a < RT; ++a)
 #pragma unroll
             for (int b2 = 0; b2 < RT; ++b2) {
-                const int r = ti + 16 * a, c = tc + 16 * b2;
+                const int r = ti + TG * a, c = tc + TG * b2;
                 double v = 0.0;
                 if (c <= r) {
                     if (r < d) v = (double)Cr[a][b2] + (r == c ? eps : 0.0);
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         // step) into the other half of the double-buffered panel.
         if (tc < 4) {
 #pragma unroll
-            for (int a = 0; a < RT; ++a) pan[0][tc][ti + 16 * a] = Ar[a][0];
+            for (int a = 0; a < RT; ++a) pan[0][tc][ti + TG * a] = Ar[a][0];
         }
         bool failed = false;
         for (int st = 0; st < DP / 4; ++st) {
@@ -177,11 +179,11 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
             };
             double xc[RT][4];
 #pragma unroll
-            for (int b2 = 0; b2 < RT; ++b2) transform(tc + 16 * b2, xc[b2]);
-            const int own_t = tc - (j0 & 15);   // column j0 + own_t is this thread's (0..3)
+            for (int b2 = 0; b2 < RT; ++b2) transform(tc + TG * b2, xc[b2]);
+            const int own_t = tc - (j0 % TG);   // column j0 + own_t is this thread's (0..3)
 #pragma unroll
             for (int a = 0; a < RT; ++a) {
-                const int i = ti + 16 * a;
+                const int i = ti + TG * a;
                 double xr[4];
                 transform(i, xr);
                 if (i > j0 + 3) {
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                     for (int t = 0; t < 4; ++t) g[t] = xr[t] * rp[t];
 #pragma unroll
                     for (int b2 = 0; b2 < RT; ++b2) {
-                        const int c = tc + 16 * b2;
+                        const int c = tc + TG * b2;
                         if (c > j0 + 3 && c <= i)
                             Ar[a][b2] -= g[0] * xc[b2][0] + g[1] * xc[b2][1] + g[2] * xc[b2][2] +
                                          g[3] * xc[b2][3];
@@ -203,16 +205,16 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                         if (own_t == t) v = xr[t];
 #pragma unroll
                     for (int b2 = 0; b2 < RT; ++b2)
-                        if (b2 == j0 / 16) Ar[a][b2] = v;
+                        if (b2 == j0 / TG) Ar[a][b2] = v;
                 }
             }
-            const int jn = j0 + 4, nt = tc - (jn & 15);
+            const int jn = j0 + 4, nt = tc - (jn % TG);
             if (jn < DP && nt >= 0 && nt < 4) {
 #pragma unroll
                 for (int b2 = 0; b2 < RT; ++b2)
-                    if (b2 == jn / 16) {
+                    if (b2 == jn / TG) {
 #pragma unroll
-                        for (int a = 0; a < RT; ++a) pan[(st + 1) & 1][nt][ti + 16 * a] = Ar[a][b2];
+                        for (int a = 0; a < RT; ++a) pan[(st + 1) & 1][nt][ti + TG * a] = Ar[a][b2];
                     }
             }
         }
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) A[ti + 16 * a][tc + 16 * b2] = Ar[a][b2];
+        for (int b2 = 0; b2 < RT; ++b2) A[ti + TG * a][tc + TG * b2] = Ar[a][b2];
     // scale s = 2^-e with 2^e near sqrt(|tr| / D)
     int e = 0;
     if (scale > 0.0 && isfinite(scale)) {
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     // W = s^-1 D^{-1/2} U^{-1}.  U^{-1} right-looking from R = I: once row i of R is
     // final, the rows below take R_r -= U_ri R_i.
     __syncthreads();
-    for (int i = tid; i < DP; i += 256) {
+    for (int i = tid; i < DP; i += NT) {
         pinv[i] = 1.0 / A[i][i];
         mus[i] = i < d ? (double)mu[(int64_t)k * d + i] : 0.0;
     }
@@ -254,14 +256,14 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) Rr[a][b2] = (ti + 16 * a == tc + 16 * b2) ? 1.0 : 0.0;
+        for (int b2 = 0; b2 < RT; ++b2) Rr[a][b2] = (ti + TG * a == tc + TG * b2) ? 1.0 : 0.0;
     // blocked by 4 rows: step st takes rows I = 4 st .. 4 st + 3 (their values y at
     // the start of the step broadcast through rpan).  Every thread finishes the
     // block rows for its columns (y'_t = y_t - sum_{w<t} U_{i0+t, i0+w} y'_w), the
     // owners of I keep y', and the rows below take R_r -= sum_t U_{r, i0+t} y'_t.
     if (ti < 4) {
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) rpan[0][ti][tc + 16 * b2] = Rr[0][b2];
+        for (int b2 = 0; b2 < RT; ++b2) rpan[0][ti][tc + TG * b2] = Rr[0][b2];
     }
     for (int st = 0; st < DP / 4; ++st) {
         const int i0 = 4 * st;
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         double yc[RT][4];
 #pragma unroll
         for (int b2 = 0; b2 < RT; ++b2) {
-            const int c = tc + 16 * b2;
+            const int c = tc + TG * b2;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 double v = rv[t][c];
@@ -284,10 +286,10 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                 yc[b2][t] = v;
             }
         }
-        const int own_t = ti - (i0 & 15);   // row i0 + own_t is this thread's (0..3)
+        const int own_t = ti - (i0 % TG);   // row i0 + own_t is this thread's (0..3)
 #pragma unroll
         for (int a = 0; a < RT; ++a) {
-            const int r = ti + 16 * a;
+            const int r = ti + TG * a;
             if (r > i0 + 3) {
                 double ur[4];
 #pragma unroll
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                 for (int b2 = 0; b2 < RT; ++b2)
                     Rr[a][b2] -= ur[0] * yc[b2][0] + ur[1] * yc[b2][1] + ur[2] * yc[b2][2] +
                                  ur[3] * yc[b2][3];
-            } else if (own_t >= 0 && own_t < 4 && a == i0 / 16) {
+            } else if (own_t >= 0 && own_t < 4 && a == i0 / TG) {
 #pragma unroll
                 for (int b2 = 0; b2 < RT; ++b2) {
                     double v = yc[b2][0];
@@ -307,20 +309,20 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
                 }
             }
         }
-        const int in = i0 + 4, nt = ti - (in & 15);
+        const int in = i0 + 4, nt = ti - (in % TG);
         if (in < DP && nt >= 0 && nt < 4) {
 #pragma unroll
             for (int a = 0; a < RT; ++a)
-                if (a == in / 16) {
+                if (a == in / TG) {
 #pragma unroll
-                    for (int b2 = 0; b2 < RT; ++b2) rpan[(st + 1) & 1][nt][tc + 16 * b2] = Rr[a][b2];
+                    for (int b2 = 0; b2 < RT; ++b2) rpan[(st + 1) & 1][nt][tc + TG * b2] = Rr[a][b2];
                 }
         }
     }
     __syncthreads();
     // log|C~| = 2 sum log L_ii from the fp64 factor, before W takes its place
     double ld = 0.0;
-    for (int i = tid; i < d; i += 256) ld += 0.5 * log(A[i][i]);   // log L_ii
+    for (int i = tid; i < d; i += NT) ld += 0.5 * log(A[i][i]);   // log L_ii
     ld = block_sum_f64(ld, red);
     // W = (L s)^{-1}; where its largest entry would leave the range the fp16
     // panel holds comfortably (above 2^14: a covariance far wider in one
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     double wmax = 0.0;
 #pragma unroll
     for (int a = 0; a < RT; ++a) {
-        const int r = ti + 16 * a;
+        const int r = ti + TG * a;
         const double f = sqrt(pinv[r]) / sc;   // 1 / (sqrt(A_rr) s)
 #pragma unroll
         for (int b2 = 0; b2 < RT; ++b2) {
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
     }
     red[tid] = wmax;
     __syncthreads();
-    for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
         if (tid < s2) red[tid] = fmax(red[tid], red[tid + s2]);
         __syncthreads();
     }
@@ -349,11 +351,11 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
-        for (int b2 = 0; b2 < RT; ++b2) W[ti + 16 * a][tc + 16 * b2] = Rr[a][b2] * wf;
+        for (int b2 = 0; b2 < RT; ++b2) W[ti + TG * a][tc + TG * b2] = Rr[a][b2] * wf;
     __syncthreads();
     // panel: out dimension o = 32 ob + l % 32 (rows), input i = 16 ks + 8 (l / 32) + q;
     // zero outside the D x D lower triangle; hi = fp16(w), lo = fp16(w - hi)
-    for (int v = tid; v < NV / 2; v += 256) {
+    for (int v = tid; v < NV / 2; v += NT) {
         const int l = v % 64, ks = (v / 64) % NKS, ob = v / (64 * NKS);
         const int o = 32 * ob + (l & 31);
         uint32_t hw[4], lw[4];
@@ -373,13 +375,13 @@ __global__ __launch_bounds__(256) void k_full_chol(int k_real, int d, float ridg
         Wk[NV / 2 + v] = make_uint4(lw[0], lw[1], lw[2], lw[3]);     // lo half
     }
     // bias W mu (fp64), the fp16 centre of the moments
-    for (int o = tid; o < DPO; o += 256) {
+    for (int o = tid; o < DPO; o += NT) {
         double bsum = 0.0;
         if (o < d)
             for (int ic = 0; ic <= o; ++ic) bsum += W[o][ic] * mus[ic];
         wbias[k * DPO + o] = (float)bsum;
     }
-    for (int i = tid; i < DP; i += 256) muh[k * DP + i] = (float)(_Float16)(float)mus[i];
+    for (int i = tid; i < DP; i += NT) muh[k * DP + i] = (float)(_Float16)(float)mus[i];
     if (tid == 0) {
         const double logdet = 2.0 * ld;
         const double lp = log((double)pi[k]);
@@ -573,15 +575,15 @@ hipError_t group_lse(const Plan& p, const FullWs& w, const void* x, float* out_l
 }
 
 hipError_t chol(const Plan& p, const FullWs& w, hipStream_t s) {
-#define FULL_CHOL(DP_)                                                                            \
-    hipLaunchKernelGGL((k_full_chol<DP_>), dim3(kFullKP * w.groups), dim3(256), 0, s, (int)p.k, (int)p.d, \
-                       p.ridge_rel, w.pi, w.mu, w.cov, w.wpk, w.wbias, w.muh, w.cvec, w.rscale,    \
-                       w.flags)
+#define FULL_CHOL(DP_, TG_)                                                                       \
+    hipLaunchKernelGGL((k_full_chol<DP_, TG_>), dim3(kFullKP * w.groups), dim3(TG_ * TG_), 0, s,     \
+                       (int)p.k, (int)p.d, p.ridge_rel, w.pi, w.mu, w.cov, w.wpk, w.wbias, w.muh,    \
+                       w.cvec, w.rscale, w.flags)
     switch (p.dp) {
-        case 16: FULL_CHOL(16); break;
-        case 32: FULL_CHOL(32); break;
-        case 64: FULL_CHOL(64); break;
-        case 128: FULL_CHOL(128); break;
+        case 16: FULL_CHOL(16, 16); break;
+        case 32: FULL_CHOL(32, 16); break;
+        case 64: FULL_CHOL(64, 16); break;
+        case 128: FULL_CHOL(128, 32); break;
         default: return hipErrorInvalidValue;
     }
 #undef FULL_CHOL
