@@ -57,17 +57,20 @@ DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="13892434a1997e62", fetch_kib=125176.5, write_kib=4144.3,
+        sources="36d68f80714d3124", fetch_kib=125188.2, write_kib=4144.3,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="53e4546cad67ebaa", fetch_kib=1251543.2, write_kib=78521.7,
-        copy_bytes=2.56e+09, copy_fetch_kib=1250035.8125, copy_write_kib=2500000.0),
+        sources="eb934dafb31f75b6", fetch_kib=1251543.4, write_kib=78338.1,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250033.875, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="53e4546cad67ebaa", fetch_kib=53735522.0, write_kib=7415500.5,
-        copy_bytes=5.12e+10, copy_fetch_kib=25000258.0625, copy_write_kib=50000000.0),
+        sources="eb934dafb31f75b6", fetch_kib=53728006.3, write_kib=7438873.6,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000264.25, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="2484ae2e4834f396", fetch_kib=65749.8, write_kib=39105.4,
+        sources="3283499735d5531b", fetch_kib=65751.9, write_kib=39101.7,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
+    "full-f16-n1e6-d128-k16": dict(
+        sources="3283499735d5531b", fetch_kib=270161.9, write_kib=70561.1,
+        copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
 FAMILY_SOURCES = {
