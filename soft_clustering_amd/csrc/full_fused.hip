@@ -767,6 +767,25 @@ constexpr int kXR = DP + 8;      // halves per row of the row-major tile
 constexpr int kGS = T + 4;
 constexpr int NVL = 2 * NOB * NKS;   // panel vectors per lane and component in memory
 __host__ __device__ constexpr int pair_of(int ob, int ks) { return ob * (ob + 1) + ks; }
+
+// The whitening MFMAs from inline asm: the accumulator stays in VGPRs (the
+// compiler would give it AGPRs next to the resident second moments, and the
+// vector unit would then copy it out for |z|^2), the hi half of the panel is
+// read from VGPRs and the lo half from AGPRs.  The compiler sees no MFMA in
+// an asm statement, so the wait states are written out: two before each (a
+// vector-ALU write of an operand just before an MFMA) and `settle` (24) after
+// the last one of a block, before any other instruction touches the
+// accumulators (a 32x32x16 result needs 18 before a vector-ALU read); its
+// "+v" operands make every later use depend on it.
+__device__ __forceinline__ void mfma_vv(f32x16& d, const half8& a, const half8& b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_av(f32x16& d, const half8& a, const half8& b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "a"(a), "v"(b));
+}
+__device__ __forceinline__ void settle(f32x16& p, f32x16& q, f32x16& r, f32x16& u) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(p), "+v"(q), "+v"(r), "+v"(u));
+}
 }  // namespace wide
 
 template <bool EM, bool VEC>
@@ -867,19 +886,22 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
 #pragma unroll
                 for (int ob = 0; ob < NOB; ++ob) {
                     if (ks > 2 * ob + 1) continue;   // above the diagonal: W is lower triangular
-                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[0][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
-                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[1][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
+                    if constexpr (EM) {   // beside the resident moments: VGPR accumulators
+                        mfma_vv(acc[ob], wv[0][pair_of(ob, ks)], xb);
+                        mfma_av(acc[ob], wv[1][pair_of(ob, ks)], xb);
+                    } else {
+                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[0][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
+                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[1][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
+                    }
                 }
             }
-            float q0 = 0.0f, q1 = 0.0f;
+            if constexpr (EM) settle(acc[0], acc[1], acc[2], acc[3]);
+            float qp[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four chains: |z|^2 waits on no long chain
 #pragma unroll
             for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    q0 = fmaf(acc[ob][r], acc[ob][r], q0);
-                    q1 = fmaf(acc[ob][r + 1], acc[ob][r + 1], q1);
-                }
-            const float q = halves_sum(q0 + q1);
+                for (int r = 0; r < 16; ++r) qp[r & 3] = fmaf(acc[ob][r], acc[ob][r], qp[r & 3]);
+            const float q = halves_sum((qp[0] + qp[1]) + (qp[2] + qp[3]));
             if (lane < 32) g_s[kl][32 * st + lane] = cvk - hqk * q;
         }
     };

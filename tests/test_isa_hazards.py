@@ -1,10 +1,12 @@
-"""Wait states around the inline-asm MFMAs of the large-K statistics kernels.
+"""Wait states around the inline-asm MFMAs of the kernels that issue some.
 
-The statistics kernels that run one wave per SIMD issue their score and s0
-MFMAs from inline asm (accumulators in VGPRs).  The compiler does not see an
-MFMA inside an asm statement, so it inserts none of the wait states the
-matrix-core dependency rules ask for; the kernel writes them out.  This test
-compiles the kernel source for gfx950 and checks the emitted code:
+The large-K statistics kernels that run one wave per SIMD issue their score
+and s0 MFMAs from inline asm, and the D <= 128 full-covariance kernels their
+whitening MFMAs (accumulators in VGPRs; in the full-covariance kernels half
+of the A operands come from AGPRs).  The compiler does not see an MFMA
+inside an asm statement, so it inserts none of the wait states the
+matrix-core dependency rules ask for; the kernels write them out.  This test
+compiles the kernel sources for gfx950 and checks the emitted code:
 
 * before each such MFMA no vector-ALU instruction writes one of its A / B
   source registers within the 8 preceding instructions (a VALU write of an
@@ -24,7 +26,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "soft_clustering_amd", "csrc", "largek.hip")
+CSRC = os.path.join(ROOT, "soft_clustering_amd", "csrc")
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                                 reason="hipcc not available")
@@ -45,8 +47,9 @@ def _split(ins):
     return parts[0], [t.strip() for t in re.split(r",(?![^\[]*\])", parts[1])]
 
 
-def _kernels(asm_text):
-    """{kernel symbol: [(instruction, from inline asm)]} of the k_lk kernels."""
+def _kernels(asm_text, key):
+    """{kernel symbol: [(instruction, from inline asm)]} of the kernels whose
+    symbol contains `key`."""
     out, cur, in_asm = {}, None, False
     for raw in asm_text.split("\n"):
         if ";;#ASMSTART" in raw:
@@ -56,7 +59,7 @@ def _kernels(asm_text):
             in_asm = False
             continue
         line = raw.split(";")[0].strip()
-        m = re.match(r"^(_ZN3gmm\S*k_lk\S*):$", line)
+        m = re.match(r"^(_ZN3gmm\S*" + key + r"\S*):$", line)
         if m:
             cur = m.group(1)
             out[cur] = []
@@ -106,26 +109,37 @@ def _check(code):
     return n, bad
 
 
-def test_inline_asm_mfma_wait_states(tmp_path):
+CASES = [
+    # source, kernel symbol key, {asm MFMAs per kernel: kernels with that many}
+    # large K: the diagonal statistics kernels at D = 128 (sweep 2 and fused
+    # E+M, x 2 storage types x 2 load paths): 34 score MFMAs (17 steps x 2
+    # blocks) and 4 s0 MFMAs per tile
+    ("largek.hip", "k_lk", {38: 8}),
+    # full covariance, D <= 128: the statistics kernels (2 load paths), 40
+    # whitening MFMAs per 32-point block (20 lower-triangle blocks, hi and lo)
+    # for each of the tile's 8 blocks
+    ("full_fused.hip", "k_full_wide", {320: 2}),
+]
+
+
+@pytest.mark.parametrize("src,key,expect", CASES, ids=[c[1] for c in CASES])
+def test_inline_asm_mfma_wait_states(tmp_path, src, key, expect):
     from soft_clustering_amd import build as b
-    out = tmp_path / "largek.s"
-    cmd = [b.HIPCC, *b.FLAGS, *b.NO_IEEE.get("largek.hip", []), "-w", "--cuda-device-only", "-S", SRC,
-           "-o", str(out)]
+    out = tmp_path / (src + ".s")
+    cmd = [b.HIPCC, *b.FLAGS, *b.NO_IEEE.get(src, []), "-w", "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
-    kernels = _kernels(out.read_text())
-    assert kernels, "no k_lk kernels found in the device code"
-    checked = 0
+    kernels = _kernels(out.read_text(), key)
+    assert kernels, f"no {key} kernels found in the device code"
+    counts = {}
     findings = []
     for name, ins in kernels.items():
         n, bad = _check(ins)
         if n:
-            checked += 1
-            # 34 score MFMAs (17 steps x 2 blocks) and 4 s0 MFMAs per tile
-            assert n == 38, (name, n)
+            counts[n] = counts.get(n, 0) + 1
         findings += [f"{name}: {x}" for x in bad]
-    # the diagonal statistics kernels at D = 128: sweep 2 and fused E+M, x 2 storage types x 2 load paths
-    assert checked == 8, checked
+    assert counts == expect, counts
     assert not findings, "\n".join(findings[:20])
 
 
