@@ -167,8 +167,10 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
     double ll = 0.0;
 
     // One point of tile t (fp16), zero outside [0, N) x [0, D).  Every load is
-    // issued unconditionally from an in-bounds address and masked afterwards,
-    // so the loads of a tile are all in flight together.
+    // issued unconditionally from an in-bounds address, so the loads of a tile
+    // are all in flight together; on the vector path the mask is applied when
+    // the tile is stored (`finish`), so that the wait for the loads comes there
+    // and not right after them.
     auto load_point = [&](int64_t t, uint4 (&xv)[DP / 8]) __attribute__((always_inline)) {
         const int64_t p = t * T + tid;
         const bool valid = p < n;
@@ -176,11 +178,8 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
         if constexpr (VEC) {
             const int cmax = d / 8;
 #pragma unroll
-            for (int c = 0; c < DP / 8; ++c) {
-                const uint4 v = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
-                const uint32_t m = (valid && c < cmax) ? ~0u : 0u;
-                xv[c] = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-            }
+            for (int c = 0; c < DP / 8; ++c)
+                xv[c] = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
         } else {
             const uint16_t* rb = reinterpret_cast<const uint16_t*>(row);
 #pragma unroll
@@ -203,6 +202,15 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
             wp[v] = __builtin_bit_cast(half8, wpk[((int64_t)k * NV + v) * 64 + lane]);
     };
 
+    auto finish = [&](int64_t t, int c, uint4 v) __attribute__((always_inline)) {
+        if constexpr (VEC) {
+            const uint32_t m = (t * T + tid < n && c < d / 8) ? ~0u : 0u;
+            return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+        } else {
+            return v;
+        }
+    };
+
     uint4 xv[DP / 8];
     half8 wp[NV];
     if (t0 < t1) {
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void k_full_fused(
         const bool valid = p < n;
         __syncthreads();   // the previous tile is done with xr_s / g_s
 #pragma unroll
-        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[tid][8 * c]) = xv[c];
+        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[tid][8 * c]) = finish(t, c, xv[c]);
         __syncthreads();
         if (t + 1 < t1) load_point(t + 1, xv);   // the next tile, behind this one's work
 
@@ -458,36 +466,39 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
     const int64_t t0 = tlo + b * tb + (b < tr ? b : tr);
     const int nt = (int)(tb + (b < tr ? 1 : 0));
 
-    // the whitening stage's point loads: thread tid < 256 holds point tid of a tile
+    // the whitening stage's point loads: thread tid < 256 holds point tid of a
+    // tile, loaded raw from an in-bounds address and masked when stored (so
+    // that the wait for the loads comes at the store, a tile later)
     uint4 xv[8];
     auto load_point = [&](int64_t t) __attribute__((always_inline)) {
         const int64_t p = t * T + tid;
-        const bool valid = p < n;
-        const _Float16* row = x + (valid ? p : 0) * ldx;
+        const _Float16* row = x + (p < n ? p : 0) * ldx;
+        const int cmax = d / 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xv[c] = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
+    };
+    auto store_point = [&](int buf, int64_t t) __attribute__((always_inline)) {
+        const bool valid = t * T + tid < n;
         const int cmax = d / 8;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const uint4 vv = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
             const uint32_t m = (valid && c < cmax) ? ~0u : 0u;
-            xv[c] = make_uint4(vv.x & m, vv.y & m, vv.z & m, vv.w & m);
+            *reinterpret_cast<uint4*>(&xr_s[buf][xoff(tid, c)]) =
+                make_uint4(xv[c].x & m, xv[c].y & m, xv[c].z & m, xv[c].w & m);
         }
-    };
-    auto store_point = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(&xr_s[buf][xoff(tid, c)]) = xv[c];
     };
 
     if (p1) {
         // ---- whitening stage: stages tile it + 1, loads tile it + 2, whitens tile it
         if (nt > 0) {
             load_point(t0);
-            store_point(0);
+            store_point(0, t0);
             if (nt > 1) load_point(t0 + 1);
         }
         __syncthreads();
         for (int it = 0; it <= nt; ++it) {
             if (it < nt) {
-                if (it + 1 < nt) store_point((it + 1) % 3);
+                if (it + 1 < nt) store_point((it + 1) % 3, t0 + it + 1);
                 if (it + 2 < nt) load_point(t0 + it + 2);
                 const uint16_t* xt = xr_s[it % 3];
                 float(*gs)[kGS] = g_s[it & 1];
@@ -852,9 +863,30 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
             return make_uint4(wv[0], wv[1], wv[2], wv[3]);
         }
     };
+    // the same in two halves, so that a load's wait comes only where its value
+    // is stored: the raw 16 bytes (vector path; the element-wise path masks as
+    // it assembles), then the mask
+    auto load_raw = [&](int64_t t, int c) __attribute__((always_inline)) {
+        if constexpr (VEC) {
+            const int64_t p = t * T + tid;
+            const _Float16* row = x + (p < n ? p : 0) * ldx;
+            const int cmax = d / 8;
+            return *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
+        } else {
+            return load_col(t, c);
+        }
+    };
+    auto finish = [&](int64_t t, int c, uint4 v) __attribute__((always_inline)) {
+        if constexpr (VEC) {
+            const uint32_t m = (t * T + tid < n && c < d / 8) ? ~0u : 0u;
+            return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+        } else {
+            return v;
+        }
+    };
     auto load_point = [&](int64_t t, uint4 (&xv)[DP / 8]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < DP / 8; ++c) xv[c] = load_col(t, c);
+        for (int c = 0; c < DP / 8; ++c) xv[c] = load_raw(t, c);
     };
     // the lower-triangle blocks of component kg's panel (group-local index)
     auto load_panel = [&](int kg, half8 (&wv)[2][NPR]) __attribute__((always_inline)) {
@@ -917,12 +949,17 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
 
     half8 wv[2][NPR];
     uint4 xv[EM ? 1 : DP / 8];   // E-step: the next tile's point, loaded behind this one
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    auto store_tile = [&](int buf, int64_t t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[buf][tid][8 * c]) = xv[c];
+        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[buf][tid][8 * c]) = finish(t, c, xv[c]);
     };
     if constexpr (EM) {
         load_panel(kq + w, wv);
+        // wait for the panel here, once: otherwise the wait inserted before its
+        // first use inside the tile loop stays in the loop and also waits for
+        // the loads of the next tile issued just before
+#pragma unroll
+        for (int i = 0; i < NPR; ++i) asm volatile("" : : "v"(wv[0][i]), "a"(wv[1][i]));
         if (t0 < t1) {
 #pragma unroll
             for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[0][tid][8 * c]) = load_col(t0, c);
@@ -939,32 +976,30 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
             // the next tile goes to the other buffer (it held tile t - 1) two
             // 16-byte columns per whitening step, each stored three steps after
             // its loads were issued: 32 registers in flight instead of 64
-            const bool more = t + 1 < t1;
+            // (after the last tile: tile t again, into a buffer no one reads; the
+            // loads are not conditional, so each one's wait stays where it is stored)
+            const int64_t tn = t + 1 < t1 ? t + 1 : t;
             const float cvk = cv_s[w], hqk = hq_s[w];
             uint4 nx[4][2];
 #pragma unroll
             for (int st = 0; st < T / 32; ++st) {
-                if (more) {
-                    nx[st % 4][0] = load_col(t + 1, 2 * st);
-                    nx[st % 4][1] = load_col(t + 1, 2 * st + 1);
-                    if (st >= 3) {
-                        const int c = 2 * (st - 3);
-                        *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = nx[(st - 3) % 4][0];
-                        *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = nx[(st - 3) % 4][1];
-                    }
+                nx[st % 4][0] = load_raw(tn, 2 * st);
+                nx[st % 4][1] = load_raw(tn, 2 * st + 1);
+                if (st >= 3) {
+                    const int c = 2 * (st - 3);
+                    *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = finish(tn, c, nx[(st - 3) % 4][0]);
+                    *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = finish(tn, c + 1, nx[(st - 3) % 4][1]);
                 }
                 whiten_step(w, wv, cur, st, cvk, hqk);
             }
-            if (more) {
 #pragma unroll
-                for (int st = T / 32; st < T / 32 + 3; ++st) {
-                    const int c = 2 * (st - 3);
-                    *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = nx[(st - 3) % 4][0];
-                    *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = nx[(st - 3) % 4][1];
-                }
+            for (int st = T / 32; st < T / 32 + 3; ++st) {
+                const int c = 2 * (st - 3);
+                *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = finish(tn, c, nx[(st - 3) % 4][0]);
+                *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = finish(tn, c + 1, nx[(st - 3) % 4][1]);
             }
         } else {
-            store_tile(0);
+            store_tile(0, t);
             __syncthreads();
             if (t + 1 < t1) load_point(t + 1, xv);   // the next tile, behind this one's work
 #pragma unroll 1
