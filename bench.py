@@ -66,10 +66,10 @@ TRAFFIC = {
         sources="eb934dafb31f75b6", fetch_kib=53728006.3, write_kib=7438873.6,
         copy_bytes=5.12e+10, copy_fetch_kib=25000264.25, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="3283499735d5531b", fetch_kib=65751.9, write_kib=39101.7,
+        sources="9d36e26eb823cc55", fetch_kib=66005.4, write_kib=39617.7,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
     "full-f16-n1e6-d128-k16": dict(
-        sources="3283499735d5531b", fetch_kib=270161.9, write_kib=70561.1,
+        sources="9d36e26eb823cc55", fetch_kib=257688.0, write_kib=41403.0,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
