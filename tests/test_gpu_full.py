@@ -159,6 +159,8 @@ CASES = [
     (2000, 100, 5, 4, True),     # D = 100 padded to 128, element-wise loads, two quads
     (2500, 128, 20, 0, False),   # two groups at D = 128
     (200, 72, 3, 0, False),      # one tile, D = 72
+    (2000, 128, 256, 0, False),  # K = 256 at D = 128: 16 groups, 64 statistics launches
+    (1500, 96, 33, 2, True),     # D = 96, three groups, element-wise loads
 ]
 
 
