@@ -66,10 +66,10 @@ TRAFFIC = {
         sources="eb934dafb31f75b6", fetch_kib=53728006.3, write_kib=7438873.6,
         copy_bytes=5.12e+10, copy_fetch_kib=25000264.25, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="9d36e26eb823cc55", fetch_kib=66005.4, write_kib=39617.7,
+        sources="c48e75ad84158d6f", fetch_kib=66004.9, write_kib=39620.9,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
     "full-f16-n1e6-d128-k16": dict(
-        sources="9d36e26eb823cc55", fetch_kib=257688.0, write_kib=41403.0,
+        sources="c48e75ad84158d6f", fetch_kib=257680.6, write_kib=41403.8,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")
@@ -335,7 +335,7 @@ def main(argv=None):
     if fp32_path:
         kname = "k_diag_split (the LL sum in its last workgroup)"
     elif full_path:
-        kname = ("k_full_wide<E-step> + k_full_merge + one k_full_wide<statistics> per quad of components "
+        kname = ("k_full_wide_e + k_full_merge + one k_full_wide per quad of components "
                  "(+ k_full_sum_ll)" if w.d > 64 else
                  "k_full_pipe (+ k_full_sum_ll)" if w.d > 32 else "k_full_fused (+ k_full_sum_ll)")
     elif w.k <= 256:

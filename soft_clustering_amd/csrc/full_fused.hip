@@ -26,6 +26,8 @@
 // wave w accumulates the second moments of components 4w..4w+3 and the first
 // moments of dimension block w over the tile.
 
+#include <type_traits>
+
 #include "full_internal.h"
 
 namespace gmm {
@@ -759,18 +761,15 @@ __global__ __launch_bounds__(pipe::kThreads, 1) void k_full_pipe(
 // fill most of the 512 registers a lane has at one wave per SIMD, so a wave
 // holds one component at a time, and the point work of every EM iteration
 // takes the two loops over the components ([LP-GMM] 3.2): an E-step launch per
-// group of 16 writes the group's log-sum-exp per point (merged over the groups
-// afterwards), then one E+M launch per quad of components normalises with the
-// merged LSE and accumulates the statistics (the whitening is done twice).
-//   E-step launch (EM = false): wave w whitens the tile against components
-//   4w..4w+3 of the group in turn, each panel loaded when its turn comes;
-//   every thread then forms its point's log-sum-exp and the other per-point
-//   outputs exactly as k_full_fused does.
-//   E+M launch: components 4 quad .. 4 quad + 3 of the group, one per wave,
-//   the panel loaded once; after the whitening every thread turns the four
-//   scores of its point into responsibilities, then wave w accumulates the
-//   second moments of its component and the first moments of dimension blocks
-//   2w, 2w + 1 of all four.
+// group of 16 (k_full_wide_e, below) writes the group's log-sum-exp per point
+// (merged over the groups afterwards), then one statistics launch per quad of
+// components (k_full_wide) normalises with the merged LSE and accumulates the
+// statistics (the whitening is done twice).
+//   Statistics launch: components 4 quad .. 4 quad + 3 of the group, one per
+//   wave, the panel loaded once; after the whitening every thread turns the
+//   four scores of its point into responsibilities, then wave w accumulates
+//   the second moments of its component and the first moments of dimension
+//   blocks 2w, 2w + 1 of all four.
 namespace wide {
 constexpr int DP = 128, NB = 8, NBLK = 36, NOB = 4, NKS = 8;
 constexpr int NPR = 20;          // lower-triangle (out block, K step) pairs: K step <= 2 ob + 1
@@ -779,10 +778,11 @@ constexpr int kGS = T + 4;
 constexpr int NVL = 2 * NOB * NKS;   // panel vectors per lane and component in memory
 __host__ __device__ constexpr int pair_of(int ob, int ks) { return ob * (ob + 1) + ks; }
 
-// The whitening MFMAs from inline asm: the accumulator stays in VGPRs (the
-// compiler would give it AGPRs next to the resident second moments, and the
-// vector unit would then copy it out for |z|^2), the hi half of the panel is
-// read from VGPRs and the lo half from AGPRs.  The compiler sees no MFMA in
+// The whitening MFMAs from inline asm: the accumulator stays in VGPRs (in the
+// statistics launch the compiler would give it AGPRs next to the resident
+// second moments, and the vector unit would then copy it out for |z|^2); the
+// statistics launch reads the hi half of the panel from VGPRs and the lo half
+// from AGPRs.  The compiler sees no MFMA in
 // an asm statement, so the wait states are written out: two before each (a
 // vector-ALU write of an operand just before an MFMA) and `settle` (24) after
 // the last one of a block, before any other instruction touches the
@@ -797,34 +797,33 @@ __device__ __forceinline__ void mfma_av(f32x16& d, const half8& a, const half8& 
 __device__ __forceinline__ void settle(f32x16& p, f32x16& q, f32x16& r, f32x16& u) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(p), "+v"(q), "+v"(r), "+v"(u));
 }
+__device__ __forceinline__ void settle2(f32x16& p, f32x16& q) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(p), "+v"(q));
+}
 }  // namespace wide
 
-template <bool EM, bool VEC>
+template <bool VEC>
 __global__ __launch_bounds__(256, 1) void k_full_wide(
-    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, int k_real,
-    const uint4* __restrict__ wpk, const float* __restrict__ wbias, const float* __restrict__ muh,
-    const float* __restrict__ cvec, const float* __restrict__ rscale, float* __restrict__ part,
-    double* __restrict__ part_ll, const FullPass ps, int64_t tlo, int64_t thi, int seg_first) {
+    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, const uint4* __restrict__ wpk,
+    const float* __restrict__ wbias, const float* __restrict__ muh, const float* __restrict__ cvec,
+    const float* __restrict__ rscale, float* __restrict__ part, const FullPass ps, int64_t tlo,
+    int64_t thi) {
     using namespace wide;
-    constexpr int KC = EM ? 4 : KP;   // components of this launch
-    const int kq = EM ? 4 * ps.quad : 0;   // the first of them within the group
-    __shared__ __attribute__((aligned(16))) uint32_t nm_s[EM ? 4 : 1][DP];   // (-mu, -mu) fp16 pairs
+    constexpr int KC = 4;   // components of this launch
+    const int kq = 4 * ps.quad;   // the first of them within the group
+    __shared__ __attribute__((aligned(16))) uint32_t nm_s[KC][DP];   // (-mu, -mu) fp16 pairs
     __shared__ __attribute__((aligned(16))) float wb_s[KC][DP];              // -W mu
     __shared__ float cv_s[KC], hq_s[KC];
     __shared__ __attribute__((aligned(16))) float g_s[KC][kGS];              // scores, then gamma
-    // the tile, row-major; E+M: two buffers, the next tile's registers are
-    // written out between the whitening and the moments of this one
-    constexpr int NBUF = EM ? 2 : 1;
-    __shared__ __attribute__((aligned(16))) uint16_t xr_s[NBUF][T][kXR];
-    __shared__ double red[256];
+    // the tile, row-major, in two buffers: the next tile is written into the
+    // other one during the whitening of this one
+    __shared__ __attribute__((aligned(16))) uint16_t xr_s[2][T][kXR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
 
-    if constexpr (EM) {
-        for (int i = tid; i < 4 * DP; i += 256) {
-            const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-muh[(kq + i / DP) * DP + i % DP]));
-            nm_s[i / DP][i % DP] = h | (h << 16);
-        }
+    for (int i = tid; i < KC * DP; i += 256) {
+        const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-muh[(kq + i / DP) * DP + i % DP]));
+        nm_s[i / DP][i % DP] = h | (h << 16);
     }
     for (int i = tid; i < KC * DP; i += 256) wb_s[i / DP][i % DP] = -wbias[(kq + i / DP) * DP + i % DP];
     if (tid < KC) {
@@ -884,10 +883,6 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
             return v;
         }
     };
-    auto load_point = [&](int64_t t, uint4 (&xv)[DP / 8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < DP / 8; ++c) xv[c] = load_raw(t, c);
-    };
     // the lower-triangle blocks of component kg's panel (group-local index)
     auto load_panel = [&](int kg, half8 (&wv)[2][NPR]) __attribute__((always_inline)) {
 #pragma unroll
@@ -918,16 +913,11 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
 #pragma unroll
                 for (int ob = 0; ob < NOB; ++ob) {
                     if (ks > 2 * ob + 1) continue;   // above the diagonal: W is lower triangular
-                    if constexpr (EM) {   // beside the resident moments: VGPR accumulators
-                        mfma_vv(acc[ob], wv[0][pair_of(ob, ks)], xb);
-                        mfma_av(acc[ob], wv[1][pair_of(ob, ks)], xb);
-                    } else {
-                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[0][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
-                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[1][pair_of(ob, ks)], xb, acc[ob], 0, 0, 0);
-                    }
+                    mfma_vv(acc[ob], wv[0][pair_of(ob, ks)], xb);
+                    mfma_av(acc[ob], wv[1][pair_of(ob, ks)], xb);
                 }
             }
-            if constexpr (EM) settle(acc[0], acc[1], acc[2], acc[3]);
+            settle(acc[0], acc[1], acc[2], acc[3]);
             float qp[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four chains: |z|^2 waits on no long chain
 #pragma unroll
             for (int ob = 0; ob < NOB; ++ob)
@@ -938,22 +928,14 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
         }
     };
 
-    float s0acc[EM ? 4 : 1] = {};
-    f32x4 acc2[EM ? NBLK : 1];
+    float s0acc[4] = {};
+    f32x4 acc2[NBLK];
     f32x4 acc1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if constexpr (EM) {
 #pragma unroll
-        for (int q = 0; q < NBLK; ++q) acc2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    double ll = 0.0;
+    for (int q = 0; q < NBLK; ++q) acc2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     half8 wv[2][NPR];
-    uint4 xv[EM ? 1 : DP / 8];   // E-step: the next tile's point, loaded behind this one
-    auto store_tile = [&](int buf, int64_t t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[buf][tid][8 * c]) = finish(t, c, xv[c]);
-    };
-    if constexpr (EM) {
+    {
         load_panel(kq + w, wv);
         // wait for the panel here, once: otherwise the wait inserted before its
         // first use inside the tile loop stays in the loop and also waits for
@@ -964,15 +946,13 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
 #pragma unroll
             for (int c = 0; c < DP / 8; ++c) *reinterpret_cast<uint4*>(&xr_s[0][tid][8 * c]) = load_col(t0, c);
         }
-    } else {
-        if (t0 < t1) load_point(t0, xv);
     }
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t p = t * T + tid;
         const bool valid = p < n;
-        const int cur = EM ? (int)((t - t0) & 1) : 0;
+        const int cur = (int)((t - t0) & 1);
         __syncthreads();   // the previous tile is done with g_s (and its own buffer)
-        if constexpr (EM) {
+        {
             // the next tile goes to the other buffer (it held tile t - 1) two
             // 16-byte columns per whitening step, each stored three steps after
             // its loads were issued: 32 registers in flight instead of 64
@@ -998,23 +978,10 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
                 *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c]) = finish(tn, c, nx[(st - 3) % 4][0]);
                 *reinterpret_cast<uint4*>(&xr_s[cur ^ 1][tid][8 * c + 8]) = finish(tn, c + 1, nx[(st - 3) % 4][1]);
             }
-        } else {
-            store_tile(0, t);
-            __syncthreads();
-            if (t + 1 < t1) load_point(t + 1, xv);   // the next tile, behind this one's work
-#pragma unroll 1
-            for (int kk = 0; kk < 4; ++kk) {
-                const int kl = 4 * w + kk;
-                load_panel(kl, wv);
-                const float cvk = cv_s[kl], hqk = hq_s[kl];
-#pragma unroll 1
-                for (int st = 0; st < T / 32; ++st) whiten_step(kl, wv, 0, st, cvk, hqk);
-            }
         }
         __syncthreads();
 
-        if constexpr (EM) {
-            // responsibilities from the merged LSE of all groups
+        {   // responsibilities from the merged LSE of all groups
             const float lse2 = valid ? ps.lse_in[p] * kLog2ef : 0.0f;
             const float lsafe = lse2 == -INFINITY ? INFINITY : lse2;   // no live component
 #pragma unroll
@@ -1023,37 +990,9 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
                 s0acc[k] += gk;
                 g_s[k][tid] = gk;
             }
-        } else {
-            // base-2 log-sum-exp of the group, per-point outputs (as k_full_fused)
-            float sv[KP];
-            float M = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < KP; ++k) {
-                sv[k] = g_s[k][tid];
-                M = fmaxf(M, sv[k]);
-            }
-            const float Ms = M == -INFINITY ? 0.0f : M;
-            float Z = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KP; ++k) Z += fast_exp2(sv[k] - Ms);
-            const float own = Ms + fast_log2(Z);
-            const float lse2 = ps.lse_in != nullptr ? (valid ? ps.lse_in[p] * kLog2ef : 0.0f) : own;
-            if (valid) {
-                ll += (double)own;
-                if (ps.out_lse) ps.out_lse[p] = lse2 * kLn2f;
-                if (ps.out_arg) {
-                    int a = 0;
-#pragma unroll
-                    for (int k = KP - 1; k >= 0; --k)
-                        if (sv[k] == M) a = k;
-                    ps.out_arg[p] = KP * ps.group + a;
-                }
-                if (ps.out_max) ps.out_max[p] = M;
-                if (ps.topm > 0) write_topm(sv, lse2, ps, p);
-            }
         }
 
-        if constexpr (EM) {
+        {
             __syncthreads();
 #pragma unroll 1
             for (int ks = 0; ks < T / 32; ++ks) {
@@ -1105,7 +1044,7 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
     }
 
     __syncthreads();
-    if constexpr (EM) {
+    {
         // rows kq..kq+3 of this workgroup's partial slot [KP][1 + D + D(D+1)/2]
         const int ncolp = 1 + d + d * (d + 1) / 2;
         float* dst = part + (int64_t)b * KP * ncolp;
@@ -1136,15 +1075,197 @@ __global__ __launch_bounds__(256, 1) void k_full_wide(
                     if (row >= col && row < d)
                         dst[(int64_t)(kq + w) * ncolp + 1 + d + tri_idx(row, col)] = acc2[blk_index(ab, bb)][r];
                 }
-    } else {
-        red[tid] = ll;
-        __syncthreads();
-        for (int s2 = 128; s2 > 0; s2 >>= 1) {
-            if (tid < s2) red[tid] += red[tid + s2];
-            __syncthreads();
-        }
-        if (tid == 0 && part_ll != nullptr) part_ll[b] = seg_first ? red[0] * kLn2 : part_ll[b] + red[0] * kLn2;
     }
+}
+
+// E-step launch for 64 < D <= 128 over a group of 16 components: eight waves,
+// two per SIMD.  Wave w takes components 4 (w / 2) .. + 3 in turn and, of
+// each, half of the lower-triangle output blocks of W (x - mu): blocks 0 and 3
+// (10 of the 20 (block, K step) pairs) for even w, blocks 1 and 2 (the other
+// 10) for odd w, so a wave holds half a panel (80 registers) and the other
+// wave on its SIMD fills the gaps of its own (the panel loads of each
+// component, |z|^2 after each 32-point block).  The two halves of |z|^2 meet
+// in LDS; every thread of the first four waves then forms its point's
+// log-sum-exp and per-point outputs as k_full_fused does.
+namespace wide_e {
+constexpr int kThreads = 512;
+constexpr int NP = 10;   // (block, K step) pairs per half
+// pair p of half h: output block and K step
+__host__ __device__ constexpr int blk(int h, int p) { return h == 0 ? (p < 2 ? 0 : 3) : (p < 4 ? 1 : 2); }
+__host__ __device__ constexpr int kst(int h, int p) { return h == 0 ? (p < 2 ? p : p - 2) : (p < 4 ? p : p - 4); }
+}  // namespace wide_e
+
+template <bool VEC>
+__global__ __launch_bounds__(wide_e::kThreads, 1) void k_full_wide_e(
+    const _Float16* __restrict__ x, int64_t n, int d, int64_t ldx, const uint4* __restrict__ wpk,
+    const float* __restrict__ wbias, const float* __restrict__ cvec, const float* __restrict__ rscale,
+    double* __restrict__ part_ll, const FullPass ps, int64_t tlo, int64_t thi, int seg_first) {
+    using namespace wide;
+    using wide_e::NP;
+    __shared__ __attribute__((aligned(16))) uint16_t xr_s[T][kXR];   // the tile, row-major
+    __shared__ __attribute__((aligned(16))) float gq_s[2][KP][kGS];  // the two halves of |z|^2
+    __shared__ __attribute__((aligned(16))) float wb_s[KP][DP];      // -W mu
+    __shared__ float cv_s[KP], hq_s[KP];
+    __shared__ double red[wide_e::kThreads];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = w & 1, kc = 4 * (w >> 1);
+    for (int i = tid; i < KP * DP; i += wide_e::kThreads) wb_s[i / DP][i % DP] = -wbias[i];
+    if (tid < KP) {
+        const float rs = rscale[tid];
+        cv_s[tid] = cvec[tid];
+        hq_s[tid] = kHalfLog2e * rs * rs;   // |z|^2 = 2^-2e |W x - W mu|^2
+    }
+
+    const int G = gridDim.x;
+    const int64_t tiles = thi - tlo;
+    const int64_t tb = tiles / G, tr = tiles % G;
+    const int b = blockIdx.x;
+    const int64_t t0 = tlo + b * tb + (b < tr ? b : tr);
+    const int64_t t1 = t0 + tb + (b < tr ? 1 : 0);
+
+    // staging: thread tid holds half a row of the next tile, point tid / 2 and
+    // 16-byte columns 8 (tid % 2) .. + 7, loaded raw and masked when stored
+    const int sp = tid >> 1, sc = 8 * (tid & 1);
+    uint4 xv[8];
+    auto load_half = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t p = t * T + sp;
+        const _Float16* row = x + (p < n ? p : 0) * ldx;
+        if constexpr (VEC) {
+            const int cmax = d / 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = sc + i;
+                xv[i] = *reinterpret_cast<const uint4*>(row + 8 * (c < cmax ? c : 0));
+            }
+        } else {
+            const bool valid = p < n;
+            const uint16_t* rb = reinterpret_cast<const uint16_t*>(row);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t wq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i0 = 8 * (sc + i) + 2 * q;
+                    const uint32_t lo = rb[i0 < d ? i0 : 0], hi = rb[i0 + 1 < d ? i0 + 1 : 0];
+                    wq[q] = (valid && i0 < d ? lo : 0u) | ((valid && i0 + 1 < d ? hi : 0u) << 16);
+                }
+                xv[i] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+            }
+        }
+    };
+    auto store_half = [&](int64_t t) __attribute__((always_inline)) {
+        const bool valid = t * T + sp < n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint4 v = xv[i];
+            if constexpr (VEC) {
+                const uint32_t m = (valid && sc + i < d / 8) ? ~0u : 0u;
+                v = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+            }
+            *reinterpret_cast<uint4*>(&xr_s[sp][8 * (sc + i)]) = v;
+        }
+    };
+
+    double ll = 0.0;
+    if (t0 < t1) load_half(t0);
+    for (int64_t t = t0; t < t1; ++t) {
+        __syncthreads();   // the previous tile is done with xr_s / gq_s
+        store_half(t);
+        __syncthreads();
+        if (t + 1 < t1) load_half(t + 1);   // the next tile, behind this one's work
+        // the half's pairs as constants: one copy of the loop per half
+        auto whiten = [&](auto half) __attribute__((always_inline)) {
+            constexpr int H = decltype(half)::value;
+            constexpr int OB0 = H == 0 ? 0 : 1, OB1 = H == 0 ? 3 : 2;   // its two blocks
+            constexpr int N0 = 2 * OB0 + 2;   // pairs (K steps) of block OB0; OB1 takes the rest
+#pragma unroll 1
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = kc + kk;
+                half8 wv[2][NP];   // this half of component k's panel
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp)
+                        wv[hl][pp] = __builtin_bit_cast(
+                            half8, wpk[((int64_t)k * NVL + (hl * NOB + wide_e::blk(H, pp)) * NKS + wide_e::kst(H, pp)) * 64 + lane]);
+#pragma unroll 1
+                for (int st = 0; st < T / 32; ++st) {
+                    f32x16 acc[2];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        acc[0][r] = wb_s[k][32 * OB0 + o];
+                        acc[1][r] = wb_s[k][32 * OB1 + o];
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const half8 xb = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(
+                            &xr_s[32 * st + (lane & 31)][16 * ks + 8 * (lane >> 5)]));
+                        if (ks < N0) {
+                            mfma_vv(acc[0], wv[0][ks], xb);
+                            mfma_vv(acc[0], wv[1][ks], xb);
+                        }
+                        if (ks <= 2 * OB1 + 1) {
+                            mfma_vv(acc[1], wv[0][N0 + ks], xb);
+                            mfma_vv(acc[1], wv[1][N0 + ks], xb);
+                        }
+                    }
+                    settle2(acc[0], acc[1]);
+                    float qp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        qp[r & 3] = fmaf(acc[0][r], acc[0][r], qp[r & 3]);
+                        qp[r & 3] = fmaf(acc[1][r], acc[1][r], qp[r & 3]);
+                    }
+                    const float q = halves_sum((qp[0] + qp[1]) + (qp[2] + qp[3]));
+                    if (lane < 32) gq_s[H][k][32 * st + lane] = q;
+                }
+            }
+        };
+        if (h == 0) whiten(std::integral_constant<int, 0>{});
+        else whiten(std::integral_constant<int, 1>{});
+        __syncthreads();
+
+        // ---- base-2 log-sum-exp of the group, per-point outputs
+        if (tid < T) {
+            const int64_t p = t * T + tid;
+            const bool valid = p < n;
+            float sv[KP];
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                sv[k] = cv_s[k] - hq_s[k] * (gq_s[0][k][tid] + gq_s[1][k][tid]);
+                M = fmaxf(M, sv[k]);
+            }
+            const float Ms = M == -INFINITY ? 0.0f : M;
+            float Z = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) Z += fast_exp2(sv[k] - Ms);
+            const float own = Ms + fast_log2(Z);
+            const float lse2 = ps.lse_in != nullptr ? (valid ? ps.lse_in[p] * kLog2ef : 0.0f) : own;
+            if (valid) {
+                ll += (double)own;
+                if (ps.out_lse) ps.out_lse[p] = lse2 * kLn2f;
+                if (ps.out_arg) {
+                    int a = 0;
+#pragma unroll
+                    for (int k = KP - 1; k >= 0; --k)
+                        if (sv[k] == M) a = k;
+                    ps.out_arg[p] = KP * ps.group + a;
+                }
+                if (ps.out_max) ps.out_max[p] = M;
+                if (ps.topm > 0) write_topm(sv, lse2, ps, p);
+            }
+        }
+    }
+
+    red[tid] = ll;
+    __syncthreads();
+    for (int s2 = wide_e::kThreads / 2; s2 > 0; s2 >>= 1) {
+        if (tid < s2) red[tid] += red[tid + s2];
+        __syncthreads();
+    }
+    if (tid == 0 && part_ll != nullptr) part_ll[b] = seg_first ? red[0] * kLn2 : part_ll[b] + red[0] * kLn2;
 }
 
 // Group g's slice of the per-component arrays and partial slots.
@@ -1214,15 +1335,19 @@ hipError_t launch_wide(const Plan& p, const FullWs& w, const void* x, bool em, i
     const bool vec = (uintptr_t)x % 16 == 0 && p.ldx % 8 == 0 && p.d % 8 == 0;
     const FullGroupPtrs q = group_ptrs<wide::DP>(p, w, ps.group);
     double* pll = (!em && !w.lse_pass) ? w.part_ll : nullptr;
-#define FULL_WIDE(EM_, VEC_)                                                                     \
-    hipLaunchKernelGGL((k_full_wide<EM_, VEC_>), dim3(grid), dim3(256), 0, s,                    \
-                       (const _Float16*)x, p.n, (int)p.d, p.ldx, (int)p.k, q.wpk, q.wbias, q.muh, \
-                       q.cvec, q.rscale, q.part, pll, ps, tlo, thi, seg_first)
-    if (em && vec) FULL_WIDE(true, true);
-    else if (em) FULL_WIDE(true, false);
-    else if (vec) FULL_WIDE(false, true);
-    else FULL_WIDE(false, false);
+#define FULL_WIDE(VEC_)                                                                          \
+    hipLaunchKernelGGL((k_full_wide<VEC_>), dim3(grid), dim3(256), 0, s, (const _Float16*)x, p.n, \
+                       (int)p.d, p.ldx, q.wpk, q.wbias, q.muh, q.cvec, q.rscale, q.part, ps, tlo, thi)
+#define FULL_WIDE_E(VEC_)                                                                        \
+    hipLaunchKernelGGL((k_full_wide_e<VEC_>), dim3(grid), dim3(wide_e::kThreads), 0, s,          \
+                       (const _Float16*)x, p.n, (int)p.d, p.ldx, q.wpk, q.wbias, q.cvec, q.rscale, \
+                       pll, ps, tlo, thi, seg_first)
+    if (em && vec) FULL_WIDE(true);
+    else if (em) FULL_WIDE(false);
+    else if (vec) FULL_WIDE_E(true);
+    else FULL_WIDE_E(false);
 #undef FULL_WIDE
+#undef FULL_WIDE_E
     return hipGetLastError();
 }
 

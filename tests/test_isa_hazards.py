@@ -115,10 +115,11 @@ CASES = [
     # E+M, x 2 storage types x 2 load paths): 34 score MFMAs (17 steps x 2
     # blocks) and 4 s0 MFMAs per tile
     ("largek.hip", "k_lk", {38: 8}),
-    # full covariance, D <= 128: the statistics kernels (2 load paths), 40
-    # whitening MFMAs per 32-point block (20 lower-triangle blocks, hi and lo)
-    # for each of the tile's 8 blocks
-    ("full_fused.hip", "k_full_wide", {320: 2}),
+    # full covariance, D <= 128: 40 whitening MFMAs per 32-point block (20
+    # lower-triangle blocks, hi and lo); the statistics kernels (2 load paths)
+    # unroll the tile's 8 blocks, the E-step kernels (k_full_wide_e, 2 load
+    # paths) hold one copy of the block loop for each half of the blocks
+    ("full_fused.hip", "k_full_wide", {40: 2, 320: 2}),
 ]
 
 
