@@ -291,11 +291,12 @@ def test_determinism_bitwise(gmm_lib):
         assert torch.equal(a, b)
 
 
-def test_full_size_workload(gmm_lib):
-    """1e6 points, D=64, K=16 in the benchmark's configuration: sum of s0 = N,
-    fused and E-only LL agree, per-point LSE / argmax on sampled points
-    against the oracle, at theta_0 and at theta_1."""
-    w = synth.WORKLOADS["full-f16-n1e6-d64-k16"]
+@pytest.mark.parametrize("name", ["full-f16-n1e6-d64-k16", "full-f16-n1e6-d128-k16"])
+def test_full_size_workload(gmm_lib, name):
+    """1e6 points, D = 64 (and D = 128), K = 16 in the benchmark's
+    configuration: sum of s0 = N, fused and E-only LL agree, per-point LSE /
+    argmax on sampled points against the oracle, at theta_0 and at theta_1."""
+    w = synth.WORKLOADS[name]
     mix = synth.make_mixture(w)
     xg = synth.sample_points(w, mix, device="cuda")
     th0 = synth.init_params(w, xg)
