@@ -161,6 +161,8 @@ CASES = [
     (200, 72, 3, 0, False),      # one tile, D = 72
     (2000, 128, 256, 0, False),  # K = 256 at D = 128: 16 groups, 64 statistics launches
     (1500, 96, 33, 2, True),     # D = 96, three groups, element-wise loads
+    (2000, 128, 7, 8, False),    # D = 128 with a padded row stride, vector loads
+    (1, 128, 2, 0, False),       # one point at D = 128
 ]
 
 
