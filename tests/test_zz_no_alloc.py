@@ -56,6 +56,7 @@ def _reference(gmm_lib, n, d, k, cov, x_dtype, th, xg):
     ("iso", "bf16", 128, 256, 60_000, 5_000),
     ("diag", "bf16", 64, 600, 40_000, 777),
     ("full", "f16", 64, 16, 100_000, 2_000),
+    ("full", "f16", 128, 20, 20_000, 1_500),   # D = 128: per-group LSE, statistics per quad
 ])
 def test_noalloc_matches_workspace_path(gmm_lib, cov, x_dtype, d, k, n1, n2):
     for n in (n1, n2):   # two calls in a row, the second smaller
