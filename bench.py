@@ -57,19 +57,19 @@ DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="36d68f80714d3124", fetch_kib=125188.2, write_kib=4144.3,
+        sources="a7534c77ad532b9b", fetch_kib=125185.2, write_kib=4144.3,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
-        sources="eb934dafb31f75b6", fetch_kib=1251543.4, write_kib=78338.1,
-        copy_bytes=2.56e+09, copy_fetch_kib=1250033.875, copy_write_kib=2500000.0),
+        sources="1ddfc6385e023df2", fetch_kib=1251543.4, write_kib=78474.3,
+        copy_bytes=2.56e+09, copy_fetch_kib=1250035.6875, copy_write_kib=2500000.0),
     "diag-bf16-n2e8-d128-k1024": dict(
-        sources="eb934dafb31f75b6", fetch_kib=53728006.3, write_kib=7438873.6,
-        copy_bytes=5.12e+10, copy_fetch_kib=25000264.25, copy_write_kib=50000000.0),
+        sources="1ddfc6385e023df2", fetch_kib=53762256.3, write_kib=7458634.4,
+        copy_bytes=5.12e+10, copy_fetch_kib=25000253.125, copy_write_kib=50000000.0),
     "full-f16-n1e6-d64-k16": dict(
-        sources="c48e75ad84158d6f", fetch_kib=66004.9, write_kib=39620.9,
+        sources="abdce93111c35cee", fetch_kib=66005.4, write_kib=39623.3,
         copy_bytes=1.28e+08, copy_fetch_kib=62511.5, copy_write_kib=125000.0),
     "full-f16-n1e6-d128-k16": dict(
-        sources="c48e75ad84158d6f", fetch_kib=257680.6, write_kib=41403.8,
+        sources="abdce93111c35cee", fetch_kib=257789.8, write_kib=41404.2,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
 }
 _SHARED_SOURCES = ("api.hip", "common.h", "plan.h", "../build.py")

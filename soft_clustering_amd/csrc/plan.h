@@ -11,7 +11,7 @@ namespace gmm {
 enum Path : int {
     PATH_DIAG_F32 = 0,   // diagonal, K <= 64: fp32-accurate split-fp16 MFMA scores and statistics
     PATH_LARGEK = 1,     // isotropic / diagonal, X in bf16 or fp16, fp16 MFMA, K <= 4096
-    PATH_FULL = 2,       // full covariance, X in fp16, fp16 MFMA whitening and moments, K <= 16, D <= 64
+    PATH_FULL = 2,       // full covariance, X in fp16, fp16 MFMA whitening and moments, K <= 256, D <= 128
 };
 
 struct Plan {
