@@ -240,13 +240,14 @@ def test_ridge_retry_and_not_pd(gmm_lib):
     assert metrics.rel(ll_b, ll_ref) <= LL_TOL
 
 
-def test_thin_component_whitening_range(gmm_lib):
+@pytest.mark.parametrize("d", [16, 128])
+def test_thin_component_whitening_range(gmm_lib, d):
     """A component whose variance in one direction is 1e-12 of the others
     (ridge_rel = 0, so nothing widens it): its inverse factor relative to the
     mean scale reaches about 1e6, beyond fp16, and the preparation rescales
     the whitening panel into range.  LL (E-step and E+M) against the oracle
-    with the same ridge."""
-    n, d, k = 3000, 16, 3
+    with the same ridge; at D = 16 and on the D <= 128 kernels."""
+    n, k = 3000, 3
     xd, xg, ldx, (pi0, mu0, cov0) = _make(n, d, k, 0, False, seed=23)
     dv = np.ones(d)
     dv[6] = 1e-12
