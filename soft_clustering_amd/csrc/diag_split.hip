@@ -716,25 +716,32 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
                     v += (double)red[(w2 * 16 * KB + k) * (2 * DP) + col];
             }
             double* o = part + (wg * k_real + k) * ncol + c;
-            *o = seg_first ? v : *o + v;   // later segments add to the slot
+            // later segments add to the slot; streamed past the L2
+            __builtin_nontemporal_store(seg_first ? v : *o + v, o);
         }
     }
     // LL of the whole pass: the last workgroup to finish sums the
-    // per-workgroup values in a fixed order (release before the count,
-    // acquire after it, both at device scope; the count returns to zero for
-    // the next launch)
+    // per-workgroup values in a fixed order.  Each value is stored as a
+    // device-scope atomic (written through to the level every XCD sees) and
+    // waited for before the count moves, and the last workgroup reads them
+    // with device-scope atomic loads: no L2 write-back or invalidation is
+    // needed for them (the partial slots above are read by the next kernel,
+    // after this one has ended).  The count returns to zero for the next
+    // launch.
     __shared__ int last_wg;
     if (tid == 0) {
-        part_ll[wg] = seg_first ? ll_wg * kLn2 : part_ll[wg] + ll_wg * kLn2;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const double llv = seg_first ? ll_wg * kLn2 : part_ll[wg] + ll_wg * kLn2;
+        __hip_atomic_store(&part_ll[wg], llv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // the store is done before the count moves
+        asm volatile("" ::: "memory");
         const unsigned prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_wg = prev == gridDim.x - 1;
     }
     __syncthreads();
     if (last_wg) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         double v = 0.0;
-        for (int p = tid; p < (int)gridDim.x; p += THREADS) v += part_ll[p];
+        for (int p = tid; p < (int)gridDim.x; p += THREADS)
+            v += __hip_atomic_load(&part_ll[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v = block_sum_f64(v, llred);
         if (tid == 0) {
             *ll_ws = v;
