@@ -57,7 +57,7 @@ DEFAULT_WORKLOAD = "diag-bf16-n2e8-d128-k1024"
 # as null.
 TRAFFIC = {
     "diag-f32-n1e6-d64-k16": dict(
-        sources="58df599be0a725a9", fetch_kib=125170.6, write_kib=4144.3,
+        sources="e577314d9fe4ccae", fetch_kib=125176.5, write_kib=4144.3,
         copy_bytes=2.56e+08, copy_fetch_kib=125011.5, copy_write_kib=250000.0),
     "iso-bf16-n1e7-d128-k256": dict(
         sources="1ddfc6385e023df2", fetch_kib=1251543.4, write_kib=78474.3,

@@ -701,19 +701,33 @@ __global__ __launch_bounds__(64 * diag_split_waves(DP, KB), 1) void k_diag_split
     __syncthreads();
     const int64_t wg = blockIdx.x;
     if constexpr (EM) {
-        // partial columns: [s0, S1_0, S2_0, S1_1, S2_1, ...] (moments of y about c)
+        // partial columns: [s0, S1_0, S2_0, S1_1, S2_1, ...] (moments of y about c).
+        // s0 per component first (its 4 WAVES terms summed once, not in the
+        // column loop, where its lanes would hold up the rest of their wave)
+        __shared__ double s0sum[16 * KB];
+        for (int k = tid; k < k_real; k += THREADS) {
+            double v = 0.0;
+            for (int w2 = 0; w2 < WAVES; ++w2)
+                for (int g2 = 0; g2 < 4; ++g2) v += (double)s0red[w2][g2][k];
+            s0sum[k] = v;
+        }
+        __syncthreads();
         const int ncol = 1 + 2 * d;
         for (int e2 = tid; e2 < k_real * ncol; e2 += THREADS) {
             const int k = e2 / ncol, c = e2 % ncol;
-            double v = 0.0;
+            double v;
             if (c == 0) {
-                for (int w2 = 0; w2 < WAVES; ++w2)
-                    for (int g2 = 0; g2 < 4; ++g2) v += (double)s0red[w2][g2][k];
+                v = s0sum[k];
             } else {
                 const int dd = (c - 1) >> 1, mom = (c - 1) & 1;
                 const int col = mom == 0 ? DP + dd : dd;   // S1 <- y, S2 <- y^2
-                for (int w2 = 0; w2 < WAVES; ++w2)
-                    v += (double)red[(w2 * 16 * KB + k) * (2 * DP) + col];
+                double v0 = 0.0, v1 = 0.0;   // even and odd waves, all reads issued together
+#pragma unroll
+                for (int w2 = 0; w2 < WAVES; w2 += 2) {
+                    v0 += (double)red[(w2 * 16 * KB + k) * (2 * DP) + col];
+                    v1 += (double)red[((w2 + 1) * 16 * KB + k) * (2 * DP) + col];
+                }
+                v = v0 + v1;
             }
             double* o = part + (wg * k_real + k) * ncol + c;
             // later segments add to the slot; streamed past the L2
