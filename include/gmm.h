@@ -120,8 +120,12 @@ typedef struct {
 } gmm_diag;
 
 /* Bytes of device workspace the descriptor needs (host call, no GPU work).
- * The size is O(K*D^2 + P*K*D + N) for a fixed number P of partial slots;
- * it never contains an N x K term ([Flash-GMM] key insight: memory O(N+K)).
+ * The size is O(K*D^2 + P*K*D + N*G) for a fixed number P of partial slots,
+ * where G is 1 for the diagonal K <= 64 plans and the number of component
+ * slices (K / 256, large-K plans) or groups (K / 16 when K > 16 or D > 64,
+ * full covariance) whose per-point log-sum-exp is kept between two passes;
+ * it never holds the N x K responsibility matrix ([Flash-GMM] key insight:
+ * memory O(N + K) per slice).
  * Returns GMM_E_ARG / GMM_E_UNSUPPORTED for descriptors the library rejects. */
 gmm_status gmm_workspace_bytes(const gmm_desc* desc, size_t* bytes /* host */);
 

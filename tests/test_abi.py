@@ -111,3 +111,17 @@ def test_null_arguments_rejected_before_launch():
     nb0 = gmm.workspace_bytes(d0)
     assert lib.gmm_em_step(ctypes.byref(d0), ctypes.c_void_p(256), nb0, ctypes.c_void_p(256), None, None) == gmm.GMM_E_ARG
     assert lib.gmm_diagnostics(ctypes.byref(d), ctypes.c_void_p(256), nb, None, None) == gmm.GMM_E_ARG
+
+
+def test_full_wide_workspace_per_point():
+    """Full covariance with several groups of 16 components, or at D > 64,
+    keeps each group's LSE, argmax and largest score per point (12 bytes per
+    point and group) between its E-step and statistics passes; nothing else
+    in its workspace grows with N, and nothing holds the N x K matrix."""
+    for d, k, groups in [(128, 40, 3), (128, 16, 1), (32, 40, 3)]:
+        w1 = gmm.workspace_bytes(gmm.make_desc(10 ** 6, d, k, "full", "f16"))
+        w2 = gmm.workspace_bytes(gmm.make_desc(2 * 10 ** 6, d, k, "full", "f16"))
+        assert abs((w2 - w1) - 12 * groups * 10 ** 6) <= 1024, (d, k, w2 - w1)
+    # D <= 64 with one group: no per-point rows at all
+    assert (gmm.workspace_bytes(gmm.make_desc(2 * 10 ** 6, 64, 16, "full", "f16")) ==
+            gmm.workspace_bytes(gmm.make_desc(10 ** 6, 64, 16, "full", "f16")))
